@@ -1,0 +1,32 @@
+"""CPU oracle for absorbed MLA decode over a paged latent cache.
+
+TEST INFRASTRUCTURE ONLY.  This package is the plain, slow, fp64 statement of
+what the GPU path computes.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the library path never does, and
+this package imports nothing from the library.  It shares no code, tables or
+helpers with the HIP kernels.
+
+Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
+printed values of the pages (``tests/golden/``), textbook special cases,
+invariants and brute force.  No function here is "parity unpinned".
+"""
+
+from .capacity import (  # noqa: F401
+    element_reduction,
+    kv_cache_bytes,
+    page_bytes,
+    physical_cache_bytes,
+    stage_ring_bytes,
+)
+from .mla_oracle import (  # noqa: F401
+    absorb_q,
+    attention_probs,
+    bf16_bits_to_f64,
+    combine_fragments,
+    decode_absorbed,
+    decode_decompressed,
+    f64_to_bf16_bits,
+    gather_rows,
+    split_decode_absorbed,
+    up_proj,
+)
