@@ -1,0 +1,163 @@
+/*
+ * Absorbed Multi-Head Latent Attention (MLA) decode over a paged latent cache,
+ * for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation (stated in the pages' terms):
+ *   - Each cached token stores one row of 576 bf16 values: the latent c_KV
+ *     (512) followed by the decoupled RoPE key k_R (64), 1152 bytes per token
+ *     per layer ("撕开 DeepSeek MLA 源码", sheratonhq.com, section 1).
+ *   - Rows live in pages of 64 tokens; a block table maps a sequence's logical
+ *     page j to a physical page (same page, section 3: page_size 64 in the
+ *     mla_plugin JSON; section 5: the page-table base feeds 16-byte loads).
+ *   - W_UK is folded into the query: q_abs = q_c . W_UK[h] (section 4, path B,
+ *     contraction 'qhd,hdc->qhc').  Scores are (q_abs . c_KV + q_R . k_R) times
+ *     1/sqrt(d_hc + d_R) = 1/sqrt(192) (section 4).  Softmax, then P . c_KV in
+ *     latent space, then the up-projection through W_UV ("DeepSeek的推理为什么
+ *     比别人便宜一个数量级", leslieaibin.github.io, section "MLA": V = c . W_UV).
+ *
+ * Fixed dimensions: num_heads H = 128, d_hc = 128, d_c = 512, d_R = 64,
+ * page_size = 64 (the mla_config.h constants and mla_plugin JSON, sheratonhq.com
+ * section 3).  Other values return MLA_ERR_UNSUPPORTED.
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major, contiguous.
+ *   - All tensor pointers are DEVICE pointers (HIP device memory of the current
+ *     device); parameter structs and size outputs are HOST pointers.
+ *   - The caller owns every buffer.  The library allocates nothing on these
+ *     calls and keeps no pointer after returning.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
+ *     enqueue work on it and return; nothing is synchronised.
+ *   - Host-side checks run before any launch and return an error without
+ *     touching the GPU: NULL pointers, unsupported dimensions, pointers not
+ *     16-byte aligned (MLA_ERR_MISALIGNED; the pages report misaligned-address
+ *     faults for 16-byte vector loads from an unaligned cache or page table,
+ *     sheratonhq.com section 5), a workspace that is too small.  A failed
+ *     launch returns MLA_ERR_HIP.  mla_last_error() then gives a thread-local
+ *     message.  No C++ exception crosses this interface.
+ *   - Values in device memory cannot be checked without a synchronisation and
+ *     are preconditions: s_q <= seqlens[b] <= max_blocks_per_seq * 64, and the
+ *     block-table entries of pages that cover tokens [0, seqlens[b]) lie in
+ *     [0, num_pages).  Entries past those pages, and cache rows at or past
+ *     seqlens[b], are never read.  Violations never make the kernels read
+ *     outside kv_blocks or block_table (lengths are clamped to the table row and
+ *     page ids to [0, num_pages)); the affected outputs are then unspecified.
+ *     A sequence with fewer visible tokens than 1 gets out_latent = 0 and
+ *     lse = -inf.
+ */
+#ifndef MLA_KV04_H
+#define MLA_KV04_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, bad field */
+  MLA_ERR_MISALIGNED = 2,  /* a tensor pointer is not 16-byte aligned */
+  MLA_ERR_UNSUPPORTED = 3, /* a dimension other than the fixed ones above */
+  MLA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
+  MLA_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} mla_status;
+
+/* Decode-step description (host struct).  The pages' plugin JSON names the
+ * same fields: num_heads, page_size, kv_cache_dtype bf16 (sheratonhq.com §3). */
+typedef struct mla_decode_params {
+  int32_t batch;              /* B >= 0 sequences */
+  int32_t s_q;                /* new query tokens per sequence: 1, or 2 for a
+                                 two-token verify step; query i of sequence b
+                                 sees tokens t <= seqlens[b] - s_q + i */
+  int32_t num_heads;          /* must be 128 */
+  int32_t page_size;          /* must be 64 */
+  int32_t max_blocks_per_seq; /* row length of block_table, >= 1 */
+  int32_t num_splits;         /* 0: one decode workgroup per compute unit of the
+                                 current device; > 0: exactly this many (the
+                                 split plan changes, the result stays within
+                                 rounding) */
+  int64_t num_pages;          /* physical pages in kv_blocks, >= 1 */
+  float scale;                /* softmax scale on (q_abs.c + q_R.k_R); > 0,
+                                 1/sqrt(192) for the DeepSeek dimensions */
+  int32_t reserved;           /* must be 0 */
+} mla_decode_params;
+
+/* q_abs[t, h, :] = q_c[t, h, :] . W_UK[h]  (bf16 in, fp32 accumulate, RNE to bf16).
+ * q_c [tokens, H, 128], w_uk [H, 128, 512], q_abs [tokens, H, 512].  tokens >= 0
+ * (0 is a no-op).  sheratonhq.com section 4, path B. */
+mla_status mla_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_abs,
+                        int32_t tokens, int32_t num_heads, void* stream);
+
+/* Workspace bytes needed by mla_decode_paged (fused = 0) or mla_decode
+ * (fused = 1) for these parameters.  With p->num_splits == 0 the current
+ * device's compute-unit count is queried (a HIP call).  Returns 0 when p is
+ * invalid or the query fails. */
+size_t mla_decode_workspace_size(const mla_decode_params* p, int32_t fused);
+
+/* Paged decode in latent space (split-KV over pages, log-sum-exp merge).
+ *   q_abs       [B, s_q, H, 512] bf16   absorbed content query
+ *   q_r         [B, s_q, H, 64]  bf16   RoPE query (already rotated)
+ *   kv_blocks   [num_pages, 64, 576] bf16, row = c_KV[512] || k_R[64]
+ *   block_table [B, max_blocks_per_seq] int32 physical page ids
+ *   seqlens     [B] int32, tokens in the cache per sequence (including the
+ *               s_q new ones)
+ *   out_latent  [B, s_q, H, 512] bf16  softmax(scores) . c_KV
+ *   lse         [B, s_q, H] fp32, natural log of the softmax denominator of the
+ *               scaled scores; may be NULL
+ *   workspace   device scratch of >= mla_decode_workspace_size(p, 0) bytes,
+ *               16-byte aligned; contents need no initialisation.
+ * Calls that share a workspace must be ordered on one stream. */
+mla_status mla_decode_paged(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv_blocks,
+                            const int32_t* block_table, const int32_t* seqlens, uint16_t* out_latent,
+                            float* lse, const mla_decode_params* p, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* out[t, h, :] = out_latent[t, h, :] . W_UV[h]  (bf16 in, fp32 accumulate, RNE).
+ * out_latent [tokens, H, 512], w_uv [H, 512, 128], out [tokens, H, 128].
+ * leslieaibin.github.io section "MLA" (V = c . W_UV) with the token sum moved
+ * before the projection. */
+mla_status mla_up_proj(const uint16_t* out_latent, const uint16_t* w_uv, uint16_t* out,
+                       int32_t tokens, int32_t num_heads, void* stream);
+
+/* Fused decode step: absorb -> paged decode -> merge -> up-projection.
+ *   q_c [B, s_q, H, 128], q_r [B, s_q, H, 64], w_uk [H, 128, 512],
+ *   w_uv [H, 512, 128], out [B, s_q, H, 128] bf16, lse as above (may be NULL).
+ * workspace >= mla_decode_workspace_size(p, 1) bytes (holds q_abs and
+ * out_latent as well). */
+mla_status mla_decode(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* w_uk,
+                      const uint16_t* w_uv, const uint16_t* kv_blocks, const int32_t* block_table,
+                      const int32_t* seqlens, uint16_t* out, float* lse, const mla_decode_params* p,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Test export of the page gather: dense[b, t, :] = kv_blocks[block_table[b][t / 64], t % 64, :]
+ * for t < seqlens[b]; rows t in [seqlens[b], max_blocks_per_seq * 64) are zero.
+ * dense [B, max_blocks_per_seq * 64, 576] bf16. */
+mla_status mla_gather_kv(const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens,
+                         uint16_t* dense, const mla_decode_params* p, void* stream);
+
+/* Benchmark timing hook.  After mla_profile_enable(1), every mla_decode_paged
+ * and mla_decode call on any stream records HIP events around each of its
+ * kernels (up to 65536 calls; the library creates those events once and keeps
+ * them).  mla_profile_collect waits for the recorded calls, writes the summed
+ * milliseconds of [absorb, plan, decode, combine, up-projection] to ms[0..4]
+ * (host array of 5) and the number of calls to *calls, and clears the record.
+ * mla_profile_enable(0) stops recording.  Off by default; not for code under
+ * graph capture. */
+mla_status mla_profile_enable(int32_t enable);
+mla_status mla_profile_collect(double* ms, int32_t* calls);
+
+/* Number of compute units of the current device (a HIP call). */
+mla_status mla_device_cu_count(int32_t* num_cus);
+
+/* Static text for a status code; never NULL. */
+const char* mla_status_string(mla_status s);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_KV04_H */

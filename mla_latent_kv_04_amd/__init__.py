@@ -1,0 +1,223 @@
+"""Absorbed MLA decode over a paged latent cache on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libmla_kv04.so`` (see include/mla.h).
+Tensors are torch tensors on the current HIP device: bf16 (or int16/uint16 bit
+views) for activations, weights and the cache, int32 for block tables and
+lengths.  Every call enqueues HIP kernels on the current torch stream; torch is
+used only for device memory and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+from . import _lib
+from ._lib import DecodeParams, MlaError  # noqa: F401
+
+NUM_HEADS = 128
+D_HC = 128
+D_C = 512
+D_R = 64
+PAGE = 64
+DEFAULT_SCALE = 1.0 / math.sqrt(D_HC + D_R)
+
+__all__ = [
+    "absorb_q", "decode_paged", "up_proj", "decode", "gather_kv", "workspace_size", "make_params",
+    "device_cu_count", "MlaError", "DecodeParams", "KernelTimer",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream() -> int:
+    torch = _torch()
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t, name, dtypes, shape=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _bf16_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _i32():
+    return (_torch().int32,)
+
+
+def make_params(batch: int, s_q: int, max_blocks_per_seq: int, num_pages: int, scale: float = DEFAULT_SCALE,
+                num_splits: int = 0) -> DecodeParams:
+    p = DecodeParams()
+    p.batch, p.s_q, p.num_heads, p.page_size = batch, s_q, NUM_HEADS, PAGE
+    p.max_blocks_per_seq, p.num_splits, p.num_pages, p.scale, p.reserved = (
+        max_blocks_per_seq, num_splits, num_pages, scale, 0)
+    return p
+
+
+def device_cu_count() -> int:
+    lib = _lib.load()
+    n = ctypes.c_int32(0)
+    _lib.check(lib.mla_device_cu_count(ctypes.byref(n)), "mla_device_cu_count")
+    return int(n.value)
+
+
+def workspace_size(params: DecodeParams, fused: bool = False) -> int:
+    lib = _lib.load()
+    n = lib.mla_decode_workspace_size(ctypes.byref(params), 1 if fused else 0)
+    if n == 0:
+        raise MlaError(_lib.MLA_ERR_INVALID_ARG, "mla_decode_workspace_size", lib.mla_last_error().decode())
+    return int(n)
+
+
+def _workspace(params, fused, workspace):
+    torch = _torch()
+    need = workspace_size(params, fused)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
+    return workspace, need
+
+
+def absorb_q(q_c, w_uk, out=None):
+    """q_abs[t, h, :] = q_c[t, h, :] . W_UK[h];  q_c [..., 128, 128], w_uk [128, 128, 512]."""
+    torch = _torch()
+    lead = q_c.shape[:-2]
+    tokens = int(math.prod(lead))
+    if out is None:
+        out = torch.empty(*lead, NUM_HEADS, D_C, dtype=torch.bfloat16, device=q_c.device)
+    lib = _lib.load()
+    st = lib.mla_absorb_q(_ptr(q_c, "q_c", _bf16_types(), (*lead, NUM_HEADS, D_HC)),
+                          _ptr(w_uk, "w_uk", _bf16_types(), (NUM_HEADS, D_HC, D_C)),
+                          _ptr(out, "q_abs", _bf16_types(), (*lead, NUM_HEADS, D_C)), tokens, NUM_HEADS, _stream())
+    _lib.check(st, "mla_absorb_q")
+    return out
+
+
+def up_proj(out_latent, w_uv, out=None):
+    """out[t, h, :] = out_latent[t, h, :] . W_UV[h];  w_uv [128, 512, 128]."""
+    torch = _torch()
+    lead = out_latent.shape[:-2]
+    tokens = int(math.prod(lead))
+    if out is None:
+        out = torch.empty(*lead, NUM_HEADS, D_HC, dtype=torch.bfloat16, device=out_latent.device)
+    lib = _lib.load()
+    st = lib.mla_up_proj(_ptr(out_latent, "out_latent", _bf16_types(), (*lead, NUM_HEADS, D_C)),
+                         _ptr(w_uv, "w_uv", _bf16_types(), (NUM_HEADS, D_C, D_HC)),
+                         _ptr(out, "out", _bf16_types(), (*lead, NUM_HEADS, D_HC)), tokens, NUM_HEADS, _stream())
+    _lib.check(st, "mla_up_proj")
+    return out
+
+
+def decode_paged(q_abs, q_r, kv_blocks, block_table, seqlens, *, scale=DEFAULT_SCALE, num_splits=0,
+                 out_latent=None, lse=None, want_lse=True, workspace=None):
+    """Paged latent-space decode.  q_abs [B, s_q, 128, 512], q_r [B, s_q, 128, 64],
+    kv_blocks [P, 64, 576], block_table [B, max_blocks] int32, seqlens [B] int32.
+    Returns (out_latent [B, s_q, 128, 512] bf16, lse [B, s_q, 128] fp32 or None)."""
+    torch = _torch()
+    B, s_q = int(q_abs.shape[0]), int(q_abs.shape[1])
+    P = int(kv_blocks.shape[0])
+    mb = int(block_table.shape[1])
+    params = make_params(B, s_q, mb, P, scale, num_splits)
+    if out_latent is None:
+        out_latent = torch.empty(B, s_q, NUM_HEADS, D_C, dtype=torch.bfloat16, device=q_abs.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, s_q, NUM_HEADS, dtype=torch.float32, device=q_abs.device)
+    workspace, need = _workspace(params, False, workspace)
+    lib = _lib.load()
+    st = lib.mla_decode_paged(
+        _ptr(q_abs, "q_abs", _bf16_types(), (B, s_q, NUM_HEADS, D_C)),
+        _ptr(q_r, "q_r", _bf16_types(), (B, s_q, NUM_HEADS, D_R)),
+        _ptr(kv_blocks, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R)),
+        _ptr(block_table, "block_table", _i32(), (B, mb)), _ptr(seqlens, "seqlens", _i32(), (B,)),
+        _ptr(out_latent, "out_latent", _bf16_types(), (B, s_q, NUM_HEADS, D_C)),
+        _ptr(lse, "lse", (torch.float32,), (B, s_q, NUM_HEADS)), ctypes.byref(params),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream())
+    _lib.check(st, "mla_decode_paged")
+    return out_latent, lse
+
+
+def decode(q_c, q_r, w_uk, w_uv, kv_blocks, block_table, seqlens, *, scale=DEFAULT_SCALE, num_splits=0, out=None,
+           lse=None, want_lse=True, workspace=None):
+    """Fused decode step (absorb -> paged decode -> merge -> up-projection).
+    Returns (out [B, s_q, 128, 128] bf16, lse [B, s_q, 128] fp32 or None)."""
+    torch = _torch()
+    B, s_q = int(q_c.shape[0]), int(q_c.shape[1])
+    P = int(kv_blocks.shape[0])
+    mb = int(block_table.shape[1])
+    params = make_params(B, s_q, mb, P, scale, num_splits)
+    if out is None:
+        out = torch.empty(B, s_q, NUM_HEADS, D_HC, dtype=torch.bfloat16, device=q_c.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, s_q, NUM_HEADS, dtype=torch.float32, device=q_c.device)
+    workspace, need = _workspace(params, True, workspace)
+    lib = _lib.load()
+    st = lib.mla_decode(
+        _ptr(q_c, "q_c", _bf16_types(), (B, s_q, NUM_HEADS, D_HC)),
+        _ptr(q_r, "q_r", _bf16_types(), (B, s_q, NUM_HEADS, D_R)),
+        _ptr(w_uk, "w_uk", _bf16_types(), (NUM_HEADS, D_HC, D_C)),
+        _ptr(w_uv, "w_uv", _bf16_types(), (NUM_HEADS, D_C, D_HC)),
+        _ptr(kv_blocks, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R)),
+        _ptr(block_table, "block_table", _i32(), (B, mb)), _ptr(seqlens, "seqlens", _i32(), (B,)),
+        _ptr(out, "out", _bf16_types(), (B, s_q, NUM_HEADS, D_HC)),
+        _ptr(lse, "lse", (torch.float32,), (B, s_q, NUM_HEADS)), ctypes.byref(params),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream())
+    _lib.check(st, "mla_decode")
+    return out, lse
+
+
+class KernelTimer:
+    """Per-kernel HIP-event timing of decode calls (library hook; see mla_profile_enable).
+
+    with KernelTimer() as kt: ...calls...;  kt.ms -> dict of summed milliseconds, kt.calls."""
+
+    NAMES = ("absorb", "plan", "decode", "combine", "up_proj")
+
+    def __enter__(self):
+        lib = _lib.load()
+        _lib.check(lib.mla_profile_enable(1), "mla_profile_enable")
+        return self
+
+    def __exit__(self, *exc):
+        lib = _lib.load()
+        ms = (ctypes.c_double * 5)()
+        calls = ctypes.c_int32(0)
+        st = lib.mla_profile_collect(ms, ctypes.byref(calls))
+        lib.mla_profile_enable(0)
+        _lib.check(st, "mla_profile_collect")
+        self.ms = dict(zip(self.NAMES, list(ms)))
+        self.calls = int(calls.value)
+        return False
+
+
+def gather_kv(kv_blocks, block_table, seqlens, out=None):
+    """Dense copy of the paged cache: [B, max_blocks * 64, 576], zero past each length."""
+    torch = _torch()
+    B = int(block_table.shape[0])
+    mb = int(block_table.shape[1])
+    P = int(kv_blocks.shape[0])
+    if out is None:
+        out = torch.empty(B, mb * PAGE, D_C + D_R, dtype=torch.bfloat16, device=kv_blocks.device)
+    params = make_params(B, 1, mb, P)
+    lib = _lib.load()
+    st = lib.mla_gather_kv(_ptr(kv_blocks, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R)),
+                           _ptr(block_table, "block_table", _i32(), (B, mb)), _ptr(seqlens, "seqlens", _i32(), (B,)),
+                           _ptr(out, "dense", _bf16_types(), (B, mb * PAGE, D_C + D_R)), ctypes.byref(params),
+                           _stream())
+    _lib.check(st, "mla_gather_kv")
+    return out

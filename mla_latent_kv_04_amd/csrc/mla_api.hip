@@ -1,0 +1,312 @@
+// C-ABI entry points: host-side validation, workspace layout, kernel launches.
+// Nothing here allocates device memory or synchronises; every call enqueues on
+// the caller's stream and returns.
+#include <stdarg.h>
+#include <string.h>
+
+#include <array>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/mla.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status fail(mla_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mla_status fail(mla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mla_status ok() {
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+mla_status hip_fail(hipError_t e, const char* what) {
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+mla_status check_params(const mla_decode_params* p) {
+  if (p == nullptr) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch %d < 0", p->batch);
+  if (p->s_q != 1 && p->s_q != 2) return fail(MLA_ERR_UNSUPPORTED, "s_q %d (supported: 1, 2)", p->s_q);
+  if (p->num_heads != mla::kHeads) return fail(MLA_ERR_UNSUPPORTED, "num_heads %d (supported: 128)", p->num_heads);
+  if (p->page_size != mla::kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size %d (supported: 64)", p->page_size);
+  if (p->max_blocks_per_seq < 1) return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", p->max_blocks_per_seq);
+  if (p->max_blocks_per_seq > (1 << 24)) return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_seq too large");
+  if (p->num_splits < 0 || p->num_splits > (1 << 16)) return fail(MLA_ERR_INVALID_ARG, "num_splits %d", p->num_splits);
+  if (p->num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages %lld < 1", (long long)p->num_pages);
+  if (!(p->scale > 0.f) || p->scale > 1e30f) return fail(MLA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (p->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "reserved must be 0");
+  if ((int64_t)p->batch * p->s_q > (1 << 24)) return fail(MLA_ERR_INVALID_ARG, "batch * s_q too large");
+  return MLA_OK;
+}
+
+mla_status resolve_wgs(const mla_decode_params* p, int* wgs) {
+  if (p->num_splits > 0) {
+    *wgs = p->num_splits;
+    return MLA_OK;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+  if (cus <= 0) return fail(MLA_ERR_HIP, "device reports %d compute units", cus);
+  *wgs = cus;
+  return MLA_OK;
+}
+
+struct WsLayout {
+  size_t cum, part_lse, part_o, q_abs, out_latent, total;
+};
+
+WsLayout layout(const mla_decode_params* p, int wgs, bool fused) {
+  const size_t units = (size_t)p->batch * p->s_q;
+  WsLayout L;
+  size_t off = 0;
+  L.cum = off;
+  off += round_up((units + 1) * sizeof(int32_t));
+  L.part_lse = off;
+  off += round_up((size_t)2 * wgs * mla::kHeads * sizeof(float));
+  L.part_o = off;
+  off += round_up((size_t)2 * wgs * mla::kHeads * mla::kLatent * sizeof(float));
+  L.q_abs = off;
+  if (fused) off += round_up(units * mla::kHeads * mla::kLatent * 2);
+  L.out_latent = off;
+  if (fused) off += round_up(units * mla::kHeads * mla::kLatent * 2);
+  L.total = off;
+  return L;
+}
+
+
+// Opt-in kernel timing for benchmarks: HIP events recorded on the caller's
+// stream around each kernel of a decode call.  Slot layout: 0 start,
+// 1 absorb done, 2 plan done, 3 decode done, 4 combine done, 5 up-proj done.
+struct Profiler {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<std::array<hipEvent_t, 6>> ev;
+  size_t used = 0;
+};
+Profiler g_prof;
+constexpr size_t kMaxProfiledCalls = 1 << 16;
+
+hipEvent_t* prof_slot() {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.enabled || g_prof.used >= kMaxProfiledCalls) return nullptr;
+  if (g_prof.used == g_prof.ev.size()) {
+    std::array<hipEvent_t, 6> e{};
+    for (auto& x : e)
+      if (hipEventCreate(&x) != hipSuccess) return nullptr;
+    g_prof.ev.push_back(e);
+  }
+  return g_prof.ev[g_prof.used++].data();
+}
+
+mla_status run_paged(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv, const int32_t* bt,
+                     const int32_t* seqlens, uint16_t* out_latent, float* lse, const mla_decode_params* p,
+                     unsigned char* ws, const WsLayout& L, int wgs, hipStream_t s, hipEvent_t* ev) {
+  mla::DecodePlanView plan;
+  plan.cum = reinterpret_cast<int32_t*>(ws + L.cum);
+  plan.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
+  plan.part_o = reinterpret_cast<float*>(ws + L.part_o);
+  hipError_t e = mla::launch_decode(q_abs, q_r, kv, bt, seqlens, out_latent, lse, p->batch, p->s_q,
+                                    p->max_blocks_per_seq, p->num_pages, p->scale, wgs, plan, s,
+                                    ev ? ev[2] : nullptr, ev ? ev[3] : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (ev != nullptr && (e = hipEventRecord(ev[4], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_MISALIGNED: return "MLA_ERR_MISALIGNED";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+mla_status mla_device_cu_count(int32_t* num_cus) {
+  if (num_cus == nullptr) return fail(MLA_ERR_INVALID_ARG, "num_cus is NULL");
+  mla_decode_params p{};
+  p.num_splits = 0;
+  int w = 0;
+  mla_status st = resolve_wgs(&p, &w);
+  if (st != MLA_OK) return st;
+  *num_cus = w;
+  return ok();
+}
+
+mla_status mla_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_abs, int32_t tokens,
+                        int32_t num_heads, void* stream) {
+  if (tokens < 0) return fail(MLA_ERR_INVALID_ARG, "tokens %d < 0", tokens);
+  if (num_heads != mla::kHeads) return fail(MLA_ERR_UNSUPPORTED, "num_heads %d (supported: 128)", num_heads);
+  if (tokens == 0) return ok();
+  if (!q_c || !w_uk || !q_abs) return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q_c) || !aligned16(w_uk) || !aligned16(q_abs)) return fail(MLA_ERR_MISALIGNED, "tensor not 16-byte aligned");
+  hipError_t e = mla::launch_absorb_q(q_c, w_uk, q_abs, tokens, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "absorb_q launch");
+  return ok();
+}
+
+mla_status mla_up_proj(const uint16_t* out_latent, const uint16_t* w_uv, uint16_t* out, int32_t tokens,
+                       int32_t num_heads, void* stream) {
+  if (tokens < 0) return fail(MLA_ERR_INVALID_ARG, "tokens %d < 0", tokens);
+  if (num_heads != mla::kHeads) return fail(MLA_ERR_UNSUPPORTED, "num_heads %d (supported: 128)", num_heads);
+  if (tokens == 0) return ok();
+  if (!out_latent || !w_uv || !out) return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(out_latent) || !aligned16(w_uv) || !aligned16(out)) return fail(MLA_ERR_MISALIGNED, "tensor not 16-byte aligned");
+  hipError_t e = mla::launch_up_proj(out_latent, w_uv, out, tokens, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "up_proj launch");
+  return ok();
+}
+
+size_t mla_decode_workspace_size(const mla_decode_params* p, int32_t fused) {
+  if (check_params(p) != MLA_OK) return 0;
+  int wgs = 0;
+  if (resolve_wgs(p, &wgs) != MLA_OK) return 0;
+  return layout(p, wgs, fused != 0).total;
+}
+
+mla_status mla_decode_paged(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv_blocks,
+                            const int32_t* block_table, const int32_t* seqlens, uint16_t* out_latent, float* lse,
+                            const mla_decode_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (p->batch == 0) return ok();
+  if (!q_abs || !q_r || !kv_blocks || !block_table || !seqlens || !out_latent)
+    return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q_abs) || !aligned16(q_r) || !aligned16(kv_blocks) || !aligned16(block_table) ||
+      !aligned16(out_latent) || !aligned16(workspace) || (reinterpret_cast<uintptr_t>(seqlens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(MLA_ERR_MISALIGNED, "tensor or workspace not aligned (16 B; seqlens and lse 4 B)");
+  int wgs = 0;
+  st = resolve_wgs(p, &wgs);
+  if (st != MLA_OK) return st;
+  const WsLayout L = layout(p, wgs, false);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = prof_slot();
+  if (ev != nullptr) {
+    hipError_t e = hipEventRecord(ev[0], s);
+    if (e == hipSuccess) e = hipEventRecord(ev[1], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  st = run_paged(q_abs, q_r, kv_blocks, block_table, seqlens, out_latent, lse, p,
+                 static_cast<unsigned char*>(workspace), L, wgs, s, ev);
+  if (st == MLA_OK && ev != nullptr) {
+    hipError_t e = hipEventRecord(ev[5], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  return st == MLA_OK ? ok() : st;
+}
+
+mla_status mla_decode(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* w_uk, const uint16_t* w_uv,
+                      const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens, uint16_t* out,
+                      float* lse, const mla_decode_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (p->batch == 0) return ok();
+  if (!q_c || !q_r || !w_uk || !w_uv || !kv_blocks || !block_table || !seqlens || !out)
+    return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q_c) || !aligned16(q_r) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(kv_blocks) ||
+      !aligned16(block_table) || !aligned16(out) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(seqlens) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(MLA_ERR_MISALIGNED, "tensor or workspace not aligned (16 B; seqlens and lse 4 B)");
+  int wgs = 0;
+  st = resolve_wgs(p, &wgs);
+  if (st != MLA_OK) return st;
+  const WsLayout L = layout(p, wgs, true);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int tokens = p->batch * p->s_q;
+  uint16_t* q_abs = reinterpret_cast<uint16_t*>(ws + L.q_abs);
+  uint16_t* ol = reinterpret_cast<uint16_t*>(ws + L.out_latent);
+  hipEvent_t* ev = prof_slot();
+  hipError_t e;
+  if (ev != nullptr && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = mla::launch_absorb_q(q_c, w_uk, q_abs, tokens, s);
+  if (e != hipSuccess) return hip_fail(e, "absorb_q launch");
+  if (ev != nullptr && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  st = run_paged(q_abs, q_r, kv_blocks, block_table, seqlens, ol, lse, p, ws, L, wgs, s, ev);
+  if (st != MLA_OK) return st;
+  e = mla::launch_up_proj(ol, w_uv, out, tokens, s);
+  if (e != hipSuccess) return hip_fail(e, "up_proj launch");
+  if (ev != nullptr && (e = hipEventRecord(ev[5], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return ok();
+}
+
+mla_status mla_profile_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.enabled = enable != 0;
+  g_prof.used = 0;
+  return ok();
+}
+
+mla_status mla_profile_collect(double* ms, int32_t* calls) {
+  if (ms == nullptr || calls == nullptr) return fail(MLA_ERR_INVALID_ARG, "NULL output pointer");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (int k = 0; k < 5; ++k) ms[k] = 0.0;
+  for (size_t i = 0; i < g_prof.used; ++i) {
+    auto& e = g_prof.ev[i];
+    hipError_t r = hipEventSynchronize(e[5]);
+    if (r != hipSuccess) return hip_fail(r, "hipEventSynchronize");
+    for (int k = 0; k < 5; ++k) {
+      float t = 0.f;
+      r = hipEventElapsedTime(&t, e[k], e[k + 1]);
+      if (r != hipSuccess) return hip_fail(r, "hipEventElapsedTime");
+      ms[k] += t;
+    }
+  }
+  *calls = (int32_t)g_prof.used;
+  g_prof.used = 0;
+  return ok();
+}
+
+mla_status mla_gather_kv(const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens,
+                         uint16_t* dense, const mla_decode_params* p, void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (p->batch == 0) return ok();
+  if (!kv_blocks || !block_table || !seqlens || !dense) return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(kv_blocks) || !aligned16(dense) || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seqlens) & 3u))
+    return fail(MLA_ERR_MISALIGNED, "tensor not aligned");
+  hipError_t e = mla::launch_gather(kv_blocks, block_table, seqlens, dense, p->batch, p->max_blocks_per_seq,
+                                    p->num_pages, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,179 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bar: block-table gathers bit-exact; floating outputs within
+max|gpu - ref| <= 1e-2 * max|ref| + 2e-3 per output tensor; lse within 2e-3 when
+both sides score with the same bf16 q_abs, and within the derived bf16-rounding
+bound of scale * 2^-8 * sum|q_abs c| (+2e-3) against the unrounded definition.
+Paged-decode parity feeds both sides the same bf16 q_abs (RNE of the exact
+q_c . W_UK); the fused path is checked against the decompress oracle."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import make_custom, make_inputs, poison_unused
+
+from ._gpu import (LSE_ATOL, absorbed_inputs, assert_close, dev_bf16, dev_i32, host_bits, host_f64,
+                   lse_bound_for_rounded_q, require_gpu, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+import mla_latent_kv_04_amd as mla  # noqa: E402
+
+
+def _print_case(name, inp):
+    print(f"[case] {name} seed={inp.seed} B={inp.batch} s_q={inp.s_q} L={list(inp.seqlens[:8])}"
+          f"{'...' if inp.batch > 8 else ''} pages={inp.num_pages}", flush=True)
+
+
+def _paged(inp, d, qa_bits, num_splits=0):
+    qa = dev_bf16(qa_bits)
+    ol, lse = mla.decode_paged(qa, d["q_r"], d["pool"], d["bt"], d["sl"], scale=inp.scale, num_splits=num_splits)
+    import torch
+    torch.cuda.synchronize()
+    return ol, lse
+
+
+# ------------------------------------------------------------------ gather
+
+@pytest.mark.parametrize("seqlens", [[1, 64, 65, 300], [4096] * 3])
+def test_gather_bit_exact(seqlens):
+    inp = make_custom(21, len(seqlens), 1, seqlens, extra_blocks=1)
+    _print_case("gather", inp)
+    d = upload(inp)
+    dense = host_bits(mla.gather_kv(d["pool"], d["bt"], d["sl"]))
+    mb = inp.max_blocks
+    want = np.zeros((inp.batch, mb * 64, 576), dtype=np.uint16)
+    for b in range(inp.batch):
+        L = int(inp.seqlens[b])
+        want[b, :L] = oracle.gather_rows(inp.pool, inp.block_table, b, L)
+    assert np.array_equal(dense, want)
+
+
+# ------------------------------------------------------------------ projections
+
+@pytest.mark.parametrize("tokens", [1, 17, 64, 130])
+def test_absorb_q(tokens):
+    inp = make_custom(22, tokens, 1, [1] * tokens)
+    d = upload(inp)
+    got = host_f64(mla.absorb_q(d["q_c"], d["w_uk"]))
+    ref = oracle.absorb_q(inp.q_c, inp.w_uk)
+    assert_close(got, ref, "q_abs")
+    # tighter: each value is the bf16 rounding of an fp32 sum of 128 products
+    assert np.max(np.abs(got - ref) / (np.abs(ref) + 1e-3)) < 2 ** -7
+
+
+@pytest.mark.parametrize("tokens", [1, 17, 64, 130])
+def test_up_proj(tokens):
+    inp = make_custom(23, tokens, 1, [1] * tokens)
+    rng = np.random.default_rng(5)
+    ol_bits = oracle.f64_to_bf16_bits(rng.standard_normal((tokens, 1, 128, 512)))
+    d = upload(inp)
+    got = host_f64(mla.up_proj(dev_bf16(ol_bits), d["w_uv"]))
+    ref = oracle.up_proj(ol_bits, inp.w_uv)
+    assert_close(got, ref, "out")
+    assert np.max(np.abs(got - ref) / (np.abs(ref) + 1e-3)) < 2 ** -7
+
+
+# ------------------------------------------------------------------ paged decode, small ragged cases
+
+SMALL = [
+    (31, 1, [1, 65, 200]),
+    (32, 2, [2, 64, 130]),
+    (33, 1, [64, 128, 63, 1000, 7]),
+    (34, 2, [3, 65, 640]),
+    (35, 1, [2500]),
+]
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 3, 40])
+@pytest.mark.parametrize("seed,s_q,seqlens", SMALL)
+def test_decode_paged_small(seed, s_q, seqlens, num_splits):
+    inp = make_custom(seed, len(seqlens), s_q, seqlens, extra_blocks=2)
+    _print_case(f"paged splits={num_splits}", inp)
+    d = upload(inp)
+    qa = absorbed_inputs(inp)
+    ol, lse = _paged(inp, d, qa, num_splits)
+    ref_ol, ref_lse = oracle.decode_absorbed(qa, inp.q_r, inp.pool, inp.block_table, inp.seqlens, s_q, inp.scale)
+    assert_close(host_f64(ol), ref_ol, "out_latent")
+    assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= LSE_ATOL
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def _sampled_check(inp, d, qa, ol, lse, batches):
+    ref_ol, ref_lse = oracle.decode_absorbed(qa, inp.q_r, inp.pool, inp.block_table, inp.seqlens, inp.s_q,
+                                             inp.scale, batches=batches)
+    got = host_f64(ol)[batches]
+    assert_close(got, ref_ol, "out_latent")
+    assert np.max(np.abs(lse.double().cpu().numpy()[batches] - ref_lse)) <= LSE_ATOL
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_workload_full_check(name):
+    inp = make_inputs(name)
+    _print_case(name, inp)
+    d = upload(inp)
+    qa = absorbed_inputs(inp)
+    ol, lse = _paged(inp, d, qa)
+    _sampled_check(inp, d, qa, ol, lse, list(range(inp.batch)))
+
+
+@pytest.mark.parametrize("name", ["c3", "c5"])
+def test_workload_sampled_check(name):
+    inp = make_inputs(name)
+    _print_case(name, inp)
+    d = upload(inp)
+    qa = absorbed_inputs(inp)
+    ol, lse = _paged(inp, d, qa)
+    L = inp.seqlens
+    batches = sorted({int(np.argmin(L)), int(np.argmax(L)), inp.batch // 2})
+    _sampled_check(inp, d, qa, ol, lse, batches)
+
+
+# ------------------------------------------------------------------ fused path vs the decompress definition
+
+def test_fused_c1_all_heads():
+    inp = make_inputs("c1")
+    _print_case("fused c1", inp)
+    d = upload(inp)
+    out, lse = mla.decode(d["q_c"], d["q_r"], d["w_uk"], d["w_uv"], d["pool"], d["bt"], d["sl"], scale=inp.scale)
+    ref, ref_lse = oracle.decode_decompressed(inp.q_c, inp.q_r, inp.w_uk, inp.w_uv, inp.pool, inp.block_table,
+                                              inp.seqlens, 1, inp.scale)
+    assert_close(host_f64(out), ref, "out")
+    # the fused path scores with bf16 q_abs: lse against the unrounded definition within the derived bound
+    assert np.all(np.abs(lse.double().cpu().numpy() - ref_lse) <= lse_bound_for_rounded_q(inp))
+
+
+@pytest.mark.parametrize("seed,s_q,seqlens", [(41, 2, [2, 77, 300]), (42, 1, [1, 4096, 129])])
+def test_fused_small_vs_decompressed(seed, s_q, seqlens):
+    inp = make_custom(seed, len(seqlens), s_q, seqlens)
+    d = upload(inp)
+    out, lse = mla.decode(d["q_c"], d["q_r"], d["w_uk"], d["w_uv"], d["pool"], d["bt"], d["sl"], scale=inp.scale,
+                          num_splits=5)
+    heads = [0, 1, 31, 32, 77, 127]
+    ref, ref_lse = oracle.decode_decompressed(inp.q_c, inp.q_r, inp.w_uk, inp.w_uv, inp.pool, inp.block_table,
+                                              inp.seqlens, s_q, inp.scale, heads=heads)
+    got = host_f64(out)[:, :, heads]
+    assert_close(got, ref, "out")
+    bound = lse_bound_for_rounded_q(inp, heads=heads)
+    assert np.all(np.abs(lse.double().cpu().numpy()[:, :, heads] - ref_lse) <= bound)
+
+
+def test_fused_c2_sampled_heads():
+    inp = make_inputs("c2")
+    d = upload(inp)
+    out, _ = mla.decode(d["q_c"], d["q_r"], d["w_uk"], d["w_uv"], d["pool"], d["bt"], d["sl"], scale=inp.scale)
+    batches, heads = [0, 7, 15], [0, 45, 127]
+    ref, _ = oracle.decode_decompressed(inp.q_c, inp.q_r, inp.w_uk, inp.w_uv, inp.pool, inp.block_table,
+                                        inp.seqlens, 1, inp.scale, batches=batches, heads=heads)
+    got = host_f64(out)[batches][:, :, heads]
+    assert_close(got, ref, "out")
