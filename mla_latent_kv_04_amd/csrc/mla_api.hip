@@ -10,7 +10,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/mla.h"
+#include "mla.h"
 #include "common.h"
 
 namespace {
