@@ -46,8 +46,12 @@ __device__ __forceinline__ float bf2f(uint16_t b) {
 }
 
 // Two fp32 -> packed pair of bf16 (low half = a).
+// Round-to-nearest-even of two floats into one register (a in the low half); a
+// two-element vector conversion maps onto the single packed conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f2bf(a)) | (static_cast<uint32_t>(f2bf(b)) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 __device__ __forceinline__ f32x16 mfma32(const s16x8& a, const s16x8& b, const f32x16& c) {

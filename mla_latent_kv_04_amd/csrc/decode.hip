@@ -14,14 +14,14 @@
 // range borders leaves one normalised partial per piece (slot 2g for the first
 // segment of workgroup g, 2g+1 for its last), merged by log-sum-exp afterwards.
 //
-// Workgroup: 256 threads = 4 waves, one per SIMD.  Each page (64 tokens x
-// 1152 B = 72 KiB) is copied HBM -> LDS with direct 16-byte loads
-// (global_load_lds_dwordx4), double buffered (2 x 72 KiB), plus a 16 KiB P
-// buffer: the 160 KiB of LDS exactly.  Wave w computes the scores of heads
+// Workgroup: 256 threads = 4 waves, one per SIMD.  Pages are processed as
+// 32-token tiles (36 KiB) copied HBM -> LDS with direct 16-byte loads
+// (global_load_lds_dwordx4) two tiles ahead into a 4-slot ring, plus two 8 KiB
+// P buffers: the 160 KiB of LDS exactly.  Wave w computes the scores of heads
 // 32w..32w+31 (its 32 queries live in 144 VGPRs) and the output of all heads
 // for latent columns 128w..128w+127 (256 accumulator registers for the whole
-// segment); see decode_kernel for the per-page steps.
-// LDS layout of a page: a latent region of token rows (64 sixteen-byte chunks)
+// segment); see decode_kernel for the per-tile steps.
+// LDS layout of a tile: a latent region of token rows (64 sixteen-byte chunks)
 // and a RoPE region (8 chunks per token), each with an XOR swizzle of the chunk
 // index that keeps both the row reads of QK (16 tokens, one chunk) and the
 // 4-row transposing reads of PV free of bank conflicts.
@@ -32,8 +32,6 @@ namespace mla {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLoadsPerThread = kChunksPerPage / kThreads;  // 18 direct loads per thread per page
-static_assert(kChunksPerPage % kThreads == 0, "page must split evenly over the workgroup");
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct DecodeArgs {
@@ -109,26 +107,33 @@ void plan_kernel(DecodeArgs a, int32_t* cum) {
 
 // ---------------------------------------------------------------------------- decode
 
-// LDS page buffer (73728 B): latent region [64 tokens][1024 B] at offset 0,
-// RoPE region [64 tokens][128 B] at offset 65536, both swizzled as above.
-constexpr int kRopeRegion = kPage * kLatent * 2;  // 65536
+// The pages are processed in tiles of 32 tokens (half a page, 36 KiB).  LDS:
+// a ring of 4 tile slots (4 x 36 KiB) and two P buffers (2 x 8 KiB): the
+// 160 KiB of LDS exactly.  Tile slot layout: latent region [32 tokens][1024 B]
+// at offset 0, RoPE region [32 tokens][128 B] at offset 32768, both swizzled as
+// above.
+constexpr int kTile = 32;
+constexpr int kTileBytes = kTile * kRowBytes;        // 36864
+constexpr int kRopeRegion = kTile * kLatent * 2;     // 32768
+constexpr int kSlots = 4;
+constexpr int kPBytes = kHeads * kTile * 2;          // 8192: P of one tile, [128 heads][32 tokens] bf16
+constexpr int kLoadsPerTile = kTileBytes / 16 / kThreads;   // 9 direct loads per thread per tile
+static_assert(kTileBytes % (16 * kThreads) == 0, "tile must split evenly over the workgroup");
 
-// Page copy HBM -> LDS: wave w copies the latent rows of tokens w, w+4, ...,
-// w+60 (one 64-lane direct load per row, lane l = chunk position l) and the
-// RoPE rows of tokens 16w .. 16w+15 (two loads; lane l -> token 8j + l/8,
-// chunk position l%8).  The per-lane global byte offsets below are constant.
-struct PageLoadOffsets {
-  uint32_t lat[4];    // latent row offset for tokens t with t % 16 == w + 4k
-  uint32_t rope[2];   // RoPE offsets (relative to token 8j) for j = 2w, 2w+1
+// Tile copy HBM -> LDS: wave w copies the latent rows of tokens w, w+4, ...,
+// w+28 (one 64-lane direct load per row, lane l = chunk position l) and the
+// RoPE rows of tokens 8w .. 8w+7 (one load; lane l -> token 8w + l/8, chunk
+// position l%8).  The per-lane global byte offsets below are constant.
+struct TileLoadOffsets {
+  uint32_t lat[4];   // latent row offset for tokens t with t % 16 == w + 4k
+  uint32_t rope;     // RoPE offset relative to token 8w
 };
 
-__device__ __forceinline__ PageLoadOffsets page_load_offsets(int lane, int wave_u) {
-  PageLoadOffsets o;
+__device__ __forceinline__ TileLoadOffsets tile_load_offsets(int lane, int wave_u) {
+  TileLoadOffsets o;
 #pragma unroll
   for (int k = 0; k < 4; ++k) o.lat[k] = (uint32_t)((lane ^ swz_lat(wave_u + 4 * k)) * 16);
-  const int tr = lane >> 3, pr = lane & 7;
-#pragma unroll
-  for (int j2 = 0; j2 < 2; ++j2) o.rope[j2] = (uint32_t)(tr * kRowBytes + kLatent * 2 + (pr ^ ((4 * j2 + (lane >> 4)) & 7)) * 16);
+  o.rope = (uint32_t)((lane >> 3) * kRowBytes + kLatent * 2 + ((lane & 7) ^ ((4 * wave_u + (lane >> 4)) & 7)) * 16);
   return o;
 }
 
@@ -136,14 +141,13 @@ __device__ __forceinline__ PageLoadOffsets page_load_offsets(int lane, int wave_
 // reads sbase + voff and its 16 bytes land at LDS byte address lds + 16 l.
 // Issued as inline asm so the compiler's wait-count model does not see the
 // LDS write: it would otherwise wait for every load in flight (including the
-// prefetch of the next page) before each LDS read.  The kernel waits for
+// prefetch of the next tiles) before each LDS read.  The kernel waits for
 // these loads itself with explicit vmcnt waits.  The leading s_nop covers the
 // one wait state an M0 write needs before an LDS DMA instruction.  The cache
 // is read once, so the loads are non-temporal: with `nt` the page stream runs
-// at about 7.0 TB/s on MI355X, without it at about 6.2 TB/s.
-// No "memory" clobber: the load only writes the LDS buffer that no wave reads
-// until the next page barrier, and a volatile asm is never moved across that
-// barrier; LDS reads of the current page may be scheduled around it freely.
+// at about 7.0 TB/s on MI355X, without it at about 6.2 TB/s.  No "memory"
+// clobber: the load only writes a ring slot that no wave reads until a later
+// tile barrier, and a volatile asm is never moved across that barrier.
 __device__ __forceinline__ void dma_b128(const unsigned char* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds));
 }
@@ -152,42 +156,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(MLA_LDS const void*)p;
 }
 
-// Rows at or past `valid` (only in a sequence's last page) are fetched from
-// row 0 of the same page instead: they are masked out of the softmax, and
-// loading finite data keeps 0 * V finite even when the unused rows of the
-// cache hold NaN or Inf bit patterns.
-__device__ __forceinline__ void issue_page(const unsigned char* __restrict__ src, unsigned char* buf,
-                                           const PageLoadOffsets& off, int wave_u, int lane, int valid) {
-  const uint32_t lbase = lds_addr(buf);
+// The 9 direct loads of one tile.  Rows at or past `valid` (only in a
+// sequence's last tile) are fetched from row 0 of the tile instead: they are
+// masked out of the softmax, and loading finite data keeps 0 * V finite even
+// when the unused rows of the cache hold NaN or Inf bit patterns.
+__device__ __forceinline__ void issue_tile(const unsigned char* __restrict__ src, uint32_t lslot,
+                                           const TileLoadOffsets& off, int wave_u, int lane, int valid) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int t = wave_u + 4 * i;
     const int trow = t < valid ? t : 0;
-    dma_b128(src + trow * kRowBytes, off.lat[i & 3], lbase + t * 1024);
+    dma_b128(src + trow * kRowBytes, off.lat[i & 3], lslot + t * 1024);
   }
-#pragma unroll
-  for (int j2 = 0; j2 < 2; ++j2) {
-    const int j = 2 * wave_u + j2;
-    const uint32_t ro = (8 * j + (lane >> 3) < valid) ? 8 * j * kRowBytes + off.rope[j2]
-                                                       : (uint32_t)(kLatent * 2 + (lane & 7) * 16);
-    dma_b128(src, ro, lbase + kRopeRegion + 1024 * j);
-  }
-}
-
-// One of the 18 direct loads of a page (d = 0..15: latent row of token
-// w + 4d; d = 16, 17: RoPE rows of tokens 8j .. 8j+7, j = 2w + d - 16).
-__device__ __forceinline__ void issue_page_part(const unsigned char* __restrict__ src, uint32_t lbase,
-                                                const PageLoadOffsets& off, int wave_u, int lane, int valid, int d) {
-  if (d < 16) {
-    const int t = wave_u + 4 * d;
-    const int trow = t < valid ? t : 0;
-    dma_b128(src + trow * kRowBytes, off.lat[d & 3], lbase + t * 1024);
-  } else {
-    const int j2 = d - 16, j = 2 * wave_u + j2;
-    const uint32_t ro = (8 * j + (lane >> 3) < valid) ? 8 * j * kRowBytes + off.rope[j2]
-                                                       : (uint32_t)(kLatent * 2 + (lane & 7) * 16);
-    dma_b128(src, ro, lbase + kRopeRegion + 1024 * j);
-  }
+  const uint32_t ro = (8 * wave_u + (lane >> 3) < valid) ? 8 * wave_u * kRowBytes + off.rope
+                                                          : (uint32_t)(kLatent * 2 + (lane & 7) * 16);
+  dma_b128(src, ro, lslot + kRopeRegion + 1024 * wave_u);
 }
 
 // The lane id through an opaque move: address offsets derived from it are
@@ -200,7 +183,7 @@ __device__ __forceinline__ int opaque_lane() {
 }
 
 // Softmax reference.  Each segment takes its per-head reference maximum from
-// its first page and keeps it: P = 2^(s - m_ref) in log2 units, so the O
+// its first tile and keeps it: P = 2^(s - m_ref) in log2 units, so the O
 // accumulators are never rescaled and any wave may accumulate any head.  A
 // later score more than kHeadroom above the reference (P beyond 2^64, far
 // outside real attention logits) makes the workgroup redo the segment once
@@ -208,23 +191,36 @@ __device__ __forceinline__ int opaque_lane() {
 // cannot overflow.
 constexpr float kHeadroom = 64.0f;
 
-// Per page (64 tokens) and wave w:
-//   QK  S^T[64 tokens, heads 32w..32w+31] over K = 576 (72 MFMAs, A = page rows from
-//       LDS, B = queries in registers); the next page's 18 direct loads are issued
-//       between these MFMAs;
-//   softmax of those 32 heads, P written as bf16 to the LDS P buffer [128 heads][64];
-//   barrier;
-//   PV  O[all 128 heads, latent columns 128w..128w+127] += P . c_KV (64 MFMAs, A = P
-//       from LDS, B = page columns via transposing reads).
-// Sharing P through LDS halves the PV operand traffic compared with every wave
-// reading all 512 latent columns for its own heads.
+// Scalar read of a value that no kernel of the launch writes (block table,
+// sequence lengths, the plan's prefix sums): through the constant address space
+// the load is a scalar one, counted by lgkmcnt, so waiting for it never waits
+// for the tile loads in flight (a vector load would, as those share vmcnt).
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
+// Per 32-token tile k (one step) and wave w:
+//   wait for tile k, barrier (P of tile k-1 visible); issue the loads of tile k+2;
+//   QK  S^T[32 tokens, heads 32w..32w+31] over K = 576: 36 MFMAs in two chains
+//       (even / odd k-steps), A = tile rows from LDS, B = queries in registers;
+//   softmax of those heads for tile k, interleaved with
+//   PV of tile k-1: O[all 128 heads, latent columns 128w..128w+127] += P . c_KV,
+//       2 k-steps x 4 head blocks x 4 column blocks of 32x32x16 MFMAs;
+//   P of tile k (bf16) -> LDS P buffer k%2.
+// P is shared through LDS so that PV can be split by latent columns; that halves
+// the PV operand traffic compared with every wave reading all 512 columns.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kPageBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char pbuf[kHeads * kPage * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kSlots * kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char pbuf[2 * kPBytes];
 
   const int U = a.batch * a.s_q;
-  const int total = a.cum[U];
+  const int total = ld_uniform(a.cum, U);
   if (total <= 0) return;
   const int W = gridDim.x;
   const int chunk = (total + W - 1) / W;
@@ -237,227 +233,409 @@ void decode_kernel(DecodeArgs a) {
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;       // which half of the wave
   const int l32 = lane & 31;
-  const PageLoadOffsets ldo = page_load_offsets(lane, wave_u);
+  const uint32_t lbase = lds_addr(lds);
 
   // Largest u with cum[u] <= start (then cum[u+1] > start).
   int lo_u = 0, hi_u = U - 1;
   while (lo_u < hi_u) {
     const int mid = (lo_u + hi_u + 1) >> 1;
-    if (a.cum[mid] <= start) lo_u = mid; else hi_u = mid - 1;
+    if (ld_uniform(a.cum, mid) <= start) lo_u = mid; else hi_u = mid - 1;
   }
   int u = lo_u;
-
-  // P buffer row of this lane's head (writes): head 32w + l32, byte 8hi inside the chunk.
-  const int pw_off = (wave_u * 32 + l32) * 128 + 8 * hi;
-  const int ph = (l32 >> 1) & 7;
 
   bool first_seg = true;
   int pos = start;
   bool redo = false;              // re-run the current segment with m_redo as the reference
   float m_redo = -INFINITY;
   while (pos < end) {
-    while (a.cum[u + 1] <= pos) ++u;
-    const int ubeg = a.cum[u], uend = a.cum[u + 1];
+    while (ld_uniform(a.cum, u + 1) <= pos) ++u;
+    const int ubeg = ld_uniform(a.cum, u), uend = ld_uniform(a.cum, u + 1);
     const int seg_end = min(end, uend);
     const int p0 = pos - ubeg, p1 = seg_end - ubeg;
     const bool complete = (pos == ubeg) && (seg_end == uend);
     const int slot = complete ? -1 : 2 * g + (first_seg ? 0 : 1);
 
     const int b = u / a.s_q;
-    const int n_vis = unit_visible(a, u);
-    const int32_t* bt_row = a.bt + (size_t)b * a.max_blocks;
+    const int n_vis = clamp_len(ld_uniform(a.seqlens, b), a.max_blocks) - a.s_q + (u - b * a.s_q) + 1;
+    const int64_t bt_row = (int64_t)b * a.max_blocks;
+    const int tok_begin = p0 * kPage;
+    const int n_tiles = (min(n_vis, p1 * kPage) - tok_begin + kTile - 1) / kTile;   // every tile has a visible token
+
+    auto tile_src = [&](int k) -> const unsigned char* {
+      int64_t phys = ld_uniform(a.bt, bt_row + p0 + (k >> 1));
+      phys = phys < 0 ? 0 : (phys >= a.num_pages ? a.num_pages - 1 : phys);
+      return (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + (k & 1) * kTileBytes;
+    };
+    auto tile_valid = [&](int k) { return min(kTile, n_vis - tok_begin - k * kTile); };
+    auto issue = [&](int k) {
+      const TileLoadOffsets ldo = tile_load_offsets(opaque_lane(), wave_u);
+      issue_tile(tile_src(k), lbase + (k & 3) * kTileBytes, ldo, wave_u, lane, tile_valid(k));
+    };
+
+    // P buffer 1 stands for "P of tile -1" in the first step: zero it.  Its last
+    // reader (the previous segment) is behind the end-of-segment barriers.
+    *(u32x4*)(pbuf + kPBytes + 32 * tid) = u32x4{0u, 0u, 0u, 0u};
+    *(u32x4*)(pbuf + kPBytes + 32 * tid + 16) = u32x4{0u, 0u, 0u, 0u};
+
+    // Loads of the first two tiles go out before the queries, so the compiler's
+    // waits for the queries never wait for them.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // earlier stores of this workgroup
+    issue(0);
+    if (n_tiles > 1) issue(1);
 
     // Queries of this wave's 32 heads as the MFMA B operand: lane l holds head
     // 32w + l32, columns 16ks + 8hi .. +7 (k-steps 0..31 latent, 32..35 RoPE).
     const int head = wave_u * 32 + l32;
-    const uint16_t* qa = a.q_abs + ((size_t)u * kHeads + head) * kLatent + 8 * hi;
-    const uint16_t* qr = a.q_r + ((size_t)u * kHeads + head) * kRope + 8 * hi;
     s16x8 q[36];
+    {
+      const uint16_t* qa = a.q_abs + ((size_t)u * kHeads + head) * kLatent + 8 * hi;
+      const uint16_t* qr = a.q_r + ((size_t)u * kHeads + head) * kRope + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) q[ks] = *(const s16x8*)(qa + 16 * ks);
+      for (int ks = 0; ks < 32; ++ks) q[ks] = *(const s16x8*)(qa + 16 * ks);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) q[32 + ks] = *(const s16x8*)(qr + 16 * ks);
+      for (int ks = 0; ks < 4; ++ks) q[32 + ks] = *(const s16x8*)(qr + 16 * ks);
+    }
 
-    auto page_src = [&](int p) -> const unsigned char* {
-      int64_t phys = bt_row[p];
-      phys = phys < 0 ? 0 : (phys >= a.num_pages ? a.num_pages - 1 : phys);
-      return (const unsigned char*)a.kv + phys * (int64_t)kPageBytes;
-    };
-
-    f32x16 o[4][4];         // O[head block hb][column block c]
-    // Reference max (log2 units) of head 32w + l32: from the first page, or the
+    f32x16 o[4][4];            // O[head block hb][column block c]
+    // Reference max (log2 units) of head 32w + l32: from the first tile, or the
     // segment's true maximum when the segment is being redone.
     float m_ref = redo ? m_redo : -INFINITY;
-    float l_part = 0.f;       // this lane's share of that head's softmax denominator
-    {
+    float l_part = 0.f;        // this lane's share of that head's softmax denominator
+    float m_seen = -INFINITY;  // largest score seen (log2 units); above m_ref + kHeadroom means overflow
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb)
+    for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) o[hb][c][j] = 0.f;
-      float m_seen = -INFINITY;
-      bool overflow = false;
+        for (int j = 0; j < 16; ++j) o[hb][c][j] = 0.f;
 
+    // kFirst: the segment's first tile (sets the softmax reference); kLast: its last
+    // tile (masks the keys past the end, issues no further loads).
+    auto step = [&](const int k, auto first, auto last) __attribute__((always_inline)) {
+      constexpr bool kFirst = decltype(first)::value;
+      constexpr bool kMasked = decltype(last)::value;
+      if (kMasked || kFirst) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerTile));   // tile k+1 may still be in flight
+      __syncthreads();   // tile k in LDS for all; P(k-1) visible; slot of tile k+2 and P buffer k%2 free
+
+      // ---- scores S^T: 36 k-steps in two accumulation chains (even / odd k-steps), the
+      // A operand read from LDS four k-steps ahead through a ring of four registers.
+      // A operand, k-step ks: token l32 of the tile, chunk 2ks + hi:
+      //   latent (ks = 8p + q < 32): aq[q] + 256p;  RoPE (ks = 32 + q): ar[q]
+      // Written as one asm block so that the two accumulators live in VGPRs: the O
+      // accumulators fill all 256 AGPRs, and compiler-selected MFMAs here would use
+      // the AGPR form and shuttle O tiles between the register files every tile.
+      // Hazards the block covers itself: the leading s_nop 1 separates a VALU write of
+      // an operand from its MFMA read; each chain starts from the constant 0 and then
+      // accumulates in place (same registers, back to back, no wait needed); a ring
+      // register is refilled only after the MFMA reading it has issued (its A read is
+      // at issue, the LDS return much later); the trailing 24 wait states exceed the
+      // wait an XDL result needs before a VALU read (passes + 4, at most 20).
+      // Except in a segment's last step the block also issues the 9 direct loads of
+      // tile k+2, one after every fourth MFMA (RoPE rows first, M0 stepping through
+      // the LDS rows), so their issue overlaps the MFMAs.  Past the end of the segment
+      // those loads fetch row 0 of the segment's last page into the free slot: a dummy
+      // that keeps every non-last step on one code path.
+      f32x16 sa, sb;
       {
-        const unsigned char* src0 = page_src(p0);
-        const uint32_t lb0 = lds_addr(lds);
-#pragma unroll
-        for (int d = 0; d < kLoadsPerThread; ++d) issue_page_part(src0, lb0, ldo, wave_u, lane, n_vis - p0 * kPage, d);
-      }
-      for (int p = p0; p < p1; ++p) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // this wave's loads of page p
-        __syncthreads();                             // page p in LDS for all; page p-1 and P free
-        const unsigned char* cur = lds + ((p - p0) & 1) * kPageBytes;
-        const bool has_next = p + 1 < p1;
-        const unsigned char* nsrc = page_src(has_next ? p + 1 : p);
-        const uint32_t nbuf = lds_addr(lds + ((p + 1 - p0) & 1) * kPageBytes);
-        const int nvalid = n_vis - (p + 1) * kPage;
-
-        // ---- scores S^T: two 32-token blocks alternate (two accumulation chains);
-        // LDS reads run kAhead MFMAs ahead; one next-page load per 4 MFMAs.
-        // A operand, token block tb, k-step ks: token 32tb + l32, chunk 2ks + hi:
-        //   latent (ks = 8p + q < 32): offA[q] + 256p + 32768tb;  RoPE (ks = 32 + q): offR[q] + 4096tb
-        int offA[8], offR[4];
+        const uint32_t cur_addr = lbase + (k & 3) * kTileBytes;
+        uint32_t aq[8], ar[4];
         {
           const int ln = opaque_lane(), lh = ln >> 5, ll = ln & 31;
           const int fa = swz_lat(ll), ga = swz_rope(ll);
 #pragma unroll
-          for (int q2 = 0; q2 < 8; ++q2) offA[q2] = ll * 1024 + 16 * ((2 * q2 + lh) ^ fa);
+          for (int q2 = 0; q2 < 8; ++q2) aq[q2] = cur_addr + ll * 1024 + 16 * ((2 * q2 + lh) ^ fa);
 #pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) offR[q2] = kRopeRegion + ll * 128 + 16 * ((2 * q2 + lh) ^ ga);
+          for (int q2 = 0; q2 < 4; ++q2) ar[q2] = cur_addr + kRopeRegion + ll * 128 + 16 * ((2 * q2 + lh) ^ ga);
         }
-        f32x16 s0, s1;
+        s16x8 tq[4];
+        if constexpr (!kMasked) {
+          const int kn = k + 2;
+          int64_t phys = ld_uniform(a.bt, bt_row + min(p0 + (kn >> 1), p1 - 1));
+          phys = phys < 0 ? 0 : (phys >= a.num_pages ? a.num_pages - 1 : phys);
+          const unsigned char* dsrc = (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + (kn & 1) * kTileBytes;
+          const int valid = tile_valid(kn);   // <= 0 past the end of the segment
+          uint32_t dv[9];
+          {
+            const int ln = opaque_lane();
+            const TileLoadOffsets ldo = tile_load_offsets(ln, wave_u);
+            dv[0] = (8 * wave_u + (ln >> 3) < valid) ? 8 * wave_u * kRowBytes + ldo.rope
+                                                     : (uint32_t)(kLatent * 2 + (ln & 7) * 16);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) { s0[j] = 0.f; s1[j] = 0.f; }
-        {
-          auto a_ptr = [&](int i) -> const s16x8* {
-            const int tb = i & 1, ks = i >> 1;
-            const unsigned char* pa = ks < 32 ? cur + offA[ks & 7] + 256 * (ks >> 3) + 32768 * tb
-                                              : cur + offR[ks - 32] + 4096 * tb;
-            return (const s16x8*)pa;
-          };
-          constexpr int kAhead = 4;
-          s16x8 abuf[kAhead];
-#pragma unroll
-          for (int i = 0; i < kAhead; ++i) abuf[i] = *a_ptr(i);
-#pragma unroll
-          for (int i = 0; i < 72; ++i) {
-            const s16x8 av = abuf[i % kAhead];
-            if (i + kAhead < 72) abuf[i % kAhead] = *a_ptr(i + kAhead);
-            if (i & 1) s1 = mfma32(av, q[i >> 1], s1);
-            else s0 = mfma32(av, q[i >> 1], s0);
-            if ((i & 3) == 3 && has_next) issue_page_part(nsrc, nbuf, ldo, wave_u, lane, nvalid, i >> 2);
+            for (int i = 0; i < 8; ++i) {
+              const int t = wave_u + 4 * i;
+              dv[1 + i] = ldo.lat[i & 3] + (t < valid ? t * kRowBytes : 0);
+            }
           }
-          __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);   // the first kAhead LDS reads
-#pragma unroll
-          for (int i = 0; i < 72; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-            if (i + kAhead < 72) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then 1 LDS read
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-
-        // ---- softmax weights (base 2).  Register j of block tb is token
-        // 32tb + 8(j/4) + 4hi + (j%4) of the page, head l32 of this wave.
-        float x[32];
-        const int tok0 = p * kPage;
-        if (tok0 + kPage > n_vis) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int t = 8 * (j >> 2) + 4 * hi + (j & 3);
-            x[j] = (tok0 + t < n_vis) ? s0[j] * a.scale_log2 : -INFINITY;
-            x[16 + j] = (tok0 + 32 + t < n_vis) ? s1[j] * a.scale_log2 : -INFINITY;
-          }
+          uint32_t m0v = lbase + (kn & 3) * kTileBytes + kRopeRegion + 1024 * wave_u;
+          asm volatile(
+              "s_nop 1\n\t"
+              "ds_read_b128 %[t0], %[a0] offset:0\n\t"
+              "ds_read_b128 %[t1], %[a1] offset:0\n\t"
+              "ds_read_b128 %[t2], %[a2] offset:0\n\t"
+              "ds_read_b128 %[t3], %[a3] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q0], 0\n\tds_read_b128 %[t0], %[a4] offset:0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d0], %[src] nt\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q1], 0\n\tds_read_b128 %[t1], %[a5] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q2], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q3], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q4], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:256\n\ts_add_u32 m0, m0, 0xffff8000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d1], %[src] nt\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q5], %[sb]\n\tds_read_b128 %[t1], %[a1] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q6], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q7], %[sb]\n\tds_read_b128 %[t3], %[a3] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q8], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:256\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d2], %[src] nt\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q9], %[sb]\n\tds_read_b128 %[t1], %[a5] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q10], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q11], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q12], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:512\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d3], %[src] nt\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q13], %[sb]\n\tds_read_b128 %[t1], %[a1] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q14], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q15], %[sb]\n\tds_read_b128 %[t3], %[a3] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q16], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:512\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d4], %[src] nt\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q17], %[sb]\n\tds_read_b128 %[t1], %[a5] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q18], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q19], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q20], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:768\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d5], %[src] nt\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q21], %[sb]\n\tds_read_b128 %[t1], %[a1] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q22], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q23], %[sb]\n\tds_read_b128 %[t3], %[a3] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q24], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:768\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d6], %[src] nt\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q25], %[sb]\n\tds_read_b128 %[t1], %[a5] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q26], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q27], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q28], %[sa]\n\tds_read_b128 %[t0], %[r0] offset:0\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d7], %[src] nt\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q29], %[sb]\n\tds_read_b128 %[t1], %[r1] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q30], %[sa]\n\tds_read_b128 %[t2], %[r2] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q31], %[sb]\n\tds_read_b128 %[t3], %[r3] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q32], %[sa]\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d8], %[src] nt\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q33], %[sb]\n\t"
+              "s_waitcnt lgkmcnt(1)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q34], %[sa]\n\t"
+              "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q35], %[sb]\n\t"
+              "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+              : [sa] "=&v"(sa), [sb] "=&v"(sb), [t0] "=&v"(tq[0]), [t1] "=&v"(tq[1]), [t2] "=&v"(tq[2]), [t3] "=&v"(tq[3]), "+{m0}"(m0v)
+              : [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]),
+                [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]),
+                [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]),
+                [q18] "v"(q[18]), [q19] "v"(q[19]), [q20] "v"(q[20]), [q21] "v"(q[21]), [q22] "v"(q[22]), [q23] "v"(q[23]),
+                [q24] "v"(q[24]), [q25] "v"(q[25]), [q26] "v"(q[26]), [q27] "v"(q[27]), [q28] "v"(q[28]), [q29] "v"(q[29]),
+                [q30] "v"(q[30]), [q31] "v"(q[31]), [q32] "v"(q[32]), [q33] "v"(q[33]), [q34] "v"(q[34]), [q35] "v"(q[35]),
+                [a0] "v"(aq[0]), [a1] "v"(aq[1]), [a2] "v"(aq[2]), [a3] "v"(aq[3]), [a4] "v"(aq[4]), [a5] "v"(aq[5]), [a6] "v"(aq[6]), [a7] "v"(aq[7]),
+                [r0] "v"(ar[0]), [r1] "v"(ar[1]), [r2] "v"(ar[2]), [r3] "v"(ar[3]),
+                [src] "s"(dsrc), [d0] "v"(dv[0]), [d1] "v"(dv[1]), [d2] "v"(dv[2]), [d3] "v"(dv[3]), [d4] "v"(dv[4]), [d5] "v"(dv[5]), [d6] "v"(dv[6]), [d7] "v"(dv[7]), [d8] "v"(dv[8])
+              : "memory");
         } else {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) { x[j] = s0[j] * a.scale_log2; x[16 + j] = s1[j] * a.scale_log2; }
+          asm volatile(
+              "s_nop 1\n\t"
+              "ds_read_b128 %[t0], %[a0] offset:0\n\t"
+              "ds_read_b128 %[t1], %[a1] offset:0\n\t"
+              "ds_read_b128 %[t2], %[a2] offset:0\n\t"
+              "ds_read_b128 %[t3], %[a3] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q0], 0\n\tds_read_b128 %[t0], %[a4] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q1], 0\n\tds_read_b128 %[t1], %[a5] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q2], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q3], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q4], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q5], %[sb]\n\tds_read_b128 %[t1], %[a1] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q6], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q7], %[sb]\n\tds_read_b128 %[t3], %[a3] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q8], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q9], %[sb]\n\tds_read_b128 %[t1], %[a5] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q10], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q11], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:256\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q12], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q13], %[sb]\n\tds_read_b128 %[t1], %[a1] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q14], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q15], %[sb]\n\tds_read_b128 %[t3], %[a3] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q16], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q17], %[sb]\n\tds_read_b128 %[t1], %[a5] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q18], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q19], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:512\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q20], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q21], %[sb]\n\tds_read_b128 %[t1], %[a1] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q22], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q23], %[sb]\n\tds_read_b128 %[t3], %[a3] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q24], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q25], %[sb]\n\tds_read_b128 %[t1], %[a5] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q26], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q27], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:768\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q28], %[sa]\n\tds_read_b128 %[t0], %[r0] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q29], %[sb]\n\tds_read_b128 %[t1], %[r1] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q30], %[sa]\n\tds_read_b128 %[t2], %[r2] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q31], %[sb]\n\tds_read_b128 %[t3], %[r3] offset:0\n\t"
+              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q32], %[sa]\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q33], %[sb]\n\t"
+              "s_waitcnt lgkmcnt(1)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q34], %[sa]\n\t"
+              "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q35], %[sb]\n\t"
+              "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+              : [sa] "=&v"(sa), [sb] "=&v"(sb), [t0] "=&v"(tq[0]), [t1] "=&v"(tq[1]), [t2] "=&v"(tq[2]), [t3] "=&v"(tq[3])
+              : [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]),
+                [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]),
+                [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]),
+                [q18] "v"(q[18]), [q19] "v"(q[19]), [q20] "v"(q[20]), [q21] "v"(q[21]), [q22] "v"(q[22]), [q23] "v"(q[23]),
+                [q24] "v"(q[24]), [q25] "v"(q[25]), [q26] "v"(q[26]), [q27] "v"(q[27]), [q28] "v"(q[28]), [q29] "v"(q[29]),
+                [q30] "v"(q[30]), [q31] "v"(q[31]), [q32] "v"(q[32]), [q33] "v"(q[33]), [q34] "v"(q[34]), [q35] "v"(q[35]),
+                [a0] "v"(aq[0]), [a1] "v"(aq[1]), [a2] "v"(aq[2]), [a3] "v"(aq[3]), [a4] "v"(aq[4]), [a5] "v"(aq[5]), [a6] "v"(aq[6]), [a7] "v"(aq[7]),
+                [r0] "v"(ar[0]), [r1] "v"(ar[1]), [r2] "v"(ar[2]), [r3] "v"(ar[3])
+              : "memory");
         }
-        float mx = x[0];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- PV of tile k-1 (at k = 0: the zeroed P buffer 1 with the current, finite
+      // tile as V, which adds exact zeros), interleaved with the softmax of tile k.
+      //   A (P), head block hb, k-step st: head 32hb + l32, tokens 16st + 8hi + 0..7
+      //     -> pprev + offP[st] + 2048 hb
+      //   B (c_KV columns, transposing reads), half r, column block c: token 16st + 8hi + 4r + e,
+      //     chunk 16w + 4c + cb, byte 8 (lane & 1) -> vprev + offV[c][r] + 16384 st + 4096 r
+      const unsigned char* vprev = lds + ((k == 0 ? 0 : k - 1) & 3) * kTileBytes;
+      const unsigned char* pprev = pbuf + ((k - 1) & 1) * kPBytes;
+      int offP[2], offV[4][2];
+      {
+        const int ln = opaque_lane(), lh = ln >> 5, ll = ln & 31;
+        const int pr = (ll >> 2) & 3;
 #pragma unroll
-        for (int j = 1; j < 32; ++j) mx = fmaxf(mx, x[j]);
+        for (int q2 = 0; q2 < 2; ++q2) offP[q2] = ll * 64 + 16 * ((2 * q2 + lh) ^ pr);
+        const int eb = (ln & 15) >> 2;
+        const int cb = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            offV[c][r] = (8 * lh + eb) * 1024 + 64 * (c ^ eb) + 16 * (cb ^ (2 * lh + r)) + 8 * (ln & 1) + 256 * wave_u;
+      }
+      auto ld_v = [&](int st, int c) -> s16x8 {
+        const s16x4 v0 = lds_read_tr4(vprev + offV[c][0] + 16384 * st);
+        const s16x4 v1 = lds_read_tr4(vprev + offV[c][1] + 16384 * st + 4096);
+        return s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      };
+      auto ld_p = [&](int st, int hb) -> s16x8 { return *(const s16x8*)(pprev + offP[st] + 2048 * hb); };
+      s16x8 pa[4], bv[4], bvn;
+      pa[0] = ld_p(0, 0);
+      bv[0] = ld_v(0, 0);
+#pragma unroll
+      for (int c = 1; c < 4; ++c) bv[c] = ld_v(0, c);
+#pragma unroll
+      for (int hb = 1; hb < 4; ++hb) pa[hb] = ld_p(0, hb);
+
+      // Scores of tile k, still unscaled (scale > 0 keeps the max).  Register j is
+      // token 8(j/4) + 4hi + (j%4) of the tile.  Keys past the end of the sequence
+      // (only in the segment's last tile) score -inf.
+      float sc[16], xa[16], ex[16];
+      float mx = -INFINITY;
+      auto score = [&](int j) {
+        sc[j] = sa[j] + sb[j];
+        if constexpr (kMasked) {
+          const int t = 8 * (j >> 2) + 4 * hi + (j & 3);
+          if (t >= tile_valid(k)) sc[j] = -INFINITY;
+        }
+        if (j & 1) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sc[j - 1], sc[j]));
+      };
+      if constexpr (kFirst) {
+        // The reference maximum is needed before the first weight: all scores first.
+#pragma unroll
+        for (int j = 0; j < 16; ++j) score(j);
+        mx *= a.scale_log2;
         m_seen = fmaxf(m_seen, mx);
-        if (p == p0 && m_ref == -INFINITY) {   // first page (a redo arrives with m_ref set)
-          m_ref = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        } else {
-          overflow |= mx > m_ref + kHeadroom;
-        }
-#pragma unroll
-        for (int j = 0; j < 32; ++j) { x[j] = __builtin_amdgcn_exp2f(x[j] - m_ref); l_part += x[j]; }
-        // P -> LDS: tokens 32tb + 8q + 4hi + 0..3 are registers 16tb + 4q + 0..3.
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            u32x2 w2;
-            w2[0] = pack_bf16x2(x[16 * tb + 4 * qq], x[16 * tb + 4 * qq + 1]);
-            w2[1] = pack_bf16x2(x[16 * tb + 4 * qq + 2], x[16 * tb + 4 * qq + 3]);
-            *(u32x2*)(pbuf + pw_off + 16 * ((4 * tb + qq) ^ ph)) = w2;
-          }
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();   // P of all 128 heads visible
+        const float mx_head = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        m_ref = redo ? m_ref : mx_head;   // a redo brings the segment's true maximum
+      }
+      __builtin_amdgcn_sched_barrier(0);
 
-        // ---- O[all heads, columns 128w + ..] += P . c_KV over the page.
-        // A operand (P), head block hb, k-step st: head 32hb + l32, tokens 16st + 8hi + 0..7
-        //   -> offP[st] + 4096hb.  B operand (transposing read), half r, column block c
-        //   (columns 128w + 32c ..): token 16st + 8hi + 4r + e, chunk 16w + 4c + cb, byte
-        //   8 (lane & 1) -> offV[c][r] + 16384st + 4096r.
-        int offP[4], offV[4][2];
-        {
-          const int ln = opaque_lane(), lh = ln >> 5, ll = ln & 31;
-          const int pr = (ll >> 1) & 7;
+      // 32 stages, one PV MFMA each, fenced so that the order below is the issue order.
+      // k-step 0 runs head-block-major: P register hb is reloaded with its k-step-1 value
+      // right after its last use; V registers are refilled for k-step 1 after their last
+      // use, the first k-step-1 column block going to the spare register bvn early.  k-step 1
+      // runs column-block-major.  The softmax of tile k is software-pipelined over the
+      // stages (score j at stage j, exponent argument at j+1, exponential at j+2, sum and
+      // packing at j+3; in the first tile the scores are all done above), so each stage's
+      // VALU work is independent and hides under its MFMA.
+      constexpr int oB = kFirst ? 0 : 1;
+      u32x2 pw[4];
 #pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) offP[q2] = ll * 128 + 16 * ((2 * q2 + lh) ^ pr);
-          const int eb = (ln & 15) >> 2;
-          const int cb = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
-#pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2)
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-              offV[q2][r] = (8 * lh + eb) * 1024 + 64 * (q2 ^ eb) + 16 * (cb ^ (2 * lh + r)) + 8 * (ln & 1) + 256 * wave_u;
+      for (int st = 0; st < 32; ++st) {
+        if (st < 16) {
+          const int hb = st >> 2, c = st & 3;
+          o[hb][c] = mfma32(pa[hb], bv[c], o[hb][c]);
+          if (c == 3) pa[hb] = ld_p(1, hb);
+          if (st == 1) bvn = ld_v(1, 0);
+          if (st >= 12 && st < 15) bv[st - 12] = ld_v(1, st - 11);
+        } else {
+          const int c = (st - 16) >> 2, hb = (st - 16) & 3;
+          o[hb][c] = mfma32(pa[hb], c == 0 ? bvn : bv[c - 1], o[hb][c]);
         }
-        {
-          // operands of k-step st: P tiles of the 4 head blocks, V tiles of the 4 column blocks
-          auto load_ops = [&](int st, s16x8* pa, s16x8* bv) {
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb) pa[hb] = *(const s16x8*)(pbuf + offP[st] + 4096 * hb);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const s16x4 lo = lds_read_tr4(cur + offV[c][0] + 16384 * st);
-              const s16x4 h4 = lds_read_tr4(cur + offV[c][1] + 16384 * st + 4096);
-              bv[c] = s16x8{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
-            }
-          };
-          s16x8 pa[2][4], bv[2][4];
-          load_ops(0, pa[0], bv[0]);
-#pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            if (st + 1 < 4) load_ops(st + 1, pa[(st + 1) & 1], bv[(st + 1) & 1]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-              for (int hb = 0; hb < 4; ++hb) o[hb][c] = mfma32(pa[st & 1][hb], bv[st & 1][c], o[hb][c]);
-          }
-          // reads of k-step st+1 (4 + 8) spread over the 16 MFMAs of k-step st
-          __builtin_amdgcn_sched_group_barrier(0x100, 12, 1);
-#pragma unroll
-          for (int st = 0; st < 4; ++st) {
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-              if (st + 1 < 4 && m < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-            }
-          }
+        if (!kFirst && st < 16) score(st);
+        if (st >= oB && st < 16 + oB) xa[st - oB] = __builtin_fmaf(sc[st - oB], a.scale_log2, -m_ref);
+        if (st >= oB + 1 && st < 17 + oB) ex[st - oB - 1] = __builtin_amdgcn_exp2f(xa[st - oB - 1]);
+        if (st >= oB + 2 && st < 18 + oB) {
+          const int j = st - oB - 2;
+          l_part += ex[j];
+          if (j & 1) pw[j >> 2][(j >> 1) & 1] = pack_bf16x2(ex[j - 1], ex[j]);
         }
+        if (st == 20) {
+          // P of tile k: tokens 8q + 4hi + 0..3 of head 32w + l32, chunk q at q ^ ((head >> 2) & 3).
+          const int ln = opaque_lane(), ll = ln & 31;
+          unsigned char* pk = pbuf + (k & 1) * kPBytes + (wave_u * 32 + ll) * 64 + 8 * (ln >> 5);
+          const int sw = (ll >> 2) & 3;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) *(u32x2*)(pk + 16 * (qq ^ sw)) = pw[qq];
+        }
+        if (!kFirst && st == 21) m_seen = fmaxf(m_seen, mx * a.scale_log2);
         __builtin_amdgcn_sched_barrier(0);
       }
+    };
 
-      // ---- end of pass: agree on a restart, publish row sums.  The page buffers
-      // are free once every wave is past this barrier; they hold the scratch.
+    int k = 0;
+    if (n_tiles == 1) {
+      step(0, Flag<true>{}, Flag<true>{});
+    } else {
+      step(0, Flag<true>{}, Flag<false>{});
+      for (k = 1; k + 1 < n_tiles; ++k) step(k, Flag<false>{}, Flag<false>{});
+      step(k, Flag<false>{}, Flag<true>{});
+    }
+
+    // PV of the last tile.
+    __syncthreads();   // P of the last tile visible
+    {
+      const unsigned char* vlast = lds + (k & 3) * kTileBytes;
+      const unsigned char* plast = pbuf + (k & 1) * kPBytes;
+      int offP[2], offV[4][2];
+      {
+        const int ln = opaque_lane(), lh = ln >> 5, ll = ln & 31;
+        const int pr = (ll >> 2) & 3;
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) offP[q2] = ll * 64 + 16 * ((2 * q2 + lh) ^ pr);
+        const int eb = (ln & 15) >> 2;
+        const int cb = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            offV[c][r] = (8 * lh + eb) * 1024 + 64 * (c ^ eb) + 16 * (cb ^ (2 * lh + r)) + 8 * (ln & 1) + 256 * wave_u;
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        s16x8 pa[4], bv[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) pa[hb] = *(const s16x8*)(plast + offP[st] + 2048 * hb);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const s16x4 v0 = lds_read_tr4(vlast + offV[c][0] + 16384 * st);
+          const s16x4 v1 = lds_read_tr4(vlast + offV[c][1] + 16384 * st + 4096);
+          bv[c] = s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        }
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) o[hb][c] = mfma32(pa[hb], bv[c], o[hb][c]);
+      }
+    }
+
+    {
+      // ---- end of segment: agree on a redo, publish row sums.  The ring slots are
+      // free once every wave is past this barrier; slot 0 holds the scratch.
       __syncthreads();
       int* flags = (int*)lds;
       float* lsum = (float*)(lds + 256);
-      const bool any_over = __builtin_amdgcn_ballot_w64(overflow) != 0;
+      const bool any_over = __builtin_amdgcn_ballot_w64(m_seen > m_ref + kHeadroom) != 0;
       const float l_head = l_part + __shfl_xor(l_part, 32, 64);
       const float m_all = fmaxf(m_seen, __shfl_xor(m_seen, 32, 64));
       if (lane == 0) flags[wave_u] = any_over ? 1 : 0;
@@ -474,19 +652,19 @@ void decode_kernel(DecodeArgs a) {
         const size_t obase = (size_t)(4 * hi) * kLatent + wave_u * 128 + l32;
         uint16_t* ob16 = a.out_latent + (size_t)u * kHeads * kLatent + obase;
         float* ob32 = a.part_o + (size_t)(slot < 0 ? 0 : slot) * kHeads * kLatent + obase;
-  #pragma unroll
+#pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
           f32x16 il;
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 16; ++j) il[j] = 1.f / lrow[32 * hb + 8 * (j >> 2) + (j & 3)];
-  #pragma unroll
+#pragma unroll
           for (int c = 0; c < 4; ++c) {
             const f32x16 v = o[hb][c] * il;
             if (slot < 0) {
-  #pragma unroll
+#pragma unroll
               for (int j = 0; j < 16; ++j) ob16[(32 * hb + 8 * (j >> 2) + (j & 3)) * kLatent + 32 * c] = f2bf(v[j]);
             } else {
-  #pragma unroll
+#pragma unroll
               for (int j = 0; j < 16; ++j) ob32[(32 * hb + 8 * (j >> 2) + (j & 3)) * kLatent + 32 * c] = v[j];
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -500,7 +678,7 @@ void decode_kernel(DecodeArgs a) {
           }
         }
       }
-      __syncthreads();   // scratch read before the next segment refills the buffers
+      __syncthreads();   // scratch read before the next segment refills the slots
       redo = again;      // a redo runs the same segment again (pos unchanged)
     }
     if (!redo) {
