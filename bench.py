@@ -28,6 +28,10 @@ import numpy as np  # noqa: E402
 METRIC = "decode attention µs/step + achieved HBM GB/s (% roofline), B=64 ctx=32K"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 ROW_BYTES = 1152               # one cached token of one layer: 576 bf16
+COPY_BYTES = 512 << 20         # device copy of known size that calibrates the HBM byte counters
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_c3_b64_traffic.md")
+KERNEL_SOURCES = ("mla_latent_kv_04_amd/csrc/decode.hip", "mla_latent_kv_04_amd/csrc/common.h")
 
 
 def log(*a):
@@ -128,11 +132,24 @@ def main():
                     help="comma list of other workloads timed for the report (c1,c2,c3max,c4,c5 or none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="only run decode launches and the calibration copy (target of rocprofv3 --pmc passes)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from the FETCH_SIZE and WRITE_SIZE pass output folders")
+    ap.add_argument("--pmc-command", action="append", default=[],
+                    help="command lines recorded in the traffic summary (repeatable)")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.pmc_command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(sequences shard across GPUs without exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
+
+    if args.pmc_run:
+        pmc_run(args.steps, args.warmup)
+        return
 
     import torch
     import mla_latent_kv_04_amd as mla
@@ -189,6 +206,7 @@ def main():
         cpu = cpu_baseline(inp, args.cpu_seconds)
         log(f"[bench] cpu baseline: {cpu}")
 
+    traffic = load_traffic()
     line = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -214,12 +232,120 @@ def main():
         "fused_us_per_step": round(fms * 1e3, 2),
         "fused_kernels_us": {k: round(v * 1e3, 2) for k, v in fper.items()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic["fetch"] + traffic["write"]),
+                     "traffic_split": traffic,
                      "kernel": "decode_kernel", "algorithmic_bytes_per_launch": r["cache_bytes"]},
         "cpu_baseline": cpu,
         "other_workloads": others,
     }
     print(json.dumps(line), flush=True)
+
+
+def kernel_source_hash():
+    """sha256 over the sources the decode kernel is compiled from: counter readings
+    taken with other sources do not describe the kernel being timed."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None when
+    it is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if line.startswith(("source_sha256:", "fetch_bytes_per_launch:",
+                                                                             "write_bytes_per_launch:")))
+    except OSError:
+        return None
+    if kv.get("source_sha256", "").strip() != kernel_source_hash():
+        return None
+    return {"fetch": float(kv["fetch_bytes_per_launch"]), "write": float(kv["write_bytes_per_launch"])}
+
+
+def pmc_run(steps, warmup):
+    """Workload for the rocprofv3 --pmc passes: `warmup + steps` paged decode launches
+    on the batch-64 workload, then one device copy of COPY_BYTES bytes whose counter
+    readings calibrate the decode kernel's."""
+    import torch
+    import mla_latent_kv_04_amd as mla
+    inp = _workload_from_synth("c3", torch, with_host_pool=False)
+    pool = _device_pool(inp.num_pages, inp.seed, torch)
+    qa = torch.randn((inp.batch, 1, 128, 512), device="cuda").to(torch.bfloat16)
+    qr = torch.randn((inp.batch, 1, 128, 64), device="cuda").to(torch.bfloat16)
+    bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
+    for _ in range(warmup + steps):
+        mla.decode_paged(qa, qr, pool, bt, sl, scale=inp.scale)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] pmc run: {warmup + steps} decode launches, copy of {COPY_BYTES} B")
+
+
+def _pmc_per_dispatch(run_dir, counter):
+    """{kernel name: [value per dispatch]} for one counter of a rocprofv3 csv run."""
+    import csv
+    import glob
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in vals.items()}
+
+
+def summarize_pmc(fetch_dir, write_dir, command):
+    """Writes the traffic summary: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the
+    decode kernel, each scaled by COPY_BYTES over what the same counter reads for the
+    copy (the copy fetches and writes COPY_BYTES exactly)."""
+    out = {}
+    for name, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _pmc_per_dispatch(run_dir, name)
+        dec = [v for k, vs in per.items() if "decode_kernel" in k for v in vs]
+        cop = [v for k, vs in per.items() if "decode_kernel" not in k and "copy" in k.lower() for v in vs]
+        if not dec or not cop:
+            raise SystemExit(f"summarize-pmc: no decode or copy dispatches with {name} in {run_dir}: {list(per)}")
+        cop_kib = max(cop)
+        factor = COPY_BYTES / (cop_kib * 1024.0)
+        dec_kib = sum(dec[1:]) / max(len(dec) - 1, 1) if len(dec) > 1 else dec[0]   # first launch is cold
+        out[name] = {"decode_kib": dec_kib, "copy_kib": cop_kib, "factor": factor, "bytes": dec_kib * 1024.0 * factor,
+                     "dispatches": len(dec)}
+    alg = 1166687 * ROW_BYTES
+    fetch, write = out["FETCH_SIZE"]["bytes"], out["WRITE_SIZE"]["bytes"]
+    lines = [
+        "# HBM traffic of decode_kernel: paged MLA decode, batch 64, seq_len U[1024,32768]",
+        "",
+        "Two rocprofv3 counter passes over `python3 bench.py --pmc-run` (decode launches, then a",
+        f"device copy of {COPY_BYTES} B that calibrates the counters), run from /tmp:",
+        "",
+        "```",
+        *command,
+        "```",
+        "",
+        "| counter | decode KiB/dispatch | copy KiB | calibration (copy bytes / copy reading) | decode bytes/launch |",
+        "|---|---|---|---|---|",
+        *[f"| {n} | {v['decode_kib']:.0f} | {v['copy_kib']:.0f} | {v['factor']:.4f} | {v['bytes']:.0f} |"
+          for n, v in out.items()],
+        "",
+        f"Algorithmic bytes per launch (cache rows read once): {alg}; fetched / algorithmic = {fetch / alg:.4f}.",
+        "",
+        f"source_sha256: {kernel_source_hash()}",
+        f"fetch_bytes_per_launch: {fetch:.0f}",
+        f"write_bytes_per_launch: {write:.0f}",
+        "",
+    ]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines))
+    log(f"[bench] wrote {TRAFFIC_FILE}: fetch {fetch:.0f} B, write {write:.0f} B per launch")
 
 
 def device_cus(mla):

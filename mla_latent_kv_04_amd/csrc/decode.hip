@@ -690,58 +690,77 @@ void decode_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------- combine
 
-// One workgroup per (work unit, 16 heads).  Units finished in place are
-// skipped; units without visible tokens get zeros and lse = -inf; split units
-// merge their partials in increasing workgroup order.
+// One workgroup per (work unit, 8 heads); wave w merges heads 2w and 2w+1 of the
+// eight, lane l covering columns 4((l & 31) + 32v) .. +3 (v = 0..3) of head
+// 2w + l/32, so each load instruction reads two contiguous 512-byte runs.  Units
+// finished in place are skipped; units without visible tokens get zeros and
+// lse = -inf; split units merge their fragments in increasing workgroup order
+// with a running maximum, loading fragment f+1 while merging fragment f.
+constexpr int kCombineHeads = 8;
+
+__device__ __forceinline__ int fragment_slot(int gg, int g0, int chunk, int ubeg) {
+  // The first fragment is its workgroup's second segment unless the unit starts
+  // exactly at that workgroup's range; every later fragment is a first segment.
+  return (gg == g0 && gg * chunk < ubeg) ? 2 * gg + 1 : 2 * gg;
+}
+
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void combine_kernel(DecodeArgs a, int W) {
   const int u = blockIdx.x;
   const int U = a.batch * a.s_q;
-  const int total = a.cum[U];
-  const int ubeg = a.cum[u], uend = a.cum[u + 1];
-  const int tid = threadIdx.x;
-  const int head = blockIdx.y * 16 + (tid >> 4);
-  const int c0 = (tid & 15) * 32;
-  uint16_t* dst = a.out_latent + ((size_t)u * kHeads + head) * kLatent + c0;
+  const int total = ld_uniform(a.cum, U);
+  const int ubeg = ld_uniform(a.cum, u), uend = ld_uniform(a.cum, u + 1);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int head = blockIdx.y * kCombineHeads + 2 * (tid >> 6) + (lane >> 5);
+  const int col = 4 * (lane & 31);   // + 128 v
+  uint16_t* dst = a.out_latent + ((size_t)u * kHeads + head) * kLatent + col;
   if (uend <= ubeg) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) *(u32x4*)(dst + 8 * v) = u32x4{0u, 0u, 0u, 0u};
-    if (a.lse != nullptr && (tid & 15) == 0) a.lse[(size_t)u * kHeads + head] = -INFINITY;
+    for (int v = 0; v < 4; ++v) *(u32x2*)(dst + 128 * v) = u32x2{0u, 0u};
+    if (a.lse != nullptr && (lane & 31) == 0) a.lse[(size_t)u * kHeads + head] = -INFINITY;
     return;
   }
   const int chunk = (total + W - 1) / W;
   const int g0 = ubeg / chunk, g1 = (uend - 1) / chunk;
   if (g0 == g1) return;
-  float m = -INFINITY;
-  for (int gg = g0; gg <= g1; ++gg) {
-    const int slot = (gg == g0 && gg * chunk < ubeg) ? 2 * gg + 1 : 2 * gg;
-    m = fmaxf(m, a.part_lse[(size_t)slot * kHeads + head]);
-  }
-  float acc[32];
+
+  auto load = [&](int gg, f32x4 (&x)[4], float& l) {
+    const int slot = fragment_slot(gg, g0, chunk, ubeg);
+    const float* src = a.part_o + ((size_t)slot * kHeads + head) * kLatent + col;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) acc[j] = 0.f;
-  float wsum = 0.f;
-  for (int gg = g0; gg <= g1; ++gg) {
-    const int slot = (gg == g0 && gg * chunk < ubeg) ? 2 * gg + 1 : 2 * gg;
-    const float w = exp2f(a.part_lse[(size_t)slot * kHeads + head] - m);
-    wsum += w;
-    const float* src = a.part_o + ((size_t)slot * kHeads + head) * kLatent + c0;
+    for (int v = 0; v < 4; ++v) x[v] = __builtin_nontemporal_load((const f32x4*)(src + 128 * v));
+    l = a.part_lse[(size_t)slot * kHeads + head];
+  };
+  f32x4 acc[4], fa[4], fb[4];
+  float m, la, lb;
+  load(g0, acc, m);
+  float wsum = 1.f;
+  auto merge = [&](const f32x4 (&x)[4], float l) {
+    // rescale the running sum to the new maximum (base 2), add fragment x
+    const float mn = fmaxf(m, l);
+    const float s_old = exp2f(m - mn), s_new = exp2f(l - mn);
+    wsum = wsum * s_old + s_new;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const f32x4 x = *(const f32x4*)(src + 4 * v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[4 * v + e] += w * x[e];
-    }
+    for (int v = 0; v < 4; ++v) acc[v] = acc[v] * s_old + x[v] * s_new;
+    m = mn;
+  };
+  // two register buffers: the load of fragment gg+1 is in flight while gg merges
+  int gg = g0 + 1;
+  load(gg, fb, lb);
+  while (true) {
+    if (gg + 1 <= g1) load(gg + 1, fa, la);
+    merge(fb, lb);
+    if (++gg > g1) break;
+    if (gg + 1 <= g1) load(gg + 1, fb, lb);
+    merge(fa, la);
+    if (++gg > g1) break;
   }
   const float inv = 1.f / wsum;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    u32x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[8 * v + 2 * e] * inv, acc[8 * v + 2 * e + 1] * inv);
-    *(u32x4*)(dst + 8 * v) = w;
-  }
-  if (a.lse != nullptr && (tid & 15) == 0) a.lse[(size_t)u * kHeads + head] = (m + __log2f(wsum)) * kLn2;
+  for (int v = 0; v < 4; ++v)
+    *(u32x2*)(dst + 128 * v) = u32x2{pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv),
+                                     pack_bf16x2(acc[v][2] * inv, acc[v][3] * inv)};
+  if (a.lse != nullptr && (lane & 31) == 0) a.lse[(size_t)u * kHeads + head] = (m + __log2f(wsum)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------- gather (test export)
@@ -783,7 +802,7 @@ hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint1
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_decode_done != nullptr && (e = hipEventRecord(ev_decode_done, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(batch * s_q, kHeads / 16), dim3(256), 0, s, a, wgs);
+  hipLaunchKernelGGL(combine_kernel, dim3(batch * s_q, kHeads / kCombineHeads), dim3(256), 0, s, a, wgs);
   return hipGetLastError();
 }
 
