@@ -182,6 +182,13 @@ __device__ __forceinline__ int opaque_lane() {
   return v;
 }
 
+// max(a, b, c) in one instruction (the compiler would quiet each operand first).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Softmax reference.  Each segment takes its per-head reference maximum from
 // its first tile and keeps it: P = 2^(s - m_ref) in log2 units, so the O
 // accumulators are never rescaled and any wave may accumulate any head.  A
@@ -216,8 +223,10 @@ struct Flag {
 // the PV operand traffic compared with every wave reading all 512 columns.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kSlots * kTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char pbuf[2 * kPBytes];
+  // 1024-byte alignment: tile slots and P buffers then start at multiples of 1024, so
+  // adding a slot base never changes the low ten bits of an offset (see below).
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kSlots * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char pbuf[2 * kPBytes];
 
   const int U = a.batch * a.s_q;
   const int total = ld_uniform(a.cum, U);
@@ -234,6 +243,34 @@ void decode_kernel(DecodeArgs a) {
   const int hi = lane >> 5;       // which half of the wave
   const int l32 = lane & 31;
   const uint32_t lbase = lds_addr(lds);
+
+  // Lane constants of the address arithmetic, kept for the whole kernel:
+  //   aql, arl: QK A-operand offsets within a tile slot of token l32, chunk hi of the
+  //     latent row and of the RoPE row (swizzled); chunk 2q + hi sits at the offset
+  //     XOR 32q (the swizzle XOR only moves the chunk index within bits 5..7);
+  //   latl[k]: direct-load source offset of latent chunk position `lane` of a row t with
+  //     t % 4 == w and (t / 4) % 4 == k;  ropel: RoPE source offset of this lane's row
+  //     (token 8w + lane/8) and chunk position relative to the tile.
+  uint32_t aql, arl, latl[4], ropel;
+  {
+    aql = l32 * 1024 + 16 * (hi ^ swz_lat(l32));
+    arl = kRopeRegion + l32 * 128 + 16 * (hi ^ swz_rope(l32));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) latl[k] = (uint32_t)((lane ^ swz_lat(wave_u + 4 * k)) * 16);
+    ropel = (uint32_t)((8 * wave_u + (lane >> 3)) * kRowBytes + kLatent * 2 +
+                       ((lane & 7) ^ ((4 * wave_u + (lane >> 4)) & 7)) * 16);
+  }
+  //   offP0: PV A operand (P) of head l32, tokens 8hi .. +7 in a P buffer (k-step st:
+  //     XOR 32st);  offV0: PV B operand (transposing reads) of column block 0, half 0,
+  //     in a tile slot: token 8hi + e (e = (lane & 15) / 4), chunk 16w + cb; column
+  //     block c, half r: XOR 64c + 16r.  Each XOR only touches bits 4..7.
+  uint32_t offP0, offV0;
+  {
+    offP0 = l32 * 64 + 16 * (hi ^ ((l32 >> 2) & 3));
+    const int eb = (lane & 15) >> 2;
+    const int cb = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    offV0 = (8 * hi + eb) * 1024 + 64 * eb + 16 * (cb ^ (2 * hi)) + 8 * (lane & 1) + 256 * wave_u;
+  }
 
   // Largest u with cum[u] <= start (then cum[u+1] > start).
   int lo_u = 0, hi_u = U - 1;
@@ -309,6 +346,57 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[hb][c][j] = 0.f;
 
+    // Operands of the next step, prepared while the current one runs its PV stages:
+    // QK A-operand addresses for tile slot kk & 3 (token l32, chunk 2ks + hi; latent
+    // k-step 8p + q at aq[q] + 256p, RoPE k-step 32 + q at ar[q]) and the direct
+    // loads of tile kn (source tile base, per-lane offsets, first LDS address).
+    uint32_t aq[8], ar[4], dv[9];
+    const unsigned char* dsrc;
+    uint32_t m0n;
+    int32_t bt_pref;
+    // Each preparation comes in three parts so that it can be spread over stages.
+    auto prep_qk = [&](int kk, int part) {
+      const uint32_t cur_addr = lbase + (kk & 3) * kTileBytes;
+      // cur_addr is a multiple of 1024: the XOR after the add only touches bits 5..7
+      if (part < 2) {
+        const uint32_t a0 = cur_addr + aql;
+#pragma unroll
+        for (int q2 = 4 * part; q2 < 4 * part + 4; ++q2) aq[q2] = a0 ^ (32u * q2);
+      } else {
+        const uint32_t r0 = cur_addr + arl;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) ar[q2] = r0 ^ (32u * q2);
+      }
+    };
+    auto prep_dma = [&](int kn, int32_t raw, int part) {
+      // past the end of the segment (valid <= 0) every row maps to row 0 of the page
+      const int valid = tile_valid(kn);
+      if (part == 0) {
+        const int32_t r = __builtin_amdgcn_readfirstlane(raw);   // uniform: keeps the base in SGPRs
+        const int64_t phys = r < 0 ? 0 : (r >= a.num_pages ? a.num_pages - 1 : r);
+        dsrc = (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + (kn & 1) * kTileBytes;
+        m0n = lbase + (kn & 3) * kTileBytes + kRopeRegion + 1024 * wave_u;
+        // rows at or past `valid` fetch the RoPE chunk of row 0 instead
+        const uint32_t r_0 = (uint32_t)(kLatent * 2 + (lane & 7) * 16);
+        const uint32_t keep = 0u - (uint32_t)(8 * wave_u + (lane >> 3) < valid);
+        dv[0] = (ropel & keep) | (r_0 & ~keep);
+      } else {
+#pragma unroll
+        for (int i = 4 * part - 4; i < 4 * part; ++i) {
+          const int t = wave_u + 4 * i;
+          dv[1 + i] = latl[i & 3] + (t < valid ? t * kRowBytes : 0);
+        }
+      }
+    };
+    {
+      const int32_t raw2 = ld_uniform(a.bt, bt_row + min(p0 + 1, p1 - 1));
+#pragma unroll
+      for (int part = 0; part < 3; ++part) {
+        prep_qk(0, part);
+        prep_dma(2, raw2, part);
+      }
+    }
+
     // kFirst: the segment's first tile (sets the softmax reference); kLast: its last
     // tile (masks the keys past the end, issues no further loads).
     auto step = [&](const int k, auto first, auto last) __attribute__((always_inline)) {
@@ -318,100 +406,82 @@ void decode_kernel(DecodeArgs a) {
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerTile));   // tile k+1 may still be in flight
       __syncthreads();   // tile k in LDS for all; P(k-1) visible; slot of tile k+2 and P buffer k%2 free
 
-      // ---- scores S^T: 36 k-steps in two accumulation chains (even / odd k-steps), the
-      // A operand read from LDS four k-steps ahead through a ring of four registers.
+      // ---- scores S^T: 36 k-steps accumulated in one chain (dependent MFMAs on the same
+      // registers issue back to back), the A operand read from LDS four k-steps ahead
+      // through a ring of four registers, one LDS wait per pair of k-steps.
       // A operand, k-step ks: token l32 of the tile, chunk 2ks + hi:
       //   latent (ks = 8p + q < 32): aq[q] + 256p;  RoPE (ks = 32 + q): ar[q]
-      // Written as one asm block so that the two accumulators live in VGPRs: the O
+      // Written as one asm block so that the accumulator lives in VGPRs: the O
       // accumulators fill all 256 AGPRs, and compiler-selected MFMAs here would use
       // the AGPR form and shuttle O tiles between the register files every tile.
       // Hazards the block covers itself: the leading s_nop 1 separates a VALU write of
-      // an operand from its MFMA read; each chain starts from the constant 0 and then
+      // an operand from its MFMA read; the chain starts from the constant 0 and then
       // accumulates in place (same registers, back to back, no wait needed); a ring
       // register is refilled only after the MFMA reading it has issued (its A read is
-      // at issue, the LDS return much later); the trailing 24 wait states exceed the
-      // wait an XDL result needs before a VALU read (passes + 4, at most 20).
+      // at issue, the LDS return much later); the trailing 14 wait states exceed the 12
+      // an 8-pass XDL result needs before a VALU or memory read.
       // Except in a segment's last step the block also issues the 9 direct loads of
       // tile k+2, one after every fourth MFMA (RoPE rows first, M0 stepping through
-      // the LDS rows), so their issue overlaps the MFMAs.  Past the end of the segment
-      // those loads fetch row 0 of the segment's last page into the free slot: a dummy
-      // that keeps every non-last step on one code path.
-      f32x16 sa, sb;
+      // the LDS rows), so their issue overlaps the MFMAs, and the scalar load of the
+      // block-table entry of tile k+3's page (the block's final lgkmcnt(0) covers it;
+      // an outstanding scalar load only makes its LDS waits stricter).  Past the end
+      // of the segment those loads fetch row 0 of the segment's last page into the
+      // free slot: a dummy that keeps every non-last step on one code path.  All
+      // operand addresses were prepared during the previous step's PV stages.
+      f32x16 sa;
       {
-        const uint32_t cur_addr = lbase + (k & 3) * kTileBytes;
-        uint32_t aq[8], ar[4];
-        {
-          const int ln = opaque_lane(), lh = ln >> 5, ll = ln & 31;
-          const int fa = swz_lat(ll), ga = swz_rope(ll);
-#pragma unroll
-          for (int q2 = 0; q2 < 8; ++q2) aq[q2] = cur_addr + ll * 1024 + 16 * ((2 * q2 + lh) ^ fa);
-#pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) ar[q2] = cur_addr + kRopeRegion + ll * 128 + 16 * ((2 * q2 + lh) ^ ga);
-        }
         s16x8 tq[4];
         if constexpr (!kMasked) {
-          const int kn = k + 2;
-          int64_t phys = ld_uniform(a.bt, bt_row + min(p0 + (kn >> 1), p1 - 1));
-          phys = phys < 0 ? 0 : (phys >= a.num_pages ? a.num_pages - 1 : phys);
-          const unsigned char* dsrc = (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + (kn & 1) * kTileBytes;
-          const int valid = tile_valid(kn);   // <= 0 past the end of the segment
-          uint32_t dv[9];
-          {
-            const int ln = opaque_lane();
-            const TileLoadOffsets ldo = tile_load_offsets(ln, wave_u);
-            dv[0] = (8 * wave_u + (ln >> 3) < valid) ? 8 * wave_u * kRowBytes + ldo.rope
-                                                     : (uint32_t)(kLatent * 2 + (ln & 7) * 16);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int t = wave_u + 4 * i;
-              dv[1 + i] = ldo.lat[i & 3] + (t < valid ? t * kRowBytes : 0);
-            }
-          }
-          uint32_t m0v = lbase + (kn & 3) * kTileBytes + kRopeRegion + 1024 * wave_u;
+          // the block-table entry of the page of tile k+3, for the next step's loads
+          const int32_t* btp = a.bt + bt_row;
+          const int bto = 4 * min(p0 + ((k + 3) >> 1), p1 - 1);
+          int32_t bt_next;
+          uint32_t m0v = m0n;
           asm volatile(
               "s_nop 1\n\t"
+              "s_load_dword %[btn], %[btp], %[bto]\n\t"
               "ds_read_b128 %[t0], %[a0] offset:0\n\t"
               "ds_read_b128 %[t1], %[a1] offset:0\n\t"
               "ds_read_b128 %[t2], %[a2] offset:0\n\t"
               "ds_read_b128 %[t3], %[a3] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q0], 0\n\tds_read_b128 %[t0], %[a4] offset:0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d0], %[src] nt\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q1], 0\n\tds_read_b128 %[t1], %[a5] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q2], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q3], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q4], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:256\n\ts_add_u32 m0, m0, 0xffff8000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d1], %[src] nt\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q5], %[sb]\n\tds_read_b128 %[t1], %[a1] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q6], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q7], %[sb]\n\tds_read_b128 %[t3], %[a3] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q8], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:256\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d2], %[src] nt\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q9], %[sb]\n\tds_read_b128 %[t1], %[a5] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q10], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q11], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q12], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:512\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d3], %[src] nt\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q13], %[sb]\n\tds_read_b128 %[t1], %[a1] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q14], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q15], %[sb]\n\tds_read_b128 %[t3], %[a3] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q16], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:512\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d4], %[src] nt\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q17], %[sb]\n\tds_read_b128 %[t1], %[a5] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q18], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q19], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q20], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:768\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d5], %[src] nt\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q21], %[sb]\n\tds_read_b128 %[t1], %[a1] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q22], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q23], %[sb]\n\tds_read_b128 %[t3], %[a3] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q24], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:768\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d6], %[src] nt\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q25], %[sb]\n\tds_read_b128 %[t1], %[a5] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q26], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q27], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q28], %[sa]\n\tds_read_b128 %[t0], %[r0] offset:0\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d7], %[src] nt\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q29], %[sb]\n\tds_read_b128 %[t1], %[r1] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q30], %[sa]\n\tds_read_b128 %[t2], %[r2] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q31], %[sb]\n\tds_read_b128 %[t3], %[r3] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q32], %[sa]\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d8], %[src] nt\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q33], %[sb]\n\t"
-              "s_waitcnt lgkmcnt(1)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q34], %[sa]\n\t"
-              "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q35], %[sb]\n\t"
-              "s_nop 7\n\ts_nop 7\n\ts_nop 7"
-              : [sa] "=&v"(sa), [sb] "=&v"(sb), [t0] "=&v"(tq[0]), [t1] "=&v"(tq[1]), [t2] "=&v"(tq[2]), [t3] "=&v"(tq[3]), "+{m0}"(m0v)
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q0], 0\n\tds_read_b128 %[t0], %[a4] offset:0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d0], %[src] nt\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q1], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:0\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q2], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:0\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q3], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:0\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q4], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:256\n\ts_add_u32 m0, m0, 0xffff8000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d1], %[src] nt\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q5], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:256\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q6], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:256\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q7], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:256\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q8], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:256\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d2], %[src] nt\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q9], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:256\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q10], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:256\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q11], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:256\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q12], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:512\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d3], %[src] nt\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q13], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:512\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q14], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:512\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q15], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:512\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q16], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:512\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d4], %[src] nt\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q17], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:512\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q18], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:512\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q19], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:512\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q20], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:768\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d5], %[src] nt\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q21], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:768\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q22], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:768\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q23], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:768\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q24], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:768\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d6], %[src] nt\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q25], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:768\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q26], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:768\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q27], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:768\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q28], %[sa]\n\tds_read_b128 %[t0], %[r0] offset:0\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d7], %[src] nt\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q29], %[sa]\n\tds_read_b128 %[t1], %[r1] offset:0\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q30], %[sa]\n\tds_read_b128 %[t2], %[r2] offset:0\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q31], %[sa]\n\tds_read_b128 %[t3], %[r3] offset:0\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q32], %[sa]\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d8], %[src] nt\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q33], %[sa]\n\t"
+              "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q34], %[sa]\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q35], %[sa]\n\t"
+              "s_nop 7\n\ts_nop 5"
+              : [sa] "=&v"(sa), [t0] "=&v"(tq[0]), [t1] "=&v"(tq[1]), [t2] "=&v"(tq[2]), [t3] "=&v"(tq[3]), [btn] "=&s"(bt_next), "+{m0}"(m0v)
               : [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]),
                 [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]),
                 [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]),
@@ -420,8 +490,9 @@ void decode_kernel(DecodeArgs a) {
                 [q30] "v"(q[30]), [q31] "v"(q[31]), [q32] "v"(q[32]), [q33] "v"(q[33]), [q34] "v"(q[34]), [q35] "v"(q[35]),
                 [a0] "v"(aq[0]), [a1] "v"(aq[1]), [a2] "v"(aq[2]), [a3] "v"(aq[3]), [a4] "v"(aq[4]), [a5] "v"(aq[5]), [a6] "v"(aq[6]), [a7] "v"(aq[7]),
                 [r0] "v"(ar[0]), [r1] "v"(ar[1]), [r2] "v"(ar[2]), [r3] "v"(ar[3]),
-                [src] "s"(dsrc), [d0] "v"(dv[0]), [d1] "v"(dv[1]), [d2] "v"(dv[2]), [d3] "v"(dv[3]), [d4] "v"(dv[4]), [d5] "v"(dv[5]), [d6] "v"(dv[6]), [d7] "v"(dv[7]), [d8] "v"(dv[8])
+                [src] "s"(dsrc), [btp] "s"(btp), [bto] "s"(bto), [d0] "v"(dv[0]), [d1] "v"(dv[1]), [d2] "v"(dv[2]), [d3] "v"(dv[3]), [d4] "v"(dv[4]), [d5] "v"(dv[5]), [d6] "v"(dv[6]), [d7] "v"(dv[7]), [d8] "v"(dv[8])
               : "memory");
+          bt_pref = bt_next;
         } else {
           asm volatile(
               "s_nop 1\n\t"
@@ -429,44 +500,44 @@ void decode_kernel(DecodeArgs a) {
               "ds_read_b128 %[t1], %[a1] offset:0\n\t"
               "ds_read_b128 %[t2], %[a2] offset:0\n\t"
               "ds_read_b128 %[t3], %[a3] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q0], 0\n\tds_read_b128 %[t0], %[a4] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q1], 0\n\tds_read_b128 %[t1], %[a5] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q2], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q3], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q4], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q5], %[sb]\n\tds_read_b128 %[t1], %[a1] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q6], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q7], %[sb]\n\tds_read_b128 %[t3], %[a3] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q8], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q9], %[sb]\n\tds_read_b128 %[t1], %[a5] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q10], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q11], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:256\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q12], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q13], %[sb]\n\tds_read_b128 %[t1], %[a1] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q14], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q15], %[sb]\n\tds_read_b128 %[t3], %[a3] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q16], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q17], %[sb]\n\tds_read_b128 %[t1], %[a5] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q18], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q19], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:512\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q20], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q21], %[sb]\n\tds_read_b128 %[t1], %[a1] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q22], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q23], %[sb]\n\tds_read_b128 %[t3], %[a3] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q24], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q25], %[sb]\n\tds_read_b128 %[t1], %[a5] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q26], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q27], %[sb]\n\tds_read_b128 %[t3], %[a7] offset:768\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q28], %[sa]\n\tds_read_b128 %[t0], %[r0] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q29], %[sb]\n\tds_read_b128 %[t1], %[r1] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q30], %[sa]\n\tds_read_b128 %[t2], %[r2] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q31], %[sb]\n\tds_read_b128 %[t3], %[r3] offset:0\n\t"
-              "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q32], %[sa]\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t1], %[q33], %[sb]\n\t"
-              "s_waitcnt lgkmcnt(1)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q34], %[sa]\n\t"
-              "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 %[sb], %[t3], %[q35], %[sb]\n\t"
-              "s_nop 7\n\ts_nop 7\n\ts_nop 7"
-              : [sa] "=&v"(sa), [sb] "=&v"(sb), [t0] "=&v"(tq[0]), [t1] "=&v"(tq[1]), [t2] "=&v"(tq[2]), [t3] "=&v"(tq[3])
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q0], 0\n\tds_read_b128 %[t0], %[a4] offset:0\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q1], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:0\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q2], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:0\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q3], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:0\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q4], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:256\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q5], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:256\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q6], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:256\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q7], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:256\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q8], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:256\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q9], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:256\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q10], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:256\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q11], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:256\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q12], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:512\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q13], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:512\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q14], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:512\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q15], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:512\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q16], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:512\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q17], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:512\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q18], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:512\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q19], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:512\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q20], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:768\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q21], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:768\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q22], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:768\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q23], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:768\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q24], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:768\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q25], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:768\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q26], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:768\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q27], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:768\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q28], %[sa]\n\tds_read_b128 %[t0], %[r0] offset:0\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q29], %[sa]\n\tds_read_b128 %[t1], %[r1] offset:0\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q30], %[sa]\n\tds_read_b128 %[t2], %[r2] offset:0\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q31], %[sa]\n\tds_read_b128 %[t3], %[r3] offset:0\n\t"
+              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q32], %[sa]\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q33], %[sa]\n\t"
+              "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q34], %[sa]\n\t"
+              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q35], %[sa]\n\t"
+              "s_nop 7\n\ts_nop 5"
+              : [sa] "=&v"(sa), [t0] "=&v"(tq[0]), [t1] "=&v"(tq[1]), [t2] "=&v"(tq[2]), [t3] "=&v"(tq[3])
               : [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]),
                 [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]),
                 [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]),
@@ -483,31 +554,18 @@ void decode_kernel(DecodeArgs a) {
       // ---- PV of tile k-1 (at k = 0: the zeroed P buffer 1 with the current, finite
       // tile as V, which adds exact zeros), interleaved with the softmax of tile k.
       //   A (P), head block hb, k-step st: head 32hb + l32, tokens 16st + 8hi + 0..7
-      //     -> pprev + offP[st] + 2048 hb
+      //     -> (pprev + offP0) XOR 32st, + 2048 hb
       //   B (c_KV columns, transposing reads), half r, column block c: token 16st + 8hi + 4r + e,
-      //     chunk 16w + 4c + cb, byte 8 (lane & 1) -> vprev + offV[c][r] + 16384 st + 4096 r
+      //     chunk 16w + 4c + cb, byte 8 (lane & 1) -> (vprev + offV0) XOR (64c + 16r), + 16384 st + 4096 r
       const unsigned char* vprev = lds + ((k == 0 ? 0 : k - 1) & 3) * kTileBytes;
       const unsigned char* pprev = pbuf + ((k - 1) & 1) * kPBytes;
-      int offP[2], offV[4][2];
-      {
-        const int ln = opaque_lane(), lh = ln >> 5, ll = ln & 31;
-        const int pr = (ll >> 2) & 3;
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) offP[q2] = ll * 64 + 16 * ((2 * q2 + lh) ^ pr);
-        const int eb = (ln & 15) >> 2;
-        const int cb = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int r = 0; r < 2; ++r)
-            offV[c][r] = (8 * lh + eb) * 1024 + 64 * (c ^ eb) + 16 * (cb ^ (2 * lh + r)) + 8 * (ln & 1) + 256 * wave_u;
-      }
+      const uint32_t vb = lds_addr(vprev) + offV0, pb = lds_addr(pprev) + offP0;
       auto ld_v = [&](int st, int c) -> s16x8 {
-        const s16x4 v0 = lds_read_tr4(vprev + offV[c][0] + 16384 * st);
-        const s16x4 v1 = lds_read_tr4(vprev + offV[c][1] + 16384 * st + 4096);
+        const s16x4 v0 = lds_read_tr4_at((vb ^ (64u * c)) + 16384 * st);
+        const s16x4 v1 = lds_read_tr4_at((vb ^ (64u * c + 16u)) + 16384 * st + 4096);
         return s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       };
-      auto ld_p = [&](int st, int hb) -> s16x8 { return *(const s16x8*)(pprev + offP[st] + 2048 * hb); };
+      auto ld_p = [&](int st, int hb) -> s16x8 { return lds_read_b128_at((pb ^ (32u * st)) + 2048 * hb); };
       s16x8 pa[4], bv[4], bvn;
       pa[0] = ld_p(0, 0);
       bv[0] = ld_v(0, 0);
@@ -522,12 +580,12 @@ void decode_kernel(DecodeArgs a) {
       float sc[16], xa[16], ex[16];
       float mx = -INFINITY;
       auto score = [&](int j) {
-        sc[j] = sa[j] + sb[j];
+        sc[j] = sa[j];
         if constexpr (kMasked) {
           const int t = 8 * (j >> 2) + 4 * hi + (j & 3);
           if (t >= tile_valid(k)) sc[j] = -INFINITY;
         }
-        if (j & 1) mx = __builtin_fmaxf(mx, __builtin_fmaxf(sc[j - 1], sc[j]));
+        if (j & 1) mx = max3f(mx, sc[j - 1], sc[j]);
       };
       if constexpr (kFirst) {
         // The reference maximum is needed before the first weight: all scores first.
@@ -579,6 +637,10 @@ void decode_kernel(DecodeArgs a) {
           for (int qq = 0; qq < 4; ++qq) *(u32x2*)(pk + 16 * (qq ^ sw)) = pw[qq];
         }
         if (!kFirst && st == 21) m_seen = fmaxf(m_seen, mx * a.scale_log2);
+        if constexpr (!kMasked) {
+          if (st >= 22 && st < 25) prep_qk(k + 1, st - 22);
+          if (st >= 25 && st < 28) prep_dma(k + 3, bt_pref, st - 25);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -597,29 +659,16 @@ void decode_kernel(DecodeArgs a) {
     {
       const unsigned char* vlast = lds + (k & 3) * kTileBytes;
       const unsigned char* plast = pbuf + (k & 1) * kPBytes;
-      int offP[2], offV[4][2];
-      {
-        const int ln = opaque_lane(), lh = ln >> 5, ll = ln & 31;
-        const int pr = (ll >> 2) & 3;
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) offP[q2] = ll * 64 + 16 * ((2 * q2 + lh) ^ pr);
-        const int eb = (ln & 15) >> 2;
-        const int cb = 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int r = 0; r < 2; ++r)
-            offV[c][r] = (8 * lh + eb) * 1024 + 64 * (c ^ eb) + 16 * (cb ^ (2 * lh + r)) + 8 * (ln & 1) + 256 * wave_u;
-      }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         s16x8 pa[4], bv[4];
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) pa[hb] = *(const s16x8*)(plast + offP[st] + 2048 * hb);
+        for (int hb = 0; hb < 4; ++hb) pa[hb] = lds_read_b128_at(((lds_addr(plast) + offP0) ^ (32u * st)) + 2048 * hb);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const s16x4 v0 = lds_read_tr4(vlast + offV[c][0] + 16384 * st);
-          const s16x4 v1 = lds_read_tr4(vlast + offV[c][1] + 16384 * st + 4096);
+          const uint32_t vl = lds_addr(vlast) + offV0;
+          const s16x4 v0 = lds_read_tr4_at((vl ^ (64u * c)) + 16384 * st);
+          const s16x4 v1 = lds_read_tr4_at((vl ^ (64u * c + 16u)) + 16384 * st + 4096);
           bv[c] = s16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         }
 #pragma unroll
@@ -643,13 +692,19 @@ void decode_kernel(DecodeArgs a) {
       __syncthreads();
       const bool again = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
       m_redo = m_all;         // the segment's true maximum: no score exceeds it on a redo
-      // normalise and write: O tile (hb, c), register j -> head 32hb + 8(j/4) + 4hi + (j%4),
-      // column 128w + 32c + l32 (the lane part 4hi is folded into the base pointer so the
-      // per-register row offsets are compile-time constants)
+      // normalise and write.  In registers, O tile (hb, c) register j is head
+      // 32hb + 8(j/4) + 4hi + (j%4), column 128w + 32c + l32: one column per lane.
+      // Each head block goes through a private LDS region of the wave (the ring is
+      // free now) so that the global stores are row-contiguous: lane (l32, hi) then
+      // holds head 32hb + 2i + hi, columns 128w + 4 l32 .. +3, and one store instruction
+      // writes two 512-byte row segments.  Row pitch 544 B keeps the two half-waves'
+      // LDS writes 32 banks apart.
       if (!again) {
         const float lse2 = m_ref + __log2f(l_head);
         const float* lrow = lsum + 4 * hi;   // head 32hb + 8(j/4) + (j%4) from here
-        const size_t obase = (size_t)(4 * hi) * kLatent + wave_u * 128 + l32;
+        constexpr int kStagePitch = 544;
+        unsigned char* stage = lds + 1024 + wave_u * (32 * kStagePitch);
+        const size_t obase = (size_t)hi * kLatent + wave_u * 128 + 4 * l32;
         uint16_t* ob16 = a.out_latent + (size_t)u * kHeads * kLatent + obase;
         float* ob32 = a.part_o + (size_t)(slot < 0 ? 0 : slot) * kHeads * kLatent + obase;
 #pragma unroll
@@ -660,15 +715,22 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const f32x16 v = o[hb][c] * il;
-            if (slot < 0) {
 #pragma unroll
-              for (int j = 0; j < 16; ++j) ob16[(32 * hb + 8 * (j >> 2) + (j & 3)) * kLatent + 32 * c] = f2bf(v[j]);
-            } else {
-#pragma unroll
-              for (int j = 0; j < 16; ++j) ob32[(32 * hb + 8 * (j >> 2) + (j & 3)) * kLatent + 32 * c] = v[j];
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < 16; ++j)
+              *(float*)(stage + (8 * (j >> 2) + 4 * hi + (j & 3)) * kStagePitch + (32 * c + l32) * 4) = v[j];
           }
+          // the wave reads back only what it wrote: LDS order within the wave suffices
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const f32x4 x = *(const f32x4*)(stage + (2 * i + hi) * kStagePitch + 16 * l32);
+            const size_t row = (size_t)(32 * hb + 2 * i) * kLatent;
+            if (slot < 0) {
+              *(u32x2*)(ob16 + row) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+            } else {
+              *(f32x4*)(ob32 + row) = x;
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
         if (hi == 0) {
           if (slot < 0) {
