@@ -46,12 +46,21 @@ def _dev_i32(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
+WARM_SECONDS = 1.5   # untimed decode work before each timed region: the clock settles under the power cap
+
+
 def _time_calls(fn, steps, warmup, torch, mla):
-    """Warm up, then time exactly `steps` calls between two synchronisations.
-    Returns (ms per call from stream events, per-kernel ms per call)."""
+    """Warm up (`warmup` calls, and at least WARM_SECONDS of calls so that the
+    engine clock has settled), then time exactly `steps` calls between two
+    synchronisations.  Returns (ms per call from stream events, per-kernel ms per call)."""
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
+    t0 = time.time()
+    while time.time() - t0 < WARM_SECONDS:
+        for _ in range(10):
+            fn(0)
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     with mla.KernelTimer() as kt:
