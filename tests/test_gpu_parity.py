@@ -139,6 +139,45 @@ def test_workload_sampled_check(name):
     _sampled_check(inp, d, qa, ol, lse, batches)
 
 
+def test_workload_c4_sampled_layers():
+    """The 60-layer long-context workload at full size: 16 sequences x 65536 tokens per
+    layer, the 60 layers' caches in one 72 GB device pool (so later layers sit at byte
+    offsets beyond 2^36), one decode call per layer as a model would run it.  Sampled
+    (layer, sequence) pairs are checked against the oracle on host copies of exactly
+    the pages that sequence reads."""
+    import torch
+    inp = make_inputs("c4")
+    layers, P = 60, inp.num_pages
+    _print_case("c4 (60 layers)", inp)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(inp.seed)
+    pool = torch.empty((layers * P, 64, 576), dtype=torch.bfloat16, device="cuda")
+    for i in range(layers):
+        pool[i * P:(i + 1) * P].normal_(generator=g)
+    qa = absorbed_inputs(inp)
+    d_qa, d_qr = dev_bf16(qa), dev_bf16(inp.q_r)
+    d_bt, d_sl = dev_i32(inp.block_table), dev_i32(inp.seqlens)
+    try:
+        for layer in (0, 37, layers - 1):
+            ol, lse = mla.decode_paged(d_qa, d_qr, pool[layer * P:(layer + 1) * P], d_bt, d_sl, scale=inp.scale)
+            torch.cuda.synchronize()
+            got_ol, got_lse = host_f64(ol), lse.double().cpu().numpy()
+            for b in (0, 7, inp.batch - 1):
+                L = int(inp.seqlens[b])
+                n = (L + 63) // 64
+                pages = inp.block_table[b, :n].astype(np.int64)
+                sub = host_bits(pool[layer * P + torch.from_numpy(pages).cuda()])
+                bt1 = np.arange(n, dtype=np.int32).reshape(1, n)
+                ref_ol, ref_lse = oracle.decode_absorbed(qa[b:b + 1], inp.q_r[b:b + 1], sub, bt1,
+                                                         inp.seqlens[b:b + 1], 1, inp.scale)
+                print(f"[c4] layer {layer} seq {b}: {L} tokens", flush=True)
+                assert_close(got_ol[b:b + 1], ref_ol, f"out_latent layer {layer} seq {b}")
+                assert np.max(np.abs(got_lse[b:b + 1] - ref_lse)) <= LSE_ATOL
+    finally:
+        del pool
+        torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ fused path vs the decompress definition
 
 def test_fused_c1_all_heads():
