@@ -30,12 +30,36 @@ void head_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
   const int n0 = blockIdx.x * NWG;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+  // Stage the weight slab with every load in flight at once (a load-store loop
+  // would pay one HBM round trip per iteration).
+  constexpr int kChunks = K * kChunksPerRowW / 256;
+  static_assert(K * kChunksPerRowW % 256 == 0, "slab must split evenly over the workgroup");
   const uint16_t* Bh = B + (size_t)h * K * N + n0;
-  for (int c = tid; c < K * kChunksPerRowW; c += 256) {
-    const int k = c / kChunksPerRowW, j = c % kChunksPerRowW;
-    const u32x4 v = *(const u32x4*)(Bh + (size_t)k * N + j * 8);
-    *(u32x4*)(tile + k * kPitch + j * 16) = v;
+  {
+    u32x4 wv[kChunks];
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int c = tid + 256 * i, k = c / kChunksPerRowW, j = c % kChunksPerRowW;
+      wv[i] = __builtin_nontemporal_load((const u32x4*)(Bh + (size_t)k * N + j * 8));
+    }
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int c = tid + 256 * i, k = c / kChunksPerRowW, j = c % kChunksPerRowW;
+      *(u32x4*)(tile + k * kPitch + j * 16) = wv[i];
+    }
   }
+
+  // A operand of token tile m0 (rows m0 + lane % 16, columns 32ks + 8(lane / 16) .. +7),
+  // all K/32 k-steps loaded together; rows past T read row 0 and are never stored.
+  constexpr int kKS = K / 32;
+  auto load_a = [&](int m0, s16x8 (&a)[kKS]) {
+    const int arow = m0 + (lane & 15);
+    const uint16_t* Ap = A + ((size_t)(arow < T ? arow : 0) * kHeads + h) * K + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) a[ks] = *(const s16x8*)(Ap + ks * 32);
+  };
+  s16x8 acur[kKS], anext[kKS];
+  load_a(0, acur);
   __syncthreads();
 
   // Transposing-read source: lane s of 16-lane group g addresses row 8g + s/4
@@ -44,23 +68,19 @@ void head_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
   const unsigned char* tr_base = tile + (8 * g + (s >> 2)) * kPitch + ((s & 3) * 4) * 2;
 
   for (int m0 = 0; m0 < T; m0 += 16) {
+    if (m0 + 16 < T) load_a(m0 + 16, anext);   // next tile's operand in flight during this tile
     f32x4 acc[kNB];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int arow = m0 + (lane & 15);
-    const bool avalid = arow < T;
-    const uint16_t* Ap = A + ((size_t)(avalid ? arow : 0) * kHeads + h) * K + 8 * (lane >> 4);
-#pragma unroll 4
-    for (int ks = 0; ks < K / 32; ++ks) {
-      s16x8 a = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (avalid) a = *(const s16x8*)(Ap + ks * 32);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
         const unsigned char* p = tr_base + ks * 32 * kPitch + (wave * kNB + nb) * 16 * 2;
         const s16x4 lo = lds_read_tr4(p);
         const s16x4 hi = lds_read_tr4(p + 4 * kPitch);
         const s16x8 b = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[nb] = mfma16(a, b, acc[nb]);
+        acc[nb] = mfma16(acur[ks], b, acc[nb]);
       }
     }
     // D layout of the 16x16 tile: lane l, register j -> row 4*(l/16) + j, column l % 16.
@@ -73,6 +93,8 @@ void head_gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict
         if (row < T) C[((size_t)row * kHeads + h) * N + col] = f2bf(acc[nb][j]);
       }
     }
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) acur[ks] = anext[ks];
   }
 }
 

@@ -97,6 +97,31 @@ def test_needle_takes_all_the_weight(s_q, pos):
             assert np.max(np.abs(got[0, i] - c[None, :])) > 0.1      # the needle is not visible to this query
 
 
+@pytest.mark.parametrize("margin,pos", [(100.0, 1000), (300.0, 2999), (100.0, 70)])
+def test_score_far_above_the_first_tile_redoes_the_segment(margin, pos):
+    """A score more than 64 log2 units above its segment's first-tile maximum makes the
+    kernel redo the segment with the true maximum; at 100 or 300 (natural units) above
+    the rest, exp against the first tile's maximum would overflow fp32."""
+    L = 3000
+    inp = make_custom(58, 1, 1, [L], extra_blocks=1)
+    qa = np.zeros((1, 1, 128, 512), dtype=np.uint16)
+    q_r = np.full((1, 1, 128, 64), 0x3F80, dtype=np.uint16)
+    pool = inp.pool.copy()
+    pool[..., 512:] = 0
+    alpha = margin / (64 * inp.scale)
+    page = inp.block_table[0, pos // 64]
+    pool[page, pos % 64, 512:] = oracle.f64_to_bf16_bits(np.full(64, alpha))
+    a_bf16 = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(np.array([alpha])))[0]
+    needle_score = 64 * a_bf16 * inp.scale                          # the score after bf16 rounding of k_R
+    ol, lse = _run(inp, dev_bf16(pool), dev_i32(inp.block_table), qa, num_splits=7, q_r=q_r)
+    got = oracle.bf16_bits_to_f64(ol)
+    c = oracle.bf16_bits_to_f64(pool[page, pos % 64, :512])
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got[0, 0] - c[None, :])) <= 2 ** -8 * np.max(np.abs(c))
+    # lse = needle + ln(1 + (L - 1) e^-needle) = needle to fp32 precision
+    assert np.max(np.abs(lse[0, 0] - needle_score)) <= 1e-5 * needle_score + 1e-3
+
+
 def test_single_token_bit_exact():
     inp = make_custom(55, 3, 1, [1, 1, 1])
     qa = absorbed_inputs(inp)
