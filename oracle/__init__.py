@@ -11,6 +11,18 @@ printed values of the pages (``tests/golden/``), textbook special cases,
 invariants and brute force.  No function here is "parity unpinned".
 """
 
+from .cache_append import (  # noqa: F401
+    append_kv,
+    append_positions,
+    append_rows,
+    append_to_pool,
+    down_project,
+    rope_angles,
+    rope_q,
+    rope_rotate,
+    rope_table,
+    slot_of,
+)
 from .capacity import (  # noqa: F401
     element_reduction,
     kv_cache_bytes,

@@ -181,3 +181,20 @@ def poison_unused(inp: MlaInputs, nan_bits: int = 0x7FC0) -> MlaInputs:
         used[inp.block_table[b, t // PAGE], t % PAGE] = True
     inp.pool[~used] = np.uint16(nan_bits)
     return inp
+
+
+D_MODEL = 7168   # hidden size d of DeepSeek ("撕开 DeepSeek MLA 源码", section 3, kHiddenDim)
+
+
+def make_append_inputs(seed: int, batch: int, s_q: int, d_model: int = D_MODEL, row: int = ROW):
+    """Hidden states of the new tokens and the joint down-projection weight.
+
+    Draw order from ``numpy.random.default_rng(seed)``: ``x [B, s_q, d]`` then
+    ``W_A [d, row]``, each ``standard_normal`` float32, the weight times
+    ``float32(1/sqrt(d))`` so the projected values have unit scale, then
+    rounded to bf16 bits (nearest, ties to even).
+    """
+    rng = np.random.default_rng(seed)
+    x = _draw_bf16(rng, (batch, s_q, d_model))
+    w_a = _draw_bf16(rng, (d_model, row), 1.0 / math.sqrt(d_model))
+    return x, w_a

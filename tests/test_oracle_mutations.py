@@ -10,6 +10,10 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
+# (oracle module, pin file) -> {name: (anchor, replacement)}
+ATTENTION = ("mla_oracle.py", "test_oracle_attention.py")
+APPEND = ("cache_append.py", "test_oracle_append.py")
+
 MUTATIONS = {
     "dropped RoPE term": ("s = (K[:n] @ q_c[b, i, h] + r[:n] @ q_r[b, i, h]) * scale",
                           "s = (K[:n] @ q_c[b, i, h]) * scale"),
@@ -26,17 +30,35 @@ MUTATIONS = {
     "W_UK heads reversed": ("qa = np.matmul(q, w_uk)", "qa = np.matmul(q, w_uk[::-1])"),
     "merge weights unnormalised": ("wn = w / tot", "wn = w"),
 }
+MUTATIONS = {name: (ATTENTION, old, new) for name, (old, new) in MUTATIONS.items()}
+MUTATIONS.update({name: (APPEND, old, new) for name, (old, new) in {
+    "rotation sign flipped": ("out[..., 0::2] = a * cos - b * sin", "out[..., 0::2] = a * cos + b * sin"),
+    "cosine and sine swapped": ("cos, sin = t[..., :half], t[..., half:]", "sin, cos = t[..., :half], t[..., half:]"),
+    "pairs taken as halves": ("a, b = v[..., 0::2], v[..., 1::2]", "a, b = v[..., :half], v[..., half:]"),
+    "frequency exponent halved": ("theta = base ** (-2.0 * i / d_r)", "theta = base ** (-1.0 * i / d_r)"),
+    "table halves in the wrong order": ("np.concatenate([np.cos(a), np.sin(a)], axis=1)",
+                                        "np.concatenate([np.sin(a), np.cos(a)], axis=1)"),
+    "angle from an fp32 product": ("return p[:, None] * theta[None, :]",
+                                   "return (p[:, None].astype(np.float32) * theta[None, :].astype(np.float32)).astype(np.float64)"),
+    "new-token position off by one": ("return L[:, None] - int(s_q) + np.arange", "return L[:, None] - int(s_q) + 1 + np.arange"),
+    "RoPE applied to the latent": ("out[..., d_c:] = rope_rotate(row[..., d_c:], rows_t)",
+                                   "out[..., :64] = rope_rotate(row[..., :64], rows_t)"),
+    "row within page shifted": ("return pg, p % page", "return pg, (p + 1) % page"),
+    "invalid page written": ("if pg < 0 or pg >= num_pages:", "if pg >= num_pages:"),
+    "query turned the other way": ("out = rope_rotate(q, rows_t)",
+                                   "out = rope_rotate(q, np.concatenate([rows_t[..., :32], -rows_t[..., 32:]], -1))"),
+}.items()})
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name, tmp_path):
-    src = open(os.path.join(ROOT, "oracle", "mla_oracle.py"), encoding="utf-8").read()
-    old, new = MUTATIONS[name]
+    (module, pins), old, new = MUTATIONS[name]
+    src = open(os.path.join(ROOT, "oracle", module), encoding="utf-8").read()
     assert old in src, "mutation anchor no longer present: " + name
     for d in ("oracle", "synth", "tests"):
         shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
                         ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutations.py"))
-    (tmp_path / "oracle" / "mla_oracle.py").write_text(src.replace(old, new), encoding="utf-8")
-    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_attention.py", "-q", "-x",
+    (tmp_path / "oracle" / module).write_text(src.replace(old, new), encoding="utf-8")
+    r = subprocess.run([sys.executable, "-m", "pytest", "tests/" + pins, "-q", "-x",
                         "-p", "no:cacheprovider"], cwd=tmp_path, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"pins missed: {name}\n{r.stdout[-2000:]}"
