@@ -136,6 +136,79 @@ mla_status mla_decode(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* 
 mla_status mla_gather_kv(const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens,
                          uint16_t* dense, const mla_decode_params* p, void* stream);
 
+/* ---------------------------------------------------------------- cache append
+ *
+ * Each decode step first appends its new tokens to the cache
+ * ("DeepSeek的推理为什么比别人便宜一个数量级", leslieaibin.github.io, the decode
+ * loop of the closing summary): the hidden state x is compressed to the latent
+ * c = x . W_DKV, d -> d_c = 512 (same page, section "MLA", first step; d = 7168
+ * for DeepSeek, kHiddenDim in sheratonhq.com section 3), and the 64-value key
+ * k_R, shared by all heads (sheratonhq.com section 1), is rotated with RoPE
+ * computed from an fp32 precomputed table with fp32 multiply-add
+ * (sheratonhq.com section 4, verification paragraph; rope_compute_dtype fp32
+ * in the section 3 plugin JSON).  Where the pages are silent this library
+ * takes k_R = RoPE(x . W_KR) from the same x, passes W_DKV and W_KR as one
+ * matrix W_A = [W_DKV | W_KR] [d, 576], applies no normalisation to c, and
+ * rotates the interleaved pairs (2i, 2i + 1), i = 0..31.
+ *
+ * New token i (0 <= i < s_q) of sequence b has position p = seqlens[b] - s_q + i
+ * (seqlens counts the new tokens, as for the decode) and its row goes to row
+ * p % 64 of page block_table[b][p / 64]. */
+
+typedef struct mla_append_params {
+  int32_t batch;              /* B >= 0 sequences */
+  int32_t s_q;                /* new tokens per sequence, >= 1 */
+  int32_t d_model;            /* hidden size d: a multiple of 256, <= 65536 (7168 for DeepSeek) */
+  int32_t page_size;          /* must be 64 */
+  int32_t max_blocks_per_seq; /* row length of block_table, >= 1 */
+  int32_t max_pos;            /* rows of rope_table, >= 1 */
+  int64_t num_pages;          /* physical pages in kv_blocks, >= 1 */
+  int32_t reserved;           /* must be 0 */
+} mla_append_params;
+
+/* Workspace bytes needed by mla_append_kv (fp32 partial sums of the split
+ * projection: at most d/256 x tokens x 576 x 4 bytes, 4.1 MiB for 64 tokens
+ * and d = 7168).  Returns 0 when p is invalid.  No HIP call. */
+size_t mla_append_workspace_size(const mla_append_params* p);
+
+/* Writes the new tokens' cache rows.
+ *   x           [B, s_q, d] bf16 hidden states of the new tokens
+ *   w_a         [d, 576] bf16, columns 0..511 = W_DKV, 512..575 = W_KR
+ *   rope_table  [max_pos, 64] fp32, row p = cos(p theta_0..31) then
+ *               sin(p theta_0..31) (mla_rope_table writes one; any table of
+ *               this layout works, e.g. a rescaled one)
+ *   block_table [B, max_blocks_per_seq] int32, seqlens [B] int32 (as for decode)
+ *   kv_blocks   [num_pages, 64, 576] bf16, updated in place: only the rows of
+ *               the new tokens are written, c in 0..511 and k_R in 512..575,
+ *               each the fp32 result rounded once to bf16 (nearest, even)
+ *   workspace   >= mla_append_workspace_size(p) bytes, 16-byte aligned, no
+ *               initialisation needed; calls sharing it must be ordered on one
+ *               stream.
+ * Accumulation is fp32 in a fixed order: repeated calls give identical bits.
+ * A token whose position is negative, >= max_pos or past the block-table row,
+ * or whose page id is outside [0, num_pages), is not written (device values are
+ * preconditions; nothing outside the buffers is touched).  Tokens of one call
+ * must not share a slot. */
+mla_status mla_append_kv(const uint16_t* x, const uint16_t* w_a, const float* rope_table,
+                         const int32_t* block_table, const int32_t* seqlens, uint16_t* kv_blocks,
+                         const mla_append_params* p, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Rotates the RoPE query in place with the key's rotation at the same position:
+ * q_r [B, s_q, num_heads, 64] bf16, token i of sequence b at p = seqlens[b] - s_q + i,
+ * every head turned by the angles of table row p (fp32 multiply-add, one RNE
+ * rounding to bf16).  Tokens with p < 0 or p >= max_pos are left unchanged.
+ * 1 <= num_heads <= 4096.  sheratonhq.com section 4 (fp32 RoPE). */
+mla_status mla_rope_q(uint16_t* q_r, const float* rope_table, const int32_t* seqlens, int32_t batch, int32_t s_q,
+                      int32_t num_heads, int32_t max_pos, void* stream);
+
+/* Fills rope_table [max_pos, 64] fp32: entry (p, i) = cos(p theta_i) and entry
+ * (p, 32 + i) = sin(p theta_i), theta_i = base^(-2i/64), with the angle, cosine
+ * and sine evaluated in double precision and each entry rounded once to fp32
+ * (an fp32 angle would carry a phase error at long positions, the failure
+ * sheratonhq.com section 4 attributes to low-precision RoPE).  base > 1
+ * (10000 is the usual value). */
+mla_status mla_rope_table(float* rope_table, int32_t max_pos, double base, void* stream);
+
 /* Benchmark timing hook.  After mla_profile_enable(1), every mla_decode_paged
  * and mla_decode call on any stream records HIP events around each of its
  * kernels (up to 65536 calls; the library creates those events once and keeps

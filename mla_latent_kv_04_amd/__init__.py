@@ -13,7 +13,7 @@ import ctypes
 import math
 
 from . import _lib
-from ._lib import DecodeParams, MlaError  # noqa: F401
+from ._lib import AppendParams, DecodeParams, MlaError  # noqa: F401
 
 NUM_HEADS = 128
 D_HC = 128
@@ -24,7 +24,8 @@ DEFAULT_SCALE = 1.0 / math.sqrt(D_HC + D_R)
 
 __all__ = [
     "absorb_q", "decode_paged", "up_proj", "decode", "gather_kv", "workspace_size", "make_params",
-    "device_cu_count", "MlaError", "DecodeParams", "KernelTimer",
+    "device_cu_count", "MlaError", "DecodeParams", "KernelTimer", "AppendParams", "append_kv",
+    "append_workspace_size", "make_append_params", "rope_q", "rope_table",
 ]
 
 
@@ -221,3 +222,72 @@ def gather_kv(kv_blocks, block_table, seqlens, out=None):
                            _stream())
     _lib.check(st, "mla_gather_kv")
     return out
+
+
+# ------------------------------------------------------------------ cache append
+
+
+def make_append_params(batch: int, s_q: int, d_model: int, max_blocks_per_seq: int, num_pages: int,
+                       max_pos: int) -> AppendParams:
+    p = AppendParams()
+    p.batch, p.s_q, p.d_model, p.page_size = batch, s_q, d_model, PAGE
+    p.max_blocks_per_seq, p.max_pos, p.num_pages, p.reserved = max_blocks_per_seq, max_pos, num_pages, 0
+    return p
+
+
+def append_workspace_size(params: AppendParams) -> int:
+    lib = _lib.load()
+    n = lib.mla_append_workspace_size(ctypes.byref(params))
+    if n == 0:
+        raise MlaError(_lib.MLA_ERR_INVALID_ARG, "mla_append_workspace_size", lib.mla_last_error().decode())
+    return int(n)
+
+
+def rope_table(max_pos: int, base: float = 10000.0, out=None):
+    """fp32 rotary table [max_pos, 64]: cosines then sines of p * base^(-2i/64)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(max_pos, D_R, dtype=torch.float32, device="cuda")
+    lib = _lib.load()
+    st = lib.mla_rope_table(_ptr(out, "rope_table", (torch.float32,), (max_pos, D_R)), max_pos, float(base), _stream())
+    _lib.check(st, "mla_rope_table")
+    return out
+
+
+def append_kv(x, w_a, table, kv_blocks, block_table, seqlens, *, workspace=None):
+    """Writes the rows of the new tokens into the paged cache (in place).
+
+    x [B, s_q, d] bf16, w_a [d, 576] bf16 (W_DKV | W_KR), table [max_pos, 64] fp32,
+    kv_blocks [P, 64, 576], block_table [B, max_blocks] int32, seqlens [B] int32
+    (including the new tokens).  Returns kv_blocks."""
+    torch = _torch()
+    B, s_q, d = (int(v) for v in x.shape)
+    P = int(kv_blocks.shape[0])
+    mb = int(block_table.shape[1])
+    max_pos = int(table.shape[0])
+    params = make_append_params(B, s_q, d, mb, P, max_pos)
+    need = append_workspace_size(params)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    lib = _lib.load()
+    st = lib.mla_append_kv(
+        _ptr(x, "x", _bf16_types(), (B, s_q, d)), _ptr(w_a, "w_a", _bf16_types(), (d, D_C + D_R)),
+        _ptr(table, "table", (torch.float32,), (max_pos, D_R)),
+        _ptr(block_table, "block_table", _i32(), (B, mb)), _ptr(seqlens, "seqlens", _i32(), (B,)),
+        _ptr(kv_blocks, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R)), ctypes.byref(params),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream())
+    _lib.check(st, "mla_append_kv")
+    return kv_blocks
+
+
+def rope_q(q_r, table, seqlens):
+    """Rotates q_r [B, s_q, H, 64] (bf16) in place to positions seqlens[b] - s_q + i."""
+    torch = _torch()
+    B, s_q, H = int(q_r.shape[0]), int(q_r.shape[1]), int(q_r.shape[2])
+    max_pos = int(table.shape[0])
+    lib = _lib.load()
+    st = lib.mla_rope_q(_ptr(q_r, "q_r", _bf16_types(), (B, s_q, H, D_R)),
+                        _ptr(table, "table", (torch.float32,), (max_pos, D_R)),
+                        _ptr(seqlens, "seqlens", _i32(), (B,)), B, s_q, H, max_pos, _stream())
+    _lib.check(st, "mla_rope_q")
+    return q_r

@@ -27,6 +27,10 @@ EXPORTS = (
     "mla_up_proj",
     "mla_decode",
     "mla_gather_kv",
+    "mla_append_workspace_size",
+    "mla_append_kv",
+    "mla_rope_q",
+    "mla_rope_table",
     "mla_profile_enable",
     "mla_profile_collect",
     "mla_device_cu_count",
@@ -47,6 +51,21 @@ class DecodeParams(ctypes.Structure):
         ("num_splits", ctypes.c_int32),
         ("num_pages", ctypes.c_int64),
         ("scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class AppendParams(ctypes.Structure):
+    """Mirror of ``mla_append_params``."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("s_q", ctypes.c_int32),
+        ("d_model", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_pos", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -72,6 +91,7 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     pp = ctypes.POINTER(DecodeParams)
+    ap = ctypes.POINTER(AppendParams)
     sigs = {
         "mla_absorb_q": ([vp, vp, vp, i32, i32, vp], ctypes.c_int),
         "mla_decode_workspace_size": ([pp, i32], sz),
@@ -79,6 +99,10 @@ def load() -> ctypes.CDLL:
         "mla_up_proj": ([vp, vp, vp, i32, i32, vp], ctypes.c_int),
         "mla_decode": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, sz, vp], ctypes.c_int),
         "mla_gather_kv": ([vp, vp, vp, vp, pp, vp], ctypes.c_int),
+        "mla_append_workspace_size": ([ap], sz),
+        "mla_append_kv": ([vp, vp, vp, vp, vp, vp, ap, vp, sz, vp], ctypes.c_int),
+        "mla_rope_q": ([vp, vp, vp, i32, i32, i32, i32, vp], ctypes.c_int),
+        "mla_rope_table": ([vp, i32, ctypes.c_double, vp], ctypes.c_int),
         "mla_device_cu_count": ([ctypes.POINTER(i32)], ctypes.c_int),
         "mla_profile_enable": ([i32], ctypes.c_int),
         "mla_profile_collect": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)], ctypes.c_int),

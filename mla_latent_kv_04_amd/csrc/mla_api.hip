@@ -12,6 +12,7 @@
 
 #include "mla.h"
 #include "common.h"
+#include "append.h"
 
 namespace {
 
@@ -136,9 +137,82 @@ mla_status run_paged(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t*
   return MLA_OK;
 }
 
+mla_status check_append(const mla_append_params* p) {
+  if (p == nullptr) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch %d < 0", p->batch);
+  if (p->s_q < 1) return fail(MLA_ERR_INVALID_ARG, "s_q %d < 1", p->s_q);
+  if ((int64_t)p->batch * p->s_q > (1 << 24)) return fail(MLA_ERR_INVALID_ARG, "batch * s_q too large");
+  if (p->d_model < 256 || p->d_model % 256 != 0 || p->d_model > (1 << 16))
+    return fail(MLA_ERR_UNSUPPORTED, "d_model %d (supported: multiples of 256 up to 65536)", p->d_model);
+  if (p->page_size != mla::kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size %d (supported: 64)", p->page_size);
+  if (p->max_blocks_per_seq < 1 || p->max_blocks_per_seq > (1 << 24))
+    return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_seq %d", p->max_blocks_per_seq);
+  if (p->max_pos < 1 || p->max_pos > (1 << 26)) return fail(MLA_ERR_INVALID_ARG, "max_pos %d", p->max_pos);
+  if (p->num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages %lld < 1", (long long)p->num_pages);
+  if (p->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "reserved must be 0");
+  return MLA_OK;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 }  // namespace
 
 extern "C" {
+
+size_t mla_append_workspace_size(const mla_append_params* p) {
+  if (check_append(p) != MLA_OK) return 0;
+  const int T = p->batch * p->s_q;
+  if (T == 0) return 16;
+  return round_up(mla::plan_append(T, p->d_model).part_bytes);
+}
+
+mla_status mla_append_kv(const uint16_t* x, const uint16_t* w_a, const float* rope_table,
+                         const int32_t* block_table, const int32_t* seqlens, uint16_t* kv_blocks,
+                         const mla_append_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = check_append(p);
+  if (st != MLA_OK) return st;
+  if (p->batch == 0) return ok();
+  if (!x || !w_a || !rope_table || !block_table || !seqlens || !kv_blocks || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(x) || !aligned16(w_a) || !aligned16(rope_table) || !aligned16(kv_blocks) || !aligned16(workspace) ||
+      !aligned4(block_table) || !aligned4(seqlens))
+    return fail(MLA_ERR_MISALIGNED, "tensor or workspace not aligned (16 B; block_table and seqlens 4 B)");
+  const size_t need = mla_append_workspace_size(p);
+  if (workspace_bytes < need) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  hipError_t e = mla::launch_append(x, w_a, rope_table, block_table, seqlens, kv_blocks,
+                                    static_cast<float*>(workspace), p->batch, p->s_q, p->d_model,
+                                    p->max_blocks_per_seq, p->num_pages, p->max_pos,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+mla_status mla_rope_q(uint16_t* q_r, const float* rope_table, const int32_t* seqlens, int32_t batch, int32_t s_q,
+                      int32_t num_heads, int32_t max_pos, void* stream) {
+  if (batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if (s_q < 1) return fail(MLA_ERR_INVALID_ARG, "s_q %d < 1", s_q);
+  if ((int64_t)batch * s_q > (1 << 24)) return fail(MLA_ERR_INVALID_ARG, "batch * s_q too large");
+  if (num_heads < 1 || num_heads > 4096) return fail(MLA_ERR_INVALID_ARG, "num_heads %d", num_heads);
+  if (max_pos < 1 || max_pos > (1 << 26)) return fail(MLA_ERR_INVALID_ARG, "max_pos %d", max_pos);
+  if (batch == 0) return ok();
+  if (!q_r || !rope_table || !seqlens) return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q_r) || !aligned16(rope_table) || !aligned4(seqlens))
+    return fail(MLA_ERR_MISALIGNED, "tensor not aligned (16 B; seqlens 4 B)");
+  hipError_t e = mla::launch_rope_q(q_r, rope_table, seqlens, batch, s_q, num_heads, max_pos,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope_q launch");
+  return ok();
+}
+
+mla_status mla_rope_table(float* rope_table, int32_t max_pos, double base, void* stream) {
+  if (max_pos < 1 || max_pos > (1 << 26)) return fail(MLA_ERR_INVALID_ARG, "max_pos %d", max_pos);
+  if (!(base > 1.0) || base > 1e30) return fail(MLA_ERR_INVALID_ARG, "base must be finite and > 1");
+  if (!rope_table) return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(rope_table)) return fail(MLA_ERR_MISALIGNED, "rope_table not 16-byte aligned");
+  hipError_t e = mla::launch_rope_table(rope_table, max_pos, base, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope_table launch");
+  return ok();
+}
 
 const char* mla_status_string(mla_status s) {
   switch (s) {

@@ -125,3 +125,80 @@ def test_fused_and_gather_argument_checks(lib):
     assert st == _lib.MLA_ERR_MISALIGNED
     assert lib.mla_gather_kv(A, A, A, None, ctypes.byref(p), None) == _lib.MLA_ERR_INVALID_ARG
     assert lib.mla_gather_kv(MIS, A, A, A2, ctypes.byref(p), None) == _lib.MLA_ERR_MISALIGNED
+
+
+# ------------------------------------------------------------------ cache append
+
+
+def _aparams(**kw):
+    p = _lib.AppendParams()
+    p.batch, p.s_q, p.d_model, p.page_size, p.max_blocks_per_seq = 4, 1, 7168, 64, 8
+    p.max_pos, p.num_pages, p.reserved = 4096, 32, 0
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _append(lib, p, ptrs=None, ws=A, ws_bytes=1 << 30):
+    x, w, tab, bt, sl, kv = ptrs or (A, A, A, A, A, A)
+    return lib.mla_append_kv(x, w, tab, bt, sl, kv, ctypes.byref(p), ws, ws_bytes, None)
+
+
+def test_append_params_struct_layout():
+    assert ctypes.sizeof(_lib.AppendParams) == 40 and _lib.AppendParams.num_pages.offset == 24
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d_model", 7000, _lib.MLA_ERR_UNSUPPORTED), ("d_model", 0, _lib.MLA_ERR_UNSUPPORTED),
+    ("d_model", 1 << 17, _lib.MLA_ERR_UNSUPPORTED), ("page_size", 32, _lib.MLA_ERR_UNSUPPORTED),
+    ("batch", -1, _lib.MLA_ERR_INVALID_ARG), ("s_q", 0, _lib.MLA_ERR_INVALID_ARG),
+    ("max_blocks_per_seq", 0, _lib.MLA_ERR_INVALID_ARG), ("max_pos", 0, _lib.MLA_ERR_INVALID_ARG),
+    ("num_pages", 0, _lib.MLA_ERR_INVALID_ARG), ("reserved", 3, _lib.MLA_ERR_INVALID_ARG),
+])
+def test_append_bad_params_rejected(lib, field, value, status):
+    p = _aparams(**{field: value})
+    assert _append(lib, p) == status
+    assert lib.mla_append_workspace_size(ctypes.byref(p)) == 0
+
+
+def test_append_workspace_size(lib):
+    # decode-sized: 9 column blocks x 28 splits of the 7168 hidden rows, fp32 partials [28, T, 576]
+    assert lib.mla_append_workspace_size(ctypes.byref(_aparams(batch=64))) == 28 * 64 * 576 * 4
+    assert lib.mla_append_workspace_size(ctypes.byref(_aparams(batch=4, s_q=2))) == 28 * 8 * 576 * 4
+    # prefill-sized: 64 token groups x 9 column blocks already fill the chip, one split
+    assert lib.mla_append_workspace_size(ctypes.byref(_aparams(batch=1, s_q=4096))) == 4096 * 576 * 4
+    # 1024 tokens: 16 groups x 9 = 144 workgroups, two splits (a divisor of 28) reach 256
+    assert lib.mla_append_workspace_size(ctypes.byref(_aparams(batch=1, s_q=1024))) == 2 * 1024 * 576 * 4
+    assert lib.mla_append_workspace_size(None) == 0
+
+
+def test_append_argument_checks(lib):
+    p = _aparams()
+    need = lib.mla_append_workspace_size(ctypes.byref(p))
+    assert _append(lib, p, ws_bytes=need - 1) == _lib.MLA_ERR_WORKSPACE
+    assert _append(lib, p, ws=None, ws_bytes=need) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_append_kv(A, A, A, A, A, A, None, A, need, None) == _lib.MLA_ERR_INVALID_ARG
+    for which in range(6):
+        ptrs = [A] * 6
+        ptrs[which] = None
+        assert _append(lib, p, tuple(ptrs)) == _lib.MLA_ERR_INVALID_ARG
+        ptrs[which] = MIS if which not in (3, 4) else ctypes.c_void_p(0x10002)
+        assert _append(lib, p, tuple(ptrs)) == _lib.MLA_ERR_MISALIGNED
+    assert _append(lib, p, ws=MIS) == _lib.MLA_ERR_MISALIGNED
+    assert _append(lib, _aparams(batch=0), (None,) * 6, ws=None, ws_bytes=0) == _lib.MLA_OK
+
+
+def test_rope_argument_checks(lib):
+    assert lib.mla_rope_q(A, A, A, -1, 1, 128, 10, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_rope_q(A, A, A, 1, 0, 128, 10, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_rope_q(A, A, A, 1, 1, 0, 10, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_rope_q(A, A, A, 1, 1, 128, 0, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_rope_q(A, None, A, 1, 1, 128, 10, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_rope_q(MIS, A, A, 1, 1, 128, 10, None) == _lib.MLA_ERR_MISALIGNED
+    assert lib.mla_rope_q(A, A, ctypes.c_void_p(0x10002), 1, 1, 128, 10, None) == _lib.MLA_ERR_MISALIGNED
+    assert lib.mla_rope_q(None, None, None, 0, 1, 128, 10, None) == _lib.MLA_OK
+    assert lib.mla_rope_table(A, 0, 10000.0, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_rope_table(A, 10, 1.0, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_rope_table(A, 10, float("nan"), None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_rope_table(None, 10, 10000.0, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_rope_table(MIS, 10, 10000.0, None) == _lib.MLA_ERR_MISALIGNED
