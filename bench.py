@@ -110,6 +110,57 @@ def run_paged(inp, pool_dev, torch, mla, steps, warmup, layers=1, pages_per_laye
     return dict(ms=ms, per=per, cache_bytes=cache_bytes, tokens=int(inp.seqlens.sum()), queries=B * s_q)
 
 
+D_MODEL = 7168                 # hidden size d of the appended tokens' states
+
+
+def append_algorithmic_bytes(tokens, d=D_MODEL):
+    """Bytes the cache append must move once: W_A [d, 576] bf16, x [T, d] bf16, the T new
+    rows written, T fp32 table rows of 64, and one block-table entry and length per token."""
+    return d * 576 * 2 + tokens * d * 2 + tokens * ROW_BYTES + tokens * 64 * 4 + tokens * 8
+
+
+def run_append(inp, pool_dev, torch, mla, steps, warmup):
+    """Time mla_append_kv (one new token per sequence of the workload, hidden size 7168)
+    and mla_rope_q on the same tokens, each as whole calls between stream events."""
+    from synth import make_append_inputs
+    x_bits, w_bits = make_append_inputs(80, inp.batch, inp.s_q)
+    x, w_a = _dev_bf16(x_bits, torch), _dev_bf16(w_bits, torch)
+    table = mla.rope_table(131072)
+    bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
+    params = mla.make_append_params(inp.batch, inp.s_q, D_MODEL, inp.max_blocks, int(pool_dev.shape[0]), 131072)
+    ws = torch.empty(mla.append_workspace_size(params), dtype=torch.uint8, device="cuda")
+    q_r = _dev_bf16(inp.q_r, torch)
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    app_ms = timed(lambda: mla.append_kv(x, w_a, table, pool_dev, bt, sl, workspace=ws), steps)
+    rope_ms = timed(lambda: mla.rope_q(q_r, table, sl), steps)
+    T = inp.batch * inp.s_q
+    alg = append_algorithmic_bytes(T)
+    achieved = alg / (app_ms * 1e-3) / 1e9
+    return {
+        "workload": f"{T} new tokens (one per sequence of the batch-64 workload), d={D_MODEL}, "
+                    "W_A [7168, 576] bf16, fp32 RoPE table of 131072 rows, rows written into the shared pool",
+        "us_per_call": round(app_ms * 1e3, 2),
+        "tokens_per_s": round(T / (app_ms * 1e-3), 1),
+        "rope_q_us_per_call": round(rope_ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "append_gemm_kernel + append_finalize_kernel (whole call)",
+                     "algorithmic_bytes_per_launch": alg},
+    }
+
+
 def cpu_baseline(inp, seconds):
     """The fp64 oracle (absorbed form), timed on host cores on a bounded sample
     of the same workload's sequences."""
@@ -209,6 +260,11 @@ def main():
         del opool
         torch.cuda.empty_cache()
 
+    # ---- cache append of the same step's new tokens (timed after the decodes: it writes
+    # one row per sequence into the pool)
+    app = run_append(inp, pool, torch, mla, args.steps, args.warmup)
+    log(f"[bench] c3 append: {app}")
+
     cpu = None
     if not args.no_cpu:
         log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f}s ...")
@@ -247,6 +303,7 @@ def main():
                      "kernel": "decode_kernel", "algorithmic_bytes_per_launch": r["cache_bytes"]},
         "cpu_baseline": cpu,
         "other_workloads": others,
+        "cache_append": app,
     }
     print(json.dumps(line), flush=True)
 
