@@ -163,15 +163,18 @@ typedef struct mla_append_params {
   int32_t max_blocks_per_seq; /* row length of block_table, >= 1 */
   int32_t max_pos;            /* rows of rope_table, >= 1 */
   int64_t num_pages;          /* physical pages in kv_blocks, >= 1 */
+  int32_t num_heads;          /* heads of q_r when mla_append_kv is given one: 1..4096 (128 for DeepSeek) */
   int32_t reserved;           /* must be 0 */
 } mla_append_params;
 
-/* Workspace bytes needed by mla_append_kv (fp32 partial sums of the split
- * projection: at most d/256 x tokens x 576 x 4 bytes, 4.1 MiB for 64 tokens
- * and d = 7168).  Returns 0 when p is invalid.  No HIP call. */
+/* Workspace bytes needed by mla_append_kv: the fp32 partial sums of the split
+ * projection, splits x tokens x 576 x 4 bytes (2 MiB for 64 tokens and
+ * d = 7168; 16 bytes when the token count alone fills the device and the
+ * projection is not split).  Returns 0 when p is invalid.  No HIP call. */
 size_t mla_append_workspace_size(const mla_append_params* p);
 
-/* Writes the new tokens' cache rows.
+/* Writes the new tokens' cache rows (and, optionally, rotates their RoPE query):
+ * two kernel launches (one when the token count alone fills the device).
  *   x           [B, s_q, d] bf16 hidden states of the new tokens
  *   w_a         [d, 576] bf16, columns 0..511 = W_DKV, 512..575 = W_KR
  *   rope_table  [max_pos, 64] fp32, row p = cos(p theta_0..31) then
@@ -181,6 +184,8 @@ size_t mla_append_workspace_size(const mla_append_params* p);
  *   kv_blocks   [num_pages, 64, 576] bf16, updated in place: only the rows of
  *               the new tokens are written, c in 0..511 and k_R in 512..575,
  *               each the fp32 result rounded once to bf16 (nearest, even)
+ *   q_r         [B, s_q, num_heads, 64] bf16 or NULL: when given, rotated in
+ *               place exactly as mla_rope_q does (same positions and table)
  *   workspace   >= mla_append_workspace_size(p) bytes, 16-byte aligned, no
  *               initialisation needed; calls sharing it must be ordered on one
  *               stream.
@@ -190,7 +195,7 @@ size_t mla_append_workspace_size(const mla_append_params* p);
  * preconditions; nothing outside the buffers is touched).  Tokens of one call
  * must not share a slot. */
 mla_status mla_append_kv(const uint16_t* x, const uint16_t* w_a, const float* rope_table,
-                         const int32_t* block_table, const int32_t* seqlens, uint16_t* kv_blocks,
+                         const int32_t* block_table, const int32_t* seqlens, uint16_t* kv_blocks, uint16_t* q_r,
                          const mla_append_params* p, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Rotates the RoPE query in place with the key's rotation at the same position:

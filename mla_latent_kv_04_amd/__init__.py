@@ -25,7 +25,7 @@ DEFAULT_SCALE = 1.0 / math.sqrt(D_HC + D_R)
 __all__ = [
     "absorb_q", "decode_paged", "up_proj", "decode", "gather_kv", "workspace_size", "make_params",
     "device_cu_count", "MlaError", "DecodeParams", "KernelTimer", "AppendParams", "append_kv",
-    "append_workspace_size", "make_append_params", "rope_q", "rope_table",
+    "append_workspace", "append_workspace_size", "make_append_params", "rope_q", "rope_table",
 ]
 
 
@@ -228,10 +228,11 @@ def gather_kv(kv_blocks, block_table, seqlens, out=None):
 
 
 def make_append_params(batch: int, s_q: int, d_model: int, max_blocks_per_seq: int, num_pages: int,
-                       max_pos: int) -> AppendParams:
+                       max_pos: int, num_heads: int = NUM_HEADS) -> AppendParams:
     p = AppendParams()
     p.batch, p.s_q, p.d_model, p.page_size = batch, s_q, d_model, PAGE
-    p.max_blocks_per_seq, p.max_pos, p.num_pages, p.reserved = max_blocks_per_seq, max_pos, num_pages, 0
+    p.max_blocks_per_seq, p.max_pos, p.num_pages = max_blocks_per_seq, max_pos, num_pages
+    p.num_heads, p.reserved = num_heads, 0
     return p
 
 
@@ -254,27 +255,35 @@ def rope_table(max_pos: int, base: float = 10000.0, out=None):
     return out
 
 
-def append_kv(x, w_a, table, kv_blocks, block_table, seqlens, *, workspace=None):
+def append_workspace(params: AppendParams):
+    """A workspace for mla_append_kv (no initialisation needed)."""
+    return _torch().empty(append_workspace_size(params), dtype=_torch().uint8, device="cuda")
+
+
+def append_kv(x, w_a, table, kv_blocks, block_table, seqlens, *, q_r=None, workspace=None):
     """Writes the rows of the new tokens into the paged cache (in place).
 
     x [B, s_q, d] bf16, w_a [d, 576] bf16 (W_DKV | W_KR), table [max_pos, 64] fp32,
     kv_blocks [P, 64, 576], block_table [B, max_blocks] int32, seqlens [B] int32
-    (including the new tokens).  Returns kv_blocks."""
+    (including the new tokens).  q_r [B, s_q, H, 64] bf16, when given, is rotated in
+    place by the same call.  A workspace passed in is reused only on one stream.
+    Returns kv_blocks."""
     torch = _torch()
     B, s_q, d = (int(v) for v in x.shape)
     P = int(kv_blocks.shape[0])
     mb = int(block_table.shape[1])
     max_pos = int(table.shape[0])
-    params = make_append_params(B, s_q, d, mb, P, max_pos)
-    need = append_workspace_size(params)
+    H = int(q_r.shape[2]) if q_r is not None else NUM_HEADS
+    params = make_append_params(B, s_q, d, mb, P, max_pos, H)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = append_workspace(params)
     lib = _lib.load()
     st = lib.mla_append_kv(
         _ptr(x, "x", _bf16_types(), (B, s_q, d)), _ptr(w_a, "w_a", _bf16_types(), (d, D_C + D_R)),
         _ptr(table, "table", (torch.float32,), (max_pos, D_R)),
         _ptr(block_table, "block_table", _i32(), (B, mb)), _ptr(seqlens, "seqlens", _i32(), (B,)),
-        _ptr(kv_blocks, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R)), ctypes.byref(params),
+        _ptr(kv_blocks, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R)),
+        _ptr(q_r, "q_r", _bf16_types(), (B, s_q, H, D_R)), ctypes.byref(params),
         _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream())
     _lib.check(st, "mla_append_kv")
     return kv_blocks

@@ -66,6 +66,7 @@ class AppendParams(ctypes.Structure):
         ("max_blocks_per_seq", ctypes.c_int32),
         ("max_pos", ctypes.c_int32),
         ("num_pages", ctypes.c_int64),
+        ("num_heads", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -100,7 +101,7 @@ def load() -> ctypes.CDLL:
         "mla_decode": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, sz, vp], ctypes.c_int),
         "mla_gather_kv": ([vp, vp, vp, vp, pp, vp], ctypes.c_int),
         "mla_append_workspace_size": ([ap], sz),
-        "mla_append_kv": ([vp, vp, vp, vp, vp, vp, ap, vp, sz, vp], ctypes.c_int),
+        "mla_append_kv": ([vp, vp, vp, vp, vp, vp, vp, ap, vp, sz, vp], ctypes.c_int),
         "mla_rope_q": ([vp, vp, vp, i32, i32, i32, i32, vp], ctypes.c_int),
         "mla_rope_table": ([vp, i32, ctypes.c_double, vp], ctypes.c_int),
         "mla_device_cu_count": ([ctypes.POINTER(i32)], ctypes.c_int),

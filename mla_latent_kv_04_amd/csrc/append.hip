@@ -12,147 +12,276 @@
 //
 // For decode-sized token counts the projection is bound by reading the 8 MiB
 // weight: the contraction is split over the hidden dimension so that about one
-// workgroup per compute unit streams its own 256 x 64 slab of W_A, and a second
-// kernel sums the fp32 partials in a fixed order (bitwise reproducible), rotates
-// the key in fp32, rounds once to bf16 and writes the row into its page.
+// workgroup per compute unit streams its own 32 KiB slab of W_A and writes an
+// fp32 partial; while its weight loads are in flight each workgroup also rotates
+// a share of the RoPE query of the same tokens.  A second kernel sums the
+// partials in split order (bitwise reproducible), rotates the key in fp32,
+// rounds once to bf16 and writes the rows into their pages.  (Summing in the
+// last-arriving workgroup of each column block instead was measured slower:
+// the arrival ticket and the device-scope release/acquire it needs cost more
+// than the second launch.)  When the token count alone fills the device the
+// contraction is not split and the first kernel writes the rows itself.
 #include "append.h"
 
 namespace mla {
 
 namespace {
 
-constexpr int kSlabRows = 256;                 // hidden-state rows of W_A per pass
-constexpr int kCols = 64;                      // output columns per workgroup
-constexpr int kColBlocks = kRow / kCols;       // 9
+constexpr int kSlabBytes = 32768;              // W_A bytes each workgroup stages per pass
 constexpr int kTokens = 64;                    // tokens per workgroup: 4 waves x 16
 constexpr int kXcds = 8;                       // MI355X: 8 accelerator dies, each with its own L2
 constexpr int kTargetWgs = 256;                // one workgroup per compute unit
+constexpr int kQEarly = 2;                     // q_R chunks per thread rotated under the weight loads
 
-// Partial projection of one (token group, K split, column block) unit:
-//   part[split][t][n0 .. n0 + 63] = sum over the split's hidden rows k of x[t][k] W_A[k][n].
+struct AppendArgs {
+  const uint16_t* x;        // [T, d]
+  const uint16_t* w;        // [d, 576]
+  const float* table;       // [max_pos, 64]
+  const int32_t* bt;        // [B, max_blocks]
+  const int32_t* seqlens;   // [B]
+  uint16_t* kv;             // [num_pages, 64, 576]
+  uint16_t* q_r;            // [T, heads, 64] or null
+  float* part;              // [splits, T, 576] when splits > 1
+  int64_t num_pages;
+  int T, d, s_q, max_blocks, max_pos, heads;
+  int splits, slabs_per_split, units, per_die;
+};
+
+// Position of token t (p = seqlens[b] - s_q + i) and its cache row index
+// page * 64 + p % 64, or -1 when that slot or its table row does not exist.
+__device__ __forceinline__ int64_t slot_of(const AppendArgs& a, int t, int* pos) {
+  const int b = t / a.s_q, i = t - b * a.s_q;
+  const int p = a.seqlens[b] - a.s_q + i;
+  *pos = p;
+  if (p < 0 || p >= a.max_pos || (p >> 6) >= a.max_blocks) return -1;
+  const int page = a.bt[(size_t)b * a.max_blocks + (p >> 6)];
+  if (page < 0 || page >= a.num_pages) return -1;
+  return (int64_t)page * kPage + (p & (kPage - 1));
+}
+
+// Rotates the four pairs held in a 16-byte chunk of bf16 (pair k = halves of word k).
+__device__ __forceinline__ u32x4 rotate_chunk(u32x4 v, const f32x4& c, const f32x4& sn) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float x0 = bf2f((uint16_t)(v[k] & 0xFFFFu)), x1 = bf2f((uint16_t)(v[k] >> 16));
+    v[k] = pack_bf16x2(x0 * c[k] - x1 * sn[k], x0 * sn[k] + x1 * c[k]);
+  }
+  return v;
+}
+
+// One 16-byte chunk of q_R: chunk idx covers pairs 4 (idx % 8) .. +3 of head
+// (idx / 8) % heads of token idx / (8 heads).
+struct QChunk {
+  u32x4 v;
+  f32x4 c, sn;
+  uint16_t* dst;
+};
+
+__device__ __forceinline__ bool load_q_chunk(const AppendArgs& a, size_t idx, QChunk& qc) {
+  const size_t per_token = (size_t)a.heads * (kRope / 8);
+  if (idx >= (size_t)a.T * per_token) return false;
+  const int t = (int)(idx / per_token);
+  const int b = t / a.s_q, i = t - b * a.s_q;
+  const int p = a.seqlens[b] - a.s_q + i;
+  if (p < 0 || p >= a.max_pos) return false;
+  const int qd = (int)(idx & 7);
+  qc.dst = a.q_r + idx * 8;
+  qc.v = *(const u32x4*)qc.dst;
+  qc.c = *(const f32x4*)(a.table + (size_t)p * kRope + 4 * qd);
+  qc.sn = *(const f32x4*)(a.table + (size_t)p * kRope + kRope / 2 + 4 * qd);
+  return true;
+}
+
+// One (token group, K split, column block) unit per workgroup:
+//   partial[t][n0 .. n0 + kCols - 1] = sum over the split's hidden rows k of x[t][k] W_A[k][n].
+// The workgroup stages a 32 KiB slab of W_A (kR rows of kCols columns) in LDS and
+// feeds the MFMA B operand with transposing LDS reads; each wave owns 16 tokens
+// and streams their x values (the A operand) 256 hidden rows at a time.
+// Narrow column blocks mean fewer K splits for the same slab size, hence fewer
+// fp32 partials, at the price of re-reading x (from L2) once per column block.
 // Units are numbered token group, then split, then column block, and handed out
 // so that each die (workgroups go round-robin over the 8 dies) takes a
-// contiguous run: the 9 column blocks that reuse one x slice then share an L2.
+// contiguous run: column blocks that reuse one x slice, and that share the
+// 128-byte lines of W_A rows, then share an L2.
+template <int kCols>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
-void append_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, float* __restrict__ part,
-                        int T, int d, int splits, int slabs_per_split, int units, int per_die) {
-  constexpr int kPitch = kCols * 2 + 32;       // 160 B: four rows a 16-lane group reads start 8 banks apart
-  constexpr int kCPR = kCols * 2 / 16;         // 8 sixteen-byte chunks per weight row
-  constexpr int kChunks = kSlabRows * kCPR / 256;
-  constexpr int kKS = kSlabRows / 32;          // k-steps of v_mfma_f32_16x16x32_bf16 per slab
-  __shared__ __attribute__((aligned(16))) unsigned char tile[kSlabRows * kPitch];
+void append_kernel(AppendArgs a) {
+  static_assert(kCols == 16 || kCols == 32 || kCols == 64, "column block");
+  constexpr int kR = kSlabBytes / (kCols * 2);           // slab rows: 1024, 512, 256
+  // Row pitch: the four rows one 16-lane group reads in a transposing read must
+  // start 8 LDS banks apart (pitch = 8 or 24 banks mod 32) to cover all 32 banks.
+  constexpr int kPitch = kCols == 16 ? 32 : kCols == 32 ? 96 : 160;
+  constexpr int kCPR = kCols * 2 / 16;                    // 16-byte chunks per weight row
+  constexpr int kChunks = kR * kCPR / 256;                // 8 per thread
+  constexpr int kNB = kCols / 16;                         // 16-column MFMA blocks per wave
+  constexpr int kSub = kR / 256;                          // 256-row A chunks per slab
+  constexpr int kColBlocks = kRow / kCols;
+  __shared__ __attribute__((aligned(16))) unsigned char tile[kR * kPitch];
 
-  const int q = (blockIdx.x % kXcds) * per_die + blockIdx.x / kXcds;
-  if (q >= units) return;                      // whole workgroup: no barrier is skipped by half of it
+  const int q = (blockIdx.x % kXcds) * a.per_die + blockIdx.x / kXcds;
+  if (q >= a.units) return;                    // whole workgroup: no barrier is skipped by half of it
   const int cb = q % kColBlocks;
-  const int split = (q / kColBlocks) % splits;
-  const int grp = q / (kColBlocks * splits);
+  const int split = (q / kColBlocks) % a.splits;
+  const int grp = q / (kColBlocks * a.splits);
   const int n0 = cb * kCols, m0 = grp * kTokens;
-  const int k_begin = split * slabs_per_split * kSlabRows;
-
+  const int k_begin = split * a.slabs_per_split * kR;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.T;
+
+  // q_R chunks of this thread (issued first: waiting for them leaves the W_A loads in flight).
+  const size_t q_stride = (size_t)a.units * 256;
+  QChunk qe[kQEarly];
+  bool qok[kQEarly];
+#pragma unroll
+  for (int k = 0; k < kQEarly; ++k)
+    qok[k] = a.q_r != nullptr && load_q_chunk(a, (size_t)q * 256 + tid + k * q_stride, qe[k]);
+
   // A operand (x): row m0 + 16 wave + lane % 16, columns 32 ks + 8 (lane / 16) .. +7 of
-  // the slab; rows past T read row 0 and are never stored.
+  // a 256-row chunk; rows past T read row 0 and are never stored.
   const int arow = m0 + 16 * wave + (lane & 15);
-  const uint16_t* Ap = x + (size_t)(arow < T ? arow : 0) * d + k_begin + 8 * (lane >> 4);
-  // Weight chunk i of this thread: slab row tid / 8 + 32 i, columns n0 + 8 (tid % 8) .. +7.
-  const uint16_t* Wp = w + (size_t)(k_begin + tid / kCPR) * kRow + n0 + 8 * (tid % kCPR);
+  const uint16_t* Ap = a.x + (size_t)(arow < T ? arow : 0) * a.d + k_begin + 8 * (lane >> 4);
+  // Weight chunk i of this thread: slab row tid / kCPR + (256 / kCPR) i, 16 bytes at column
+  // n0 + 8 (tid % kCPR).
+  constexpr int kRowStep = 256 / kCPR;
+  const uint16_t* Wp = a.w + (size_t)(k_begin + tid / kCPR) * kRow + n0 + 8 * (tid % kCPR);
   unsigned char* wdst = tile + (tid / kCPR) * kPitch + (tid % kCPR) * 16;
 
   u32x4 wv[kChunks];
-  s16x8 a[kKS];
-  auto load_slab = [&](int s) {
-    const size_t k0 = (size_t)s * kSlabRows;
+  auto load_w = [&](int s) {
+    const size_t k0 = (size_t)s * kR;
 #pragma unroll
     for (int i = 0; i < kChunks; ++i)
-      wv[i] = __builtin_nontemporal_load((const u32x4*)(Wp + (k0 + 32 * i) * kRow));
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) a[ks] = *(const s16x8*)(Ap + k0 + 32 * ks);
+      wv[i] = __builtin_nontemporal_load((const u32x4*)(Wp + (k0 + kRowStep * i) * kRow));
   };
+  auto load_a = [&](int c, s16x8 (&av)[8]) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) av[ks] = *(const s16x8*)(Ap + (size_t)c * 256 + 32 * ks);
+  };
+
+  const int chunks = a.slabs_per_split * kSub;
+  s16x8 anext[8];
+  load_w(0);
+  load_a(0, anext);
+
+#pragma unroll
+  for (int k = 0; k < kQEarly; ++k)
+    if (qok[k]) *(u32x4*)qe[k].dst = rotate_chunk(qe[k].v, qe[k].c, qe[k].sn);
 
   // Transposing-read source: lane s of 16-lane group g addresses slab row 8g + s/4
   // (rows +4 for the second read) and columns 4 (s % 4) .. +3 of a 16-column block.
   const int g = lane >> 4, sl = lane & 15;
   const unsigned char* tr_base = tile + (8 * g + (sl >> 2)) * kPitch + (sl & 3) * 8;
 
-  f32x4 acc[4];
+  f32x4 acc[kNB];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < kNB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_slab(0);
-  for (int s = 0; s < slabs_per_split; ++s) {
+  for (int s = 0; s < a.slabs_per_split; ++s) {
     if (s > 0) __syncthreads();                // every wave is done reading the previous slab
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) *(u32x4*)(wdst + 32 * i * kPitch) = wv[i];
-    s16x8 acur[kKS];
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) acur[ks] = a[ks];
-    if (s + 1 < slabs_per_split) load_slab(s + 1);   // next slab in flight during this one
+    for (int i = 0; i < kChunks; ++i) *(u32x4*)(wdst + kRowStep * i * kPitch) = wv[i];
+    if (s + 1 < a.slabs_per_split) load_w(s + 1);   // next slab in flight during this one
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) {
+    for (int u = 0; u < kSub; ++u) {
+      s16x8 acur[8];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const unsigned char* p = tr_base + ks * 32 * kPitch + nb * 32;
-        const s16x4 lo = lds_read_tr4(p);
-        const s16x4 hi = lds_read_tr4(p + 4 * kPitch);
-        const s16x8 b = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[nb] = mfma16(acur[ks], b, acc[nb]);
+      for (int ks = 0; ks < 8; ++ks) acur[ks] = anext[ks];
+      const int c = s * kSub + u;
+      if (c + 1 < chunks) load_a(c + 1, anext);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const unsigned char* p = tr_base + (u * 256 + ks * 32) * kPitch + nb * 32;
+          const s16x4 lo = lds_read_tr4(p);
+          const s16x4 hi = lds_read_tr4(p + 4 * kPitch);
+          const s16x8 b = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[nb] = mfma16(acur[ks], b, acc[nb]);
+        }
       }
     }
   }
 
   // D layout of a 16x16 tile: lane l, register j -> row 4 (l / 16) + j, column l % 16.
-  float* P = part + (size_t)split * T * kRow;
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int col = n0 + 16 * nb + (lane & 15);
+  if (a.splits == 1) {
+    // The sum is complete: rotate key pairs (columns 2i, 2i + 1 sit in lanes l, l ^ 1) and
+    // store each pair of bf16 from its even lane.
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = m0 + 16 * wave + 4 * (lane >> 4) + j;
-      if (row < T) P[(size_t)row * kRow + col] = acc[nb][j];
+      int p = 0;
+      const int64_t dst = row < T ? slot_of(a, row, &p) : -1;
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int col = n0 + 16 * nb + (lane & 15);
+        float v = acc[nb][j];
+        const float other = __shfl_xor(v, 1);
+        if (col >= kLatent && dst >= 0) {
+          const int pr = (col - kLatent) >> 1;
+          const float c = a.table[(size_t)p * kRope + pr], sn = a.table[(size_t)p * kRope + kRope / 2 + pr];
+          v = (lane & 1) ? other * sn + v * c : v * c - other * sn;
+        }
+        const float partner = __shfl_xor(v, 1);
+        if (dst >= 0 && !(lane & 1)) *(uint32_t*)(a.kv + dst * kRow + col) = pack_bf16x2(v, partner);
+      }
+    }
+  } else {
+    float* P = a.part + (size_t)split * T * kRow;
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int col = n0 + 16 * nb + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = m0 + 16 * wave + 4 * (lane >> 4) + j;
+        if (row < T) P[(size_t)row * kRow + col] = acc[nb][j];
+      }
+    }
+  }
+
+  // q_R chunks beyond the first kQEarly per thread (only when tokens outnumber the units' threads).
+  if (a.q_r != nullptr) {
+    for (size_t idx = (size_t)q * 256 + tid + kQEarly * q_stride; idx < (size_t)T * a.heads * (kRope / 8);
+         idx += q_stride) {
+      QChunk qc;
+      if (load_q_chunk(a, idx, qc)) *(u32x4*)qc.dst = rotate_chunk(qc.v, qc.c, qc.sn);
     }
   }
 }
 
-// One workgroup per new token: sum the split partials in split order, rotate the
-// last 64 values as 32 interleaved pairs with the position's fp32 table row,
-// round to bf16 and write the row into its page.  Thread j owns columns 4j .. 4j + 3.
-__global__ __attribute__((amdgpu_flat_work_group_size(192, 192)))
-void append_finalize_kernel(const float* __restrict__ part, int splits, int T, const float* __restrict__ table,
-                            int max_pos, const int32_t* __restrict__ bt, const int32_t* __restrict__ seqlens, int s_q,
-                            int max_blocks, int64_t num_pages, uint16_t* __restrict__ kv) {
-  const int t = blockIdx.x;
-  const int b = t / s_q, i = t - b * s_q;
-  const int p = seqlens[b] - s_q + i;
-  if (p < 0 || p >= max_pos || (p >> 6) >= max_blocks) return;
-  const int page = bt[(size_t)b * max_blocks + (p >> 6)];
-  if (page < 0 || page >= num_pages) return;
-  const int j = threadIdx.x;
-  if (j >= kRow / 4) return;
+// One wave per (new token, 64-column block): lane l sums the split partials of
+// column 64 cb + l in split order, all loads of up to kBatch splits issued before
+// the first addition; in the last block (the key) lanes 2i and 2i + 1 hold pair
+// i, exchange values and rotate it with the position's fp32 table row; then the
+// value is rounded to bf16 and each pair is stored from its even lane.
+__global__ __attribute__((amdgpu_flat_work_group_size(64, 64)))
+void append_finalize_kernel(AppendArgs a) {
+  constexpr int kBatch = 16;
+  const int t = blockIdx.x, cb = blockIdx.y, lane = threadIdx.x;
+  int p = 0;
+  const int64_t dst = slot_of(a, t, &p);
+  if (dst < 0) return;
+  const int col = 64 * cb + lane;
+  const float* src = a.part + (size_t)t * kRow + col;
+  const size_t stride = (size_t)a.T * kRow;
+  float v[kBatch];
+#pragma unroll
+  for (int sp = 0; sp < kBatch; ++sp)
+    if (sp < a.splits) v[sp] = src[sp * stride];
+  float acc = v[0];
+#pragma unroll
+  for (int sp = 1; sp < kBatch; ++sp)
+    if (sp < a.splits) acc += v[sp];
+  for (int sp = kBatch; sp < a.splits; ++sp) acc += src[sp * stride];
 
-  const float* src = part + (size_t)t * kRow + 4 * j;
-  const size_t stride = (size_t)T * kRow;
-  f32x4 acc = *(const f32x4*)src;
-#pragma unroll 4
-  for (int s = 1; s < splits; ++s) acc += *(const f32x4*)(src + s * stride);
-
-  if (j >= kLatent / 4) {
-    // columns 512 + 4r .. +3 hold pairs 2r and 2r + 1 of the key
-    const int r = j - kLatent / 4;
-    const float* row = table + (size_t)p * kRope;
-    const float c0 = row[2 * r], c1 = row[2 * r + 1];
-    const float s0 = row[kRope / 2 + 2 * r], s1 = row[kRope / 2 + 2 * r + 1];
-    const f32x4 v = acc;
-    acc[0] = v[0] * c0 - v[1] * s0;
-    acc[1] = v[0] * s0 + v[1] * c0;
-    acc[2] = v[2] * c1 - v[3] * s1;
-    acc[3] = v[2] * s1 + v[3] * c1;
+  float other = __shfl_xor(acc, 1);
+  if (col >= kLatent) {
+    const int pr = (col - kLatent) >> 1;
+    const float c = a.table[(size_t)p * kRope + pr], sn = a.table[(size_t)p * kRope + kRope / 2 + pr];
+    acc = (lane & 1) ? other * sn + acc * c : acc * c - other * sn;
+    other = __shfl_xor(acc, 1);
   }
-  u32x2 out;
-  out[0] = pack_bf16x2(acc[0], acc[1]);
-  out[1] = pack_bf16x2(acc[2], acc[3]);
-  *(u32x2*)(kv + ((size_t)page * kPage + (p & (kPage - 1))) * kRow + 4 * j) = out;
+  if (!(lane & 1)) *(uint32_t*)(a.kv + dst * kRow + col) = pack_bf16x2(acc, other);
 }
 
 // q_r [T, H, 64] rotated in place.  One workgroup per token; thread tid always owns
@@ -195,9 +324,13 @@ __global__ void rope_table_kernel(float* __restrict__ table, int max_pos, double
 
 AppendPlan plan_append(int tokens, int d_model) {
   AppendPlan pl{};
-  const int slabs = d_model / kSlabRows;
   const int groups = (tokens + kTokens - 1) / kTokens;
-  const int base_units = kColBlocks * groups;
+  // One token group (decode): 32-column blocks halve the fp32 partials of 64-column
+  // ones; more groups (prefill-sized): 64-column blocks read x fewer times.
+  const int cols = groups == 1 && d_model % 512 == 0 ? 32 : 64;
+  const int rows = kSlabBytes / (cols * 2);
+  const int slabs = d_model / rows;
+  const int base_units = (kRow / cols) * groups;
   int splits = slabs;
   for (int s = 1; s <= slabs; ++s) {
     if (slabs % s == 0 && (int64_t)base_units * s >= kTargetWgs) {
@@ -205,26 +338,49 @@ AppendPlan plan_append(int tokens, int d_model) {
       break;
     }
   }
+  pl.cols = cols;
   pl.splits = splits;
   pl.slabs_per_split = slabs / splits;
   pl.units = base_units * splits;
-  pl.part_bytes = (size_t)splits * tokens * kRow * sizeof(float);
+  pl.part_bytes = splits > 1 ? (size_t)splits * tokens * kRow * sizeof(float) : 0;
   return pl;
 }
 
 hipError_t launch_append(const uint16_t* x, const uint16_t* w_a, const float* table, const int32_t* bt,
-                         const int32_t* seqlens, uint16_t* kv, float* part, int batch, int s_q, int d_model,
-                         int max_blocks, int64_t num_pages, int max_pos, hipStream_t s) {
+                         const int32_t* seqlens, uint16_t* kv, uint16_t* q_r, int heads, unsigned char* ws,
+                         int batch, int s_q, int d_model, int max_blocks, int64_t num_pages, int max_pos,
+                         hipStream_t s) {
   const int T = batch * s_q;
   if (T <= 0) return hipSuccess;
   const AppendPlan pl = plan_append(T, d_model);
-  const int per_die = (pl.units + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL(append_gemm_kernel, dim3(per_die * kXcds), dim3(256), 0, s, x, w_a, part, T, d_model, pl.splits,
-                     pl.slabs_per_split, pl.units, per_die);
+  AppendArgs a;
+  a.x = x;
+  a.w = w_a;
+  a.table = table;
+  a.bt = bt;
+  a.seqlens = seqlens;
+  a.kv = kv;
+  a.q_r = q_r;
+  a.part = reinterpret_cast<float*>(ws);
+  a.num_pages = num_pages;
+  a.T = T;
+  a.d = d_model;
+  a.s_q = s_q;
+  a.max_blocks = max_blocks;
+  a.max_pos = max_pos;
+  a.heads = q_r != nullptr ? heads : 0;
+  a.splits = pl.splits;
+  a.slabs_per_split = pl.slabs_per_split;
+  a.units = pl.units;
+  a.per_die = (pl.units + kXcds - 1) / kXcds;
+  const dim3 grid(a.per_die * kXcds);
+  if (pl.cols == 32)
+    hipLaunchKernelGGL(append_kernel<32>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<64>, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(append_finalize_kernel, dim3(T), dim3(192), 0, s, part, pl.splits, T, table, max_pos, bt, seqlens,
-                     s_q, max_blocks, num_pages, kv);
+  if (e != hipSuccess || pl.splits == 1) return e;
+  hipLaunchKernelGGL(append_finalize_kernel, dim3(T, kRow / 64), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

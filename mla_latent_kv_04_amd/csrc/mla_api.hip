@@ -149,6 +149,7 @@ mla_status check_append(const mla_append_params* p) {
     return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_seq %d", p->max_blocks_per_seq);
   if (p->max_pos < 1 || p->max_pos > (1 << 26)) return fail(MLA_ERR_INVALID_ARG, "max_pos %d", p->max_pos);
   if (p->num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages %lld < 1", (long long)p->num_pages);
+  if (p->num_heads < 1 || p->num_heads > 4096) return fail(MLA_ERR_INVALID_ARG, "num_heads %d", p->num_heads);
   if (p->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "reserved must be 0");
   return MLA_OK;
 }
@@ -162,12 +163,12 @@ extern "C" {
 size_t mla_append_workspace_size(const mla_append_params* p) {
   if (check_append(p) != MLA_OK) return 0;
   const int T = p->batch * p->s_q;
-  if (T == 0) return 16;
-  return round_up(mla::plan_append(T, p->d_model).part_bytes);
+  const size_t part = T > 0 ? round_up(mla::plan_append(T, p->d_model).part_bytes) : 0;
+  return part > 0 ? part : 16;
 }
 
 mla_status mla_append_kv(const uint16_t* x, const uint16_t* w_a, const float* rope_table,
-                         const int32_t* block_table, const int32_t* seqlens, uint16_t* kv_blocks,
+                         const int32_t* block_table, const int32_t* seqlens, uint16_t* kv_blocks, uint16_t* q_r,
                          const mla_append_params* p, void* workspace, size_t workspace_bytes, void* stream) {
   mla_status st = check_append(p);
   if (st != MLA_OK) return st;
@@ -175,12 +176,12 @@ mla_status mla_append_kv(const uint16_t* x, const uint16_t* w_a, const float* ro
   if (!x || !w_a || !rope_table || !block_table || !seqlens || !kv_blocks || !workspace)
     return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!aligned16(x) || !aligned16(w_a) || !aligned16(rope_table) || !aligned16(kv_blocks) || !aligned16(workspace) ||
-      !aligned4(block_table) || !aligned4(seqlens))
+      !aligned4(block_table) || !aligned4(seqlens) || !aligned16(q_r))
     return fail(MLA_ERR_MISALIGNED, "tensor or workspace not aligned (16 B; block_table and seqlens 4 B)");
   const size_t need = mla_append_workspace_size(p);
   if (workspace_bytes < need) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
-  hipError_t e = mla::launch_append(x, w_a, rope_table, block_table, seqlens, kv_blocks,
-                                    static_cast<float*>(workspace), p->batch, p->s_q, p->d_model,
+  hipError_t e = mla::launch_append(x, w_a, rope_table, block_table, seqlens, kv_blocks, q_r, p->num_heads,
+                                    static_cast<unsigned char*>(workspace), p->batch, p->s_q, p->d_model,
                                     p->max_blocks_per_seq, p->num_pages, p->max_pos,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "append launch");

@@ -133,19 +133,20 @@ def test_fused_and_gather_argument_checks(lib):
 def _aparams(**kw):
     p = _lib.AppendParams()
     p.batch, p.s_q, p.d_model, p.page_size, p.max_blocks_per_seq = 4, 1, 7168, 64, 8
-    p.max_pos, p.num_pages, p.reserved = 4096, 32, 0
+    p.max_pos, p.num_pages, p.num_heads, p.reserved = 4096, 32, 128, 0
     for k, v in kw.items():
         setattr(p, k, v)
     return p
 
 
-def _append(lib, p, ptrs=None, ws=A, ws_bytes=1 << 30):
+def _append(lib, p, ptrs=None, ws=A, ws_bytes=1 << 30, q_r=None):
     x, w, tab, bt, sl, kv = ptrs or (A, A, A, A, A, A)
-    return lib.mla_append_kv(x, w, tab, bt, sl, kv, ctypes.byref(p), ws, ws_bytes, None)
+    return lib.mla_append_kv(x, w, tab, bt, sl, kv, q_r, ctypes.byref(p), ws, ws_bytes, None)
 
 
 def test_append_params_struct_layout():
     assert ctypes.sizeof(_lib.AppendParams) == 40 and _lib.AppendParams.num_pages.offset == 24
+    assert _lib.AppendParams.num_heads.offset == 32
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -154,6 +155,7 @@ def test_append_params_struct_layout():
     ("batch", -1, _lib.MLA_ERR_INVALID_ARG), ("s_q", 0, _lib.MLA_ERR_INVALID_ARG),
     ("max_blocks_per_seq", 0, _lib.MLA_ERR_INVALID_ARG), ("max_pos", 0, _lib.MLA_ERR_INVALID_ARG),
     ("num_pages", 0, _lib.MLA_ERR_INVALID_ARG), ("reserved", 3, _lib.MLA_ERR_INVALID_ARG),
+    ("num_heads", 0, _lib.MLA_ERR_INVALID_ARG), ("num_heads", 5000, _lib.MLA_ERR_INVALID_ARG),
 ])
 def test_append_bad_params_rejected(lib, field, value, status):
     p = _aparams(**{field: value})
@@ -162,13 +164,21 @@ def test_append_bad_params_rejected(lib, field, value, status):
 
 
 def test_append_workspace_size(lib):
-    # decode-sized: 9 column blocks x 28 splits of the 7168 hidden rows, fp32 partials [28, T, 576]
-    assert lib.mla_append_workspace_size(ctypes.byref(_aparams(batch=64))) == 28 * 64 * 576 * 4
-    assert lib.mla_append_workspace_size(ctypes.byref(_aparams(batch=4, s_q=2))) == 28 * 8 * 576 * 4
-    # prefill-sized: 64 token groups x 9 column blocks already fill the chip, one split
-    assert lib.mla_append_workspace_size(ctypes.byref(_aparams(batch=1, s_q=4096))) == 4096 * 576 * 4
+    def size(**kw):
+        return lib.mla_append_workspace_size(ctypes.byref(_aparams(**kw)))
+    C = 0                                             # fp32 partials only
+    # decode-sized: 18 column blocks of 32 x 14 splits of the 7168 hidden rows, partials [14, T, 576]
+    assert size(batch=64) == C + 14 * 64 * 576 * 4
+    assert size(batch=4, s_q=2) == C + 14 * 8 * 576 * 4
+    # d = 16384: 32 slabs of 512 rows, 16 splits already give 18 x 16 >= 256 workgroups
+    assert size(d_model=16384) == C + 16 * 4 * 576 * 4
+    # d = 768 is not a multiple of 512: 64-column blocks, 3 slabs of 256 rows, 3 splits
+    assert size(d_model=768) == C + 3 * 4 * 576 * 4
     # 1024 tokens: 16 groups x 9 = 144 workgroups, two splits (a divisor of 28) reach 256
-    assert lib.mla_append_workspace_size(ctypes.byref(_aparams(batch=1, s_q=1024))) == 2 * 1024 * 576 * 4
+    assert size(batch=1, s_q=1024) == C + 2 * 1024 * 576 * 4
+    # prefill-sized: 64 token groups x 9 column blocks fill the chip, one split and no partials
+    assert size(batch=1, s_q=4096) == 16
+    assert size(batch=0) == 16
     assert lib.mla_append_workspace_size(None) == 0
 
 
@@ -177,7 +187,7 @@ def test_append_argument_checks(lib):
     need = lib.mla_append_workspace_size(ctypes.byref(p))
     assert _append(lib, p, ws_bytes=need - 1) == _lib.MLA_ERR_WORKSPACE
     assert _append(lib, p, ws=None, ws_bytes=need) == _lib.MLA_ERR_INVALID_ARG
-    assert lib.mla_append_kv(A, A, A, A, A, A, None, A, need, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_append_kv(A, A, A, A, A, A, None, None, A, need, None) == _lib.MLA_ERR_INVALID_ARG
     for which in range(6):
         ptrs = [A] * 6
         ptrs[which] = None
@@ -185,6 +195,7 @@ def test_append_argument_checks(lib):
         ptrs[which] = MIS if which not in (3, 4) else ctypes.c_void_p(0x10002)
         assert _append(lib, p, tuple(ptrs)) == _lib.MLA_ERR_MISALIGNED
     assert _append(lib, p, ws=MIS) == _lib.MLA_ERR_MISALIGNED
+    assert _append(lib, p, q_r=MIS) == _lib.MLA_ERR_MISALIGNED
     assert _append(lib, _aparams(batch=0), (None,) * 6, ws=None, ws_bytes=0) == _lib.MLA_OK
 
 

@@ -116,6 +116,9 @@ CASES = [
     ("1024-tokens-d1024", 73, 1, 1024, [5000], 1024),
     ("4096-tokens-d512", 74, 2, 2048, [2048, 2500], 512),
     ("one-slab-d256", 75, 7, 1, [9, 1, 64, 127, 128, 129, 700], 256),
+    ("two-slabs-per-split-d16384", 84, 3, 1, [5, 64, 1000], 16384),
+    ("seven-splits-d3584", 85, 64, 1, None, 3584),
+    ("d768-64-columns", 86, 4, 2, [2, 3, 64, 65], 768),
 ]
 
 
@@ -251,3 +254,53 @@ def test_append_then_decode_sees_the_new_rows(tables):
     ref_ol, ref_lse = oracle.decode_absorbed(q_abs, ref_qr, ref_pool, inp.block_table, inp.seqlens, 2, inp.scale)
     assert_close(oracle.bf16_bits_to_f64(host_bits(ol)), ref_ol, "out_latent after append")
     assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= 2e-3 + 2 ** -8 * np.max(np.abs(ref_lse))
+
+
+@pytest.mark.parametrize("batch,s_q,seqlens,d", [(64, 1, None, 7168), (2, 2048, [2048, 2100], 512),
+                                                 (3, 2, [2, 64, 4097], 2048)])
+def test_append_rotates_the_query_in_the_same_launch(tables, batch, s_q, seqlens, d):
+    if seqlens is None:
+        seqlens = np.random.default_rng(87).integers(1, 5000, batch)
+    inp = make_custom(88, batch, s_q, seqlens)
+    x, w_a = make_append_inputs(89, batch, s_q, d_model=d)
+    pool = dev_bf16(inp.pool)
+    q_r = dev_bf16(inp.q_r)
+    mla.append_kv(dev_bf16(x), dev_bf16(w_a), tables[0], pool, dev_i32(inp.block_table), dev_i32(inp.seqlens),
+                  q_r=q_r)
+    torch.cuda.synchronize()
+    pos = oracle.append_positions(inp.seqlens, s_q)
+    ref = oracle.rope_q(inp.q_r, tables[1], pos)
+    qf = oracle.bf16_bits_to_f64(inp.q_r)
+    t = tables[1].astype(np.float64)[pos][:, :, None, :]
+    assert_bf16_match(host_bits(q_r), ref, rotation_err(qf[..., 0::2], qf[..., 1::2], t[..., :32], t[..., 32:]),
+                      "q_R rotated by the append launch")
+    rows, ref_pool = oracle.append_kv(x, w_a, tables[1], inp.block_table, inp.seqlens, inp.pool, s_q)
+    got_pool = host_bits(pool)
+    same = np.all(ref_pool == inp.pool, axis=-1)
+    assert np.array_equal(got_pool[same], inp.pool[same])
+    E = projection_err(x, w_a, tables[1], pos)
+    got_rows = np.stack([np.stack([got_pool[oracle.slot_of(inp.block_table, b, int(pos[b, i]), inp.num_pages)]
+                                   for i in range(s_q)]) for b in range(batch)])
+    assert_bf16_match(got_rows, rows, E, "rows")
+
+
+def test_one_workspace_across_plans(tables):
+    """Calls with different split plans share one workspace that starts as NaN garbage;
+    each result is right."""
+    cases = [(64, 1, 7168), (3, 1, 16384), (5, 2, 768), (1, 1024, 1024), (2, 2048, 512), (64, 1, 7168)]
+    need = max(mla.append_workspace_size(mla.make_append_params(b, s, d, 80, 4096, MAX_POS)) for b, s, d in cases)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    for n, (b, s_q, d) in enumerate(cases):
+        seqlens = np.random.default_rng(100 + n).integers(s_q, 64 * 40, b)
+        inp = make_custom(100 + n, b, s_q, seqlens)
+        x, w_a = make_append_inputs(200 + n, b, s_q, d_model=d)
+        pool = dev_bf16(inp.pool)
+        mla.append_kv(dev_bf16(x), dev_bf16(w_a), tables[0], pool, dev_i32(inp.block_table), dev_i32(inp.seqlens),
+                      workspace=ws)
+        torch.cuda.synchronize()
+        rows, _ = oracle.append_kv(x, w_a, tables[1], inp.block_table, inp.seqlens, inp.pool, s_q)
+        pos = oracle.append_positions(inp.seqlens, s_q)
+        got_pool = host_bits(pool)
+        got_rows = np.stack([np.stack([got_pool[oracle.slot_of(inp.block_table, bb, int(pos[bb, i]), inp.num_pages)]
+                                       for i in range(s_q)]) for bb in range(b)])
+        assert_bf16_match(got_rows, rows, projection_err(x, w_a, tables[1], pos), f"case {n}")
