@@ -94,9 +94,10 @@ __device__ __forceinline__ bool load_q_chunk(const AppendArgs& a, size_t idx, QC
 
 // One (token group, K split, column block) unit per workgroup:
 //   partial[t][n0 .. n0 + kCols - 1] = sum over the split's hidden rows k of x[t][k] W_A[k][n].
-// The workgroup stages a 32 KiB slab of W_A (kR rows of kCols columns) in LDS and
-// feeds the MFMA B operand with transposing LDS reads; each wave owns 16 tokens
-// and streams their x values (the A operand) 256 hidden rows at a time.
+// The workgroup stages a 32 KiB slab of W_A (kR rows of kCols columns) and the
+// matching x slab (64 tokens x kR hidden values, loaded a whole 1 KiB row segment
+// per instruction) in LDS; the MFMA B operand comes from transposing LDS reads,
+// the A operand from plain 16-byte LDS reads, each wave owning 16 tokens.
 // Narrow column blocks mean fewer K splits for the same slab size, hence fewer
 // fp32 partials, at the price of re-reading x (from L2) once per column block.
 // Units are numbered token group, then split, then column block, and handed out
@@ -106,17 +107,22 @@ __device__ __forceinline__ bool load_q_chunk(const AppendArgs& a, size_t idx, QC
 template <int kCols>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void append_kernel(AppendArgs a) {
-  static_assert(kCols == 16 || kCols == 32 || kCols == 64, "column block");
-  constexpr int kR = kSlabBytes / (kCols * 2);           // slab rows: 1024, 512, 256
+  static_assert(kCols == 32 || kCols == 64, "column block");
+  constexpr int kR = kSlabBytes / (kCols * 2);           // slab rows: 512, 256
   // Row pitch: the four rows one 16-lane group reads in a transposing read must
   // start 8 LDS banks apart (pitch = 8 or 24 banks mod 32) to cover all 32 banks.
-  constexpr int kPitch = kCols == 16 ? 32 : kCols == 32 ? 96 : 160;
+  constexpr int kPitch = kCols == 32 ? 96 : 160;
+  // x slab rows (one token each) padded by 16 bytes: the 8 rows one group of 8 lanes
+  // reads with a 16-byte read then start 4 banks apart.
+  constexpr int kXPitch = kR * 2 + 16;
+  constexpr int kXCPR = kR * 2 / 16;                      // 16-byte chunks per x slab row
+  constexpr int kXChunks = kTokens * kXCPR / 256;         // per thread: 16, 8
   constexpr int kCPR = kCols * 2 / 16;                    // 16-byte chunks per weight row
   constexpr int kChunks = kR * kCPR / 256;                // 8 per thread
   constexpr int kNB = kCols / 16;                         // 16-column MFMA blocks per wave
-  constexpr int kSub = kR / 256;                          // 256-row A chunks per slab
   constexpr int kColBlocks = kRow / kCols;
   __shared__ __attribute__((aligned(16))) unsigned char tile[kR * kPitch];
+  __shared__ __attribute__((aligned(16))) unsigned char xs[kTokens * kXPitch];
 
   const int q = (blockIdx.x % kXcds) * a.per_die + blockIdx.x / kXcds;
   if (q >= a.units) return;                    // whole workgroup: no barrier is skipped by half of it
@@ -136,32 +142,32 @@ void append_kernel(AppendArgs a) {
   for (int k = 0; k < kQEarly; ++k)
     qok[k] = a.q_r != nullptr && load_q_chunk(a, (size_t)q * 256 + tid + k * q_stride, qe[k]);
 
-  // A operand (x): row m0 + 16 wave + lane % 16, columns 32 ks + 8 (lane / 16) .. +7 of
-  // a 256-row chunk; rows past T read row 0 and are never stored.
-  const int arow = m0 + 16 * wave + (lane & 15);
-  const uint16_t* Ap = a.x + (size_t)(arow < T ? arow : 0) * a.d + k_begin + 8 * (lane >> 4);
+  // x chunk i of this thread: slab row (token) tid / kXCPR + (256 / kXCPR) i, 16 bytes at
+  // hidden offset 8 (tid % kXCPR); tokens past T read token 0 and are never stored.
+  constexpr int kXRowStep = 256 / kXCPR;
+  const uint16_t* Xp[kXChunks];
+#pragma unroll
+  for (int i = 0; i < kXChunks; ++i) {
+    const int row = m0 + tid / kXCPR + kXRowStep * i;
+    Xp[i] = a.x + (size_t)(row < T ? row : 0) * a.d + k_begin + 8 * (tid % kXCPR);
+  }
+  unsigned char* xdst = xs + (tid / kXCPR) * kXPitch + (tid % kXCPR) * 16;
   // Weight chunk i of this thread: slab row tid / kCPR + (256 / kCPR) i, 16 bytes at column
   // n0 + 8 (tid % kCPR).
   constexpr int kRowStep = 256 / kCPR;
   const uint16_t* Wp = a.w + (size_t)(k_begin + tid / kCPR) * kRow + n0 + 8 * (tid % kCPR);
   unsigned char* wdst = tile + (tid / kCPR) * kPitch + (tid % kCPR) * 16;
 
-  u32x4 wv[kChunks];
-  auto load_w = [&](int s) {
+  u32x4 wv[kChunks], xv[kXChunks];
+  auto load_slab = [&](int s) {
     const size_t k0 = (size_t)s * kR;
 #pragma unroll
     for (int i = 0; i < kChunks; ++i)
       wv[i] = __builtin_nontemporal_load((const u32x4*)(Wp + (k0 + kRowStep * i) * kRow));
-  };
-  auto load_a = [&](int c, s16x8 (&av)[8]) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) av[ks] = *(const s16x8*)(Ap + (size_t)c * 256 + 32 * ks);
+    for (int i = 0; i < kXChunks; ++i) xv[i] = *(const u32x4*)(Xp[i] + k0);
   };
-
-  const int chunks = a.slabs_per_split * kSub;
-  s16x8 anext[8];
-  load_w(0);
-  load_a(0, anext);
+  load_slab(0);
 
 #pragma unroll
   for (int k = 0; k < kQEarly; ++k)
@@ -171,6 +177,8 @@ void append_kernel(AppendArgs a) {
   // (rows +4 for the second read) and columns 4 (s % 4) .. +3 of a 16-column block.
   const int g = lane >> 4, sl = lane & 15;
   const unsigned char* tr_base = tile + (8 * g + (sl >> 2)) * kPitch + (sl & 3) * 8;
+  // A operand: token 16 wave + lane % 16, hidden offsets 32 ks + 8 (lane / 16) .. +7.
+  const unsigned char* a_base = xs + (16 * wave + (lane & 15)) * kXPitch + 16 * (lane >> 4);
 
   f32x4 acc[kNB];
 #pragma unroll
@@ -180,25 +188,20 @@ void append_kernel(AppendArgs a) {
     if (s > 0) __syncthreads();                // every wave is done reading the previous slab
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) *(u32x4*)(wdst + kRowStep * i * kPitch) = wv[i];
-    if (s + 1 < a.slabs_per_split) load_w(s + 1);   // next slab in flight during this one
+#pragma unroll
+    for (int i = 0; i < kXChunks; ++i) *(u32x4*)(xdst + kXRowStep * i * kXPitch) = xv[i];
+    if (s + 1 < a.slabs_per_split) load_slab(s + 1);   // next slab in flight during this one
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-      s16x8 acur[8];
+    for (int ks = 0; ks < kR / 32; ++ks) {
+      const s16x8 av = *(const s16x8*)(a_base + ks * 64);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) acur[ks] = anext[ks];
-      const int c = s * kSub + u;
-      if (c + 1 < chunks) load_a(c + 1, anext);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-          const unsigned char* p = tr_base + (u * 256 + ks * 32) * kPitch + nb * 32;
-          const s16x4 lo = lds_read_tr4(p);
-          const s16x4 hi = lds_read_tr4(p + 4 * kPitch);
-          const s16x8 b = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[nb] = mfma16(acur[ks], b, acc[nb]);
-        }
+      for (int nb = 0; nb < kNB; ++nb) {
+        const unsigned char* p = tr_base + ks * 32 * kPitch + nb * 32;
+        const s16x4 lo = lds_read_tr4(p);
+        const s16x4 hi = lds_read_tr4(p + 4 * kPitch);
+        const s16x8 b = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[nb] = mfma16(av, b, acc[nb]);
       }
     }
   }
