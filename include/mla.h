@@ -225,6 +225,13 @@ mla_status mla_rope_table(float* rope_table, int32_t max_pos, double base, void*
 mla_status mla_profile_enable(int32_t enable);
 mla_status mla_profile_collect(double* ms, int32_t* calls);
 
+/* The same hook for mla_append_kv calls (recorded while mla_profile_enable(1) is
+ * in force, up to 65536 calls): writes the summed milliseconds of [projection
+ * kernel, partial-sum kernel] to ms[0..1] (host array of 2; the second is 0 for
+ * calls whose projection is not split) and the number of calls to *calls, and
+ * clears that record. */
+mla_status mla_profile_collect_append(double* ms, int32_t* calls);
+
 /* Number of compute units of the current device (a HIP call). */
 mla_status mla_device_cu_count(int32_t* num_cus);
 

@@ -183,9 +183,11 @@ def decode(q_c, q_r, w_uk, w_uv, kv_blocks, block_table, seqlens, *, scale=DEFAU
 
 
 class KernelTimer:
-    """Per-kernel HIP-event timing of decode calls (library hook; see mla_profile_enable).
+    """Per-kernel HIP-event timing of decode and cache-append calls (library hook; see
+    mla_profile_enable).
 
-    with KernelTimer() as kt: ...calls...;  kt.ms -> dict of summed milliseconds, kt.calls."""
+    with KernelTimer() as kt: ...calls...;  kt.ms -> dict of summed milliseconds of decode
+    calls, kt.calls; kt.append_ms, kt.append_calls likewise for append calls."""
 
     NAMES = ("absorb", "plan", "decode", "combine", "up_proj")
 
@@ -194,15 +196,23 @@ class KernelTimer:
         _lib.check(lib.mla_profile_enable(1), "mla_profile_enable")
         return self
 
+    APPEND_NAMES = ("append_proj", "append_sum")
+
     def __exit__(self, *exc):
         lib = _lib.load()
         ms = (ctypes.c_double * 5)()
         calls = ctypes.c_int32(0)
         st = lib.mla_profile_collect(ms, ctypes.byref(calls))
+        ams = (ctypes.c_double * 2)()
+        acalls = ctypes.c_int32(0)
+        st2 = lib.mla_profile_collect_append(ams, ctypes.byref(acalls))
         lib.mla_profile_enable(0)
         _lib.check(st, "mla_profile_collect")
+        _lib.check(st2, "mla_profile_collect_append")
         self.ms = dict(zip(self.NAMES, list(ms)))
         self.calls = int(calls.value)
+        self.append_ms = dict(zip(self.APPEND_NAMES, list(ams)))
+        self.append_calls = int(acalls.value)
         return False
 
 

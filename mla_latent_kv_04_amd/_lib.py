@@ -33,6 +33,7 @@ EXPORTS = (
     "mla_rope_table",
     "mla_profile_enable",
     "mla_profile_collect",
+    "mla_profile_collect_append",
     "mla_device_cu_count",
     "mla_status_string",
     "mla_last_error",
@@ -107,6 +108,7 @@ def load() -> ctypes.CDLL:
         "mla_device_cu_count": ([ctypes.POINTER(i32)], ctypes.c_int),
         "mla_profile_enable": ([i32], ctypes.c_int),
         "mla_profile_collect": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)], ctypes.c_int),
+        "mla_profile_collect_append": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)], ctypes.c_int),
         "mla_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "mla_last_error": ([], ctypes.c_char_p),
     }

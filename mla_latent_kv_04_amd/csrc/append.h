@@ -20,7 +20,7 @@ AppendPlan plan_append(int tokens, int d_model);
 hipError_t launch_append(const uint16_t* x, const uint16_t* w_a, const float* table, const int32_t* bt,
                          const int32_t* seqlens, uint16_t* kv, uint16_t* q_r, int heads, unsigned char* ws,
                          int batch, int s_q, int d_model, int max_blocks, int64_t num_pages, int max_pos,
-                         hipStream_t s);
+                         hipStream_t s, hipEvent_t ev_proj_done = nullptr);
 hipError_t launch_rope_q(uint16_t* q_r, const float* table, const int32_t* seqlens, int batch, int s_q, int heads,
                          int max_pos, hipStream_t s);
 hipError_t launch_rope_table(float* table, int max_pos, double base, hipStream_t s);

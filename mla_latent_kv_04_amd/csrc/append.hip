@@ -352,9 +352,9 @@ AppendPlan plan_append(int tokens, int d_model) {
 hipError_t launch_append(const uint16_t* x, const uint16_t* w_a, const float* table, const int32_t* bt,
                          const int32_t* seqlens, uint16_t* kv, uint16_t* q_r, int heads, unsigned char* ws,
                          int batch, int s_q, int d_model, int max_blocks, int64_t num_pages, int max_pos,
-                         hipStream_t s) {
+                         hipStream_t s, hipEvent_t ev_proj_done) {
   const int T = batch * s_q;
-  if (T <= 0) return hipSuccess;
+  if (T <= 0) return ev_proj_done != nullptr ? hipEventRecord(ev_proj_done, s) : hipSuccess;
   const AppendPlan pl = plan_append(T, d_model);
   AppendArgs a;
   a.x = x;
@@ -382,6 +382,7 @@ hipError_t launch_append(const uint16_t* x, const uint16_t* w_a, const float* ta
   else
     hipLaunchKernelGGL(append_kernel<64>, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev_proj_done != nullptr) e = hipEventRecord(ev_proj_done, s);
   if (e != hipSuccess || pl.splits == 1) return e;
   hipLaunchKernelGGL(append_finalize_kernel, dim3(T, kRow / 64), dim3(64), 0, s, a);
   return hipGetLastError();

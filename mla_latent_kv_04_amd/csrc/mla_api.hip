@@ -106,6 +106,9 @@ struct Profiler {
   bool enabled = false;
   std::vector<std::array<hipEvent_t, 6>> ev;
   size_t used = 0;
+  // cache-append calls: 0 start, 1 projection done, 2 partial sums done
+  std::vector<std::array<hipEvent_t, 3>> aev;
+  size_t aused = 0;
 };
 Profiler g_prof;
 constexpr size_t kMaxProfiledCalls = 1 << 16;
@@ -120,6 +123,18 @@ hipEvent_t* prof_slot() {
     g_prof.ev.push_back(e);
   }
   return g_prof.ev[g_prof.used++].data();
+}
+
+hipEvent_t* prof_append_slot() {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.enabled || g_prof.aused >= kMaxProfiledCalls) return nullptr;
+  if (g_prof.aused == g_prof.aev.size()) {
+    std::array<hipEvent_t, 3> e{};
+    for (auto& x : e)
+      if (hipEventCreate(&x) != hipSuccess) return nullptr;
+    g_prof.aev.push_back(e);
+  }
+  return g_prof.aev[g_prof.aused++].data();
 }
 
 mla_status run_paged(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv, const int32_t* bt,
@@ -180,11 +195,15 @@ mla_status mla_append_kv(const uint16_t* x, const uint16_t* w_a, const float* ro
     return fail(MLA_ERR_MISALIGNED, "tensor or workspace not aligned (16 B; block_table and seqlens 4 B)");
   const size_t need = mla_append_workspace_size(p);
   if (workspace_bytes < need) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
-  hipError_t e = mla::launch_append(x, w_a, rope_table, block_table, seqlens, kv_blocks, q_r, p->num_heads,
-                                    static_cast<unsigned char*>(workspace), p->batch, p->s_q, p->d_model,
-                                    p->max_blocks_per_seq, p->num_pages, p->max_pos,
-                                    static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = prof_append_slot();
+  hipError_t e;
+  if (ev != nullptr && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = mla::launch_append(x, w_a, rope_table, block_table, seqlens, kv_blocks, q_r, p->num_heads,
+                         static_cast<unsigned char*>(workspace), p->batch, p->s_q, p->d_model,
+                         p->max_blocks_per_seq, p->num_pages, p->max_pos, s, ev ? ev[1] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "append launch");
+  if (ev != nullptr && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return ok();
 }
 
@@ -346,6 +365,7 @@ mla_status mla_profile_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   g_prof.enabled = enable != 0;
   g_prof.used = 0;
+  g_prof.aused = 0;
   return ok();
 }
 
@@ -366,6 +386,26 @@ mla_status mla_profile_collect(double* ms, int32_t* calls) {
   }
   *calls = (int32_t)g_prof.used;
   g_prof.used = 0;
+  return ok();
+}
+
+mla_status mla_profile_collect_append(double* ms, int32_t* calls) {
+  if (ms == nullptr || calls == nullptr) return fail(MLA_ERR_INVALID_ARG, "NULL output pointer");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  ms[0] = ms[1] = 0.0;
+  for (size_t i = 0; i < g_prof.aused; ++i) {
+    auto& e = g_prof.aev[i];
+    hipError_t r = hipEventSynchronize(e[2]);
+    if (r != hipSuccess) return hip_fail(r, "hipEventSynchronize");
+    for (int k = 0; k < 2; ++k) {
+      float t = 0.f;
+      r = hipEventElapsedTime(&t, e[k], e[k + 1]);
+      if (r != hipSuccess) return hip_fail(r, "hipEventElapsedTime");
+      ms[k] += t;
+    }
+  }
+  *calls = (int32_t)g_prof.aused;
+  g_prof.aused = 0;
   return ok();
 }
 
