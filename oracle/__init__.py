@@ -30,6 +30,7 @@ from .capacity import (  # noqa: F401
     physical_cache_bytes,
     stage_ring_bytes,
 )
+from .prefill import decompress_kv  # noqa: F401
 from .mla_oracle import (  # noqa: F401
     absorb_q,
     attention_probs,

@@ -79,7 +79,7 @@ def _absorbed(case):
 TINY = dict(H=2, d_hc=4, d_c=8, d_r=2, page=4)
 
 
-@pytest.mark.parametrize("s_q,seqlens", [(1, [1, 5, 7]), (2, [2, 4, 7]), (1, [4, 8, 3])])
+@pytest.mark.parametrize("s_q,seqlens", [(1, [1, 5, 7]), (2, [2, 4, 7]), (1, [4, 8, 3]), (5, [5, 9, 12])])
 def test_decompressed_matches_brute_force(s_q, seqlens):
     case = _rand_case(3, 3, s_q, seqlens, **TINY)
     out, lse = _decomp(case)
@@ -88,7 +88,7 @@ def test_decompressed_matches_brute_force(s_q, seqlens):
     assert np.max(np.abs(lse - blse)) <= 1e-12 * np.max(np.abs(blse))
 
 
-@pytest.mark.parametrize("s_q,seqlens", [(1, [1, 5, 7]), (2, [2, 6, 7])])
+@pytest.mark.parametrize("s_q,seqlens", [(1, [1, 5, 7]), (2, [2, 6, 7]), (6, [6, 9, 20])])
 def test_absorbed_equals_decompressed_tiny(s_q, seqlens):
     case = _rand_case(4, 3, s_q, seqlens, **TINY)
     out, lse = _decomp(case)
@@ -177,6 +177,40 @@ def test_two_token_verify_equals_two_decode_steps():
         assert np.array_equal(o1[:, 0], out2[:, i]) and np.array_equal(l1[:, 0], lse2[:, i])
         a1, al1 = _absorbed(c1)
         assert np.array_equal(a1[:, 0], ol2[:, i]) and np.array_equal(al1[:, 0], llse2[:, i])
+
+
+@pytest.mark.parametrize("s_q", [3, 8])
+def test_prefill_chunk_equals_sequential_decode_steps(s_q):
+    """A chunk of s_q new tokens (prefill) equals s_q one-token decode steps: query i sees
+    the first L - s_q + i + 1 tokens."""
+    H, d_hc, d_c, d_r, page = 4, 16, 32, 8, 8
+    case = _rand_case(18, 2, s_q, [s_q + 9, s_q], H, d_hc, d_c, d_r, page)
+    out, lse = _decomp(case)
+    for i in range(s_q):
+        c1 = dict(case)
+        c1.update(s_q=1, q_c=case["q_c"][:, i:i + 1], q_r=case["q_r"][:, i:i + 1],
+                  seqlens=case["seqlens"] - s_q + 1 + i)
+        o1, l1 = _decomp(c1)
+        # equal up to fp64 rounding (the expanded K and V are products over different row counts)
+        assert np.max(np.abs(o1[:, 0] - out[:, i])) <= 1e-12 * np.max(np.abs(out))
+        assert np.max(np.abs(l1[:, 0] - lse[:, i])) <= 1e-12 * np.max(np.abs(lse))
+
+
+def test_whole_prompt_is_causal_sdpa():
+    """With every cached token new (s_q = L), the decompress path is textbook causal
+    attention: torch SDPA (fp64, CPU, is_causal) on q = [q_c | q_R], k = [c W_UK^T | k_R],
+    v = c W_UV, per head."""
+    H, d_hc, d_c, d_r, page, L = 3, 8, 16, 4, 4, 11
+    case = _rand_case(19, 1, L, [L], H, d_hc, d_c, d_r, page, permute=True)
+    out, lse = _decomp(case)
+    rows = oracle.gather_rows(case["pool"], case["block_table"], 0, L)
+    c, r = torch.from_numpy(rows[:, :d_c]), torch.from_numpy(rows[:, d_c:])
+    for h in range(H):
+        k = torch.cat([c @ torch.from_numpy(case["w_uk"][h]).T, r], dim=1)
+        v = c @ torch.from_numpy(case["w_uv"][h])
+        q = torch.cat([torch.from_numpy(case["q_c"][0, :, h]), torch.from_numpy(case["q_r"][0, :, h])], dim=1)
+        ref = F.scaled_dot_product_attention(q[None], k[None], v[None], is_causal=True, scale=case["scale"])[0]
+        assert np.max(np.abs(out[0, :, h] - ref.numpy())) <= 1e-12 * float(ref.abs().max())
 
 
 def test_softmax_rows_sum_to_one():

@@ -13,6 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # (oracle module, pin file) -> {name: (anchor, replacement)}
 ATTENTION = ("mla_oracle.py", "test_oracle_attention.py")
 APPEND = ("cache_append.py", "test_oracle_append.py")
+PREFILL = ("prefill.py", "test_oracle_prefill.py")
 
 MUTATIONS = {
     "dropped RoPE term": ("s = (K[:n] @ q_c[b, i, h] + r[:n] @ q_r[b, i, h]) * scale",
@@ -47,6 +48,14 @@ MUTATIONS.update({name: (APPEND, old, new) for name, (old, new) in {
     "invalid page written": ("if pg < 0 or pg >= num_pages:", "if pg >= num_pages:"),
     "query turned the other way": ("out = rope_rotate(q, rows_t)",
                                    "out = rope_rotate(q, np.concatenate([rows_t[..., :32], -rows_t[..., 32:]], -1))"),
+}.items()})
+MUTATIONS.update({name: (PREFILL, old, new) for name, (old, new) in {
+    "decompress V heads reversed": ('V[b, :, :n] = np.einsum("tc,hce->hte", c, w_uv)',
+                                    'V[b, :, :n] = np.einsum("tc,hce->hte", c, w_uv[::-1])'),
+    "decompress latent columns shifted": ("c = _as_f64(gather_rows(pool, block_table, b, n))[:, :d_c]",
+                                          "c = _as_f64(gather_rows(pool, block_table, b, n))[:, 1:d_c + 1]"),
+    "decompress key transposed": ('K[b, :, :n] = np.einsum("tc,hdc->htd", c, w_uk)',
+                                  'K[b, :, :n] = np.einsum("tc,hdc->htd", c[::-1], w_uk)'),
 }.items()})
 
 
