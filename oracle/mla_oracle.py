@@ -29,7 +29,8 @@ Readings where the pages are silent (each listed with its reason in the
 design notes): W_UV is laid out [H, d_c, d_hc]; q_R and k_R arrive already
 rotated; softmax is the standard max-subtracted one; with s_q > 1 query i of
 a sequence of length L (which already includes the s_q new tokens) sees
-tokens t <= L - s_q + i; ``lse`` is the natural log of the softmax
+tokens t <= L - s_q + i, and a query that sees no token (L < s_q) gets a zero
+output and lse = -inf; ``lse`` is the natural log of the softmax
 denominator of the scaled scores.  Nothing here rounds: all arithmetic is
 fp64 on the exact values of the bf16 inputs.
 """
@@ -117,7 +118,7 @@ def _visible(L: int, s_q: int, i: int) -> int:
 
 
 def decode_decompressed(q_c, q_r, w_uk, w_uv, pool, block_table, seqlens, s_q: int, scale: float,
-                        batches=None, heads=None):
+                        batches=None, heads=None, queries=None):
     """Plain multi-head attention after expanding K and V from the cached latent.
 
     Shapes (H heads, d_hc content dim, d_c latent, d_R rope, P page):
@@ -125,8 +126,8 @@ def decode_decompressed(q_c, q_r, w_uk, w_uv, pool, block_table, seqlens, s_q: i
     w_uv [H, d_c, d_hc], pool [pages, P, d_c + d_R], block_table [B, max_blocks],
     seqlens [B].  Arrays may be bf16 bits (uint16) or floats.
 
-    Returns ``out [nb, s_q, nh, d_hc]`` and ``lse [nb, s_q, nh]`` for the selected
-    sequences and heads (all by default).
+    Returns ``out [nb, nq, nh, d_hc]`` and ``lse [nb, nq, nh]`` for the selected
+    sequences, query indices (of the s_q new tokens) and heads (all by default).
     """
     q_c = _as_f64(q_c)
     q_r = _as_f64(q_r)
@@ -135,8 +136,9 @@ def decode_decompressed(q_c, q_r, w_uk, w_uv, pool, block_table, seqlens, s_q: i
     d_c = w_uk.shape[2]
     batches = list(range(q_c.shape[0])) if batches is None else list(batches)
     heads = list(range(q_c.shape[2])) if heads is None else list(heads)
-    out = np.zeros((len(batches), s_q, len(heads), w_uv.shape[2]))
-    lse = np.zeros((len(batches), s_q, len(heads)))
+    queries = list(range(s_q)) if queries is None else list(queries)
+    out = np.zeros((len(batches), len(queries), len(heads), w_uv.shape[2]))
+    lse = np.zeros((len(batches), len(queries), len(heads)))
     for bi, b in enumerate(batches):
         L = int(seqlens[b])
         rows = _as_f64(gather_rows(pool, block_table, b, L))
@@ -144,12 +146,16 @@ def decode_decompressed(q_c, q_r, w_uk, w_uv, pool, block_table, seqlens, s_q: i
         for hi, h in enumerate(heads):
             K = c @ w_uk[h].T          # K[t, d] = sum_c' c[t, c'] W_UK[h, d, c']
             V = c @ w_uv[h]            # V[t, e] = sum_c' c[t, c'] W_UV[h, c', e]
-            for i in range(s_q):
+            for qi, i in enumerate(queries):
                 n = _visible(L, s_q, i)
+                if n <= 0:                 # no visible token: zero output, lse = -inf
+                    out[bi, qi, hi] = 0.0
+                    lse[bi, qi, hi] = -np.inf
+                    continue
                 s = (K[:n] @ q_c[b, i, h] + r[:n] @ q_r[b, i, h]) * scale
                 p, lz = _softmax_lse(s)
-                out[bi, i, hi] = p @ V[:n]
-                lse[bi, i, hi] = lz
+                out[bi, qi, hi] = p @ V[:n]
+                lse[bi, qi, hi] = lz
     return out, lse
 
 
@@ -195,6 +201,9 @@ def decode_absorbed(q_abs, q_r, pool, block_table, seqlens, s_q: int, scale: flo
         rows = _as_f64(gather_rows(pool, block_table, b, L))
         for i in range(s_q):
             n = _visible(L, s_q, i)
+            if n <= 0:                     # no visible token: zero output, lse = -inf
+                lse[bi, i] = -np.inf
+                continue
             p, lz = attention_probs(q_abs[b, i], q_r[b, i], rows[:n], scale)
             out[bi, i] = p @ rows[:n, :d_c]
             lse[bi, i] = lz

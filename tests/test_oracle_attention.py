@@ -318,3 +318,22 @@ def test_split_and_merge_equals_whole(bounds):
     assert np.max(np.abs(lse - lse_w)) <= 1e-13 * np.max(np.abs(lse_w))
     if len(frags) == 1:
         assert np.array_equal(out, frags[0][0]) and np.array_equal(lse, frags[0][1])
+
+
+def test_queries_that_see_nothing_get_zero_and_minus_infinity():
+    """L < s_q: the first s_q - L queries of the chunk see no token (the library's contract)."""
+    H, d_hc, d_c, d_r, page = 2, 4, 8, 2, 4
+    case = _rand_case(20, 2, 5, [3, 6], H, d_hc, d_c, d_r, page)
+    out, lse = _decomp(case)
+    ol, lse2 = _absorbed(case)
+    assert np.all(out[0, :2] == 0) and np.all(np.isneginf(lse[0, :2]))
+    assert np.all(ol[0, :2] == 0) and np.all(np.isneginf(lse2[0, :2]))
+    assert np.all(np.isfinite(lse[0, 2:])) and np.all(np.isfinite(lse[1]))
+    # the rest is unaffected: query 2 of sequence 0 sees exactly token 0
+    one = dict(case)
+    one.update(s_q=1, q_c=case["q_c"][:, 2:3], q_r=case["q_r"][:, 2:3], seqlens=np.array([1, 4]))
+    o1, _ = _decomp(one)
+    assert np.max(np.abs(o1[0, 0] - out[0, 2])) <= 1e-12 * np.max(np.abs(out[0, 2]))
+    sel, _ = oracle.decode_decompressed(case["q_c"], case["q_r"], case["w_uk"], case["w_uv"], case["pool"],
+                                        case["block_table"], case["seqlens"], 5, case["scale"], queries=[4, 1])
+    assert np.array_equal(sel[:, 0], out[:, 4]) and np.array_equal(sel[:, 1], out[:, 1])

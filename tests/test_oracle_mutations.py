@@ -44,7 +44,7 @@ MUTATIONS.update({name: (APPEND, old, new) for name, (old, new) in {
     "new-token position off by one": ("return L[:, None] - int(s_q) + np.arange", "return L[:, None] - int(s_q) + 1 + np.arange"),
     "RoPE applied to the latent": ("out[..., d_c:] = rope_rotate(row[..., d_c:], rows_t)",
                                    "out[..., :64] = rope_rotate(row[..., :64], rows_t)"),
-    "row within page shifted": ("return pg, p % page", "return pg, (p + 1) % page"),
+    "appended row within page shifted": ("return pg, p % page", "return pg, (p + 1) % page"),
     "invalid page written": ("if pg < 0 or pg >= num_pages:", "if pg >= num_pages:"),
     "query turned the other way": ("out = rope_rotate(q, rows_t)",
                                    "out = rope_rotate(q, np.concatenate([rows_t[..., :32], -rows_t[..., 32:]], -1))"),
