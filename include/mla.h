@@ -67,9 +67,11 @@ typedef enum mla_status {
  * same fields: num_heads, page_size, kv_cache_dtype bf16 (sheratonhq.com §3). */
 typedef struct mla_decode_params {
   int32_t batch;              /* B >= 0 sequences */
-  int32_t s_q;                /* new query tokens per sequence: 1, or 2 for a
-                                 two-token verify step; query i of sequence b
-                                 sees tokens t <= seqlens[b] - s_q + i */
+  int32_t s_q;                /* new query tokens per sequence, 1 .. 256: 1 for
+                                 a decode step, 2 for a two-token verify step,
+                                 more for a short prefill chunk; query i of
+                                 sequence b sees tokens t <= seqlens[b] - s_q + i
+                                 (longer chunks: mla_prefill) */
   int32_t num_heads;          /* must be 128 */
   int32_t page_size;          /* must be 64 */
   int32_t max_blocks_per_seq; /* row length of block_table, >= 1 */
@@ -214,6 +216,53 @@ mla_status mla_rope_q(uint16_t* q_r, const float* rope_table, const int32_t* seq
  * (10000 is the usual value). */
 mla_status mla_rope_table(float* rope_table, int32_t max_pos, double base, void* stream);
 
+/* ---------------------------------------------------------------- prefill
+ *
+ * A chunk of s_q new tokens per sequence whose rows are already in the cache
+ * (seqlens counts them; query i sees the first seqlens[b] - s_q + i + 1 tokens).
+ * Short chunks are cheapest with matrix absorption, long ones with the keys and
+ * values expanded per head ("decompress"): K_h = c . W_UK[h]^T and
+ * V_h = c . W_UV[h] for every cached token ("DeepSeek的推理为什么比别人便宜一个数量级",
+ * leslieaibin.github.io, section "MLA"), then plain attention with the 192-wide
+ * score q_c . K_h + q_R . k_R.  The pages switch branches at
+ * kPrefillThresh = 256 query rows (sheratonhq.com section 3; section 6 reports
+ * the gain).  Both branches compute the same function. */
+
+typedef struct mla_prefill_params {
+  int32_t batch;              /* B >= 0 sequences */
+  int32_t s_q;                /* chunk length M >= 1 (at most 256 on the absorbed branch) */
+  int32_t num_heads;          /* must be 128 */
+  int32_t page_size;          /* must be 64 */
+  int32_t max_blocks_per_seq; /* row length of block_table, >= 1 */
+  int32_t mode;               /* 0: decompress when s_q >= threshold, else absorb;
+                                 1: always absorb; 2: always decompress */
+  int64_t num_pages;          /* physical pages in kv_blocks, >= 1 */
+  float scale;                /* 1/sqrt(192) for the DeepSeek dimensions */
+  int32_t threshold;          /* 0: 256 (the pages' kPrefillThresh); else 1 .. 257 */
+  int32_t reserved;           /* must be 0 */
+} mla_prefill_params;
+
+/* Workspace bytes of mla_prefill: on the decompress branch the expanded K and V,
+ * each [batch, max_blocks_per_seq * 64, 128, 128] bf16 (32 KiB per token slot),
+ * K at offset 0 and V at the size of one rounded up to 256 bytes; rows at or past
+ * seqlens[b] are left as they were.  On the absorbed branch what mla_decode
+ * needs.  0 when p is invalid. */
+size_t mla_prefill_workspace_size(const mla_prefill_params* p);
+
+/* Attention output of the chunk's queries.
+ *   q_c [B, s_q, 128, 128], q_r [B, s_q, 128, 64] (rotated), w_uk [128, 128, 512],
+ *   w_uv [128, 512, 128], kv_blocks / block_table / seqlens as for decode,
+ *   out [B, s_q, 128, 128] bf16, lse [B, s_q, 128] fp32 (may be NULL).
+ * Decompress branch: bf16 K and V (fp32 accumulation), fp32 scores and online
+ * softmax, fp32 accumulation of P . V with P rounded to bf16.  Absorbed branch:
+ * exactly mla_decode.  Workspace contents need no initialisation; calls sharing
+ * it must be ordered on one stream.  Preconditions on device values as for
+ * decode; a query with no visible token gets out = 0, lse = -inf. */
+mla_status mla_prefill(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* w_uk, const uint16_t* w_uv,
+                       const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens, uint16_t* out,
+                       float* lse, const mla_prefill_params* p, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* Benchmark timing hook.  After mla_profile_enable(1), every mla_decode_paged
  * and mla_decode call on any stream records HIP events around each of its
  * kernels (up to 65536 calls; the library creates those events once and keeps
@@ -231,6 +280,10 @@ mla_status mla_profile_collect(double* ms, int32_t* calls);
  * calls whose projection is not split) and the number of calls to *calls, and
  * clears that record. */
 mla_status mla_profile_collect_append(double* ms, int32_t* calls);
+
+/* The same for decompress-branch mla_prefill calls: ms[0] = decompress kernels,
+ * ms[1] = attention kernel. */
+mla_status mla_profile_collect_prefill(double* ms, int32_t* calls);
 
 /* Number of compute units of the current device (a HIP call). */
 mla_status mla_device_cu_count(int32_t* num_cus);

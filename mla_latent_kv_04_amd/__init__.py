@@ -13,7 +13,7 @@ import ctypes
 import math
 
 from . import _lib
-from ._lib import AppendParams, DecodeParams, MlaError  # noqa: F401
+from ._lib import AppendParams, DecodeParams, MlaError, PrefillParams  # noqa: F401
 
 NUM_HEADS = 128
 D_HC = 128
@@ -26,7 +26,10 @@ __all__ = [
     "absorb_q", "decode_paged", "up_proj", "decode", "gather_kv", "workspace_size", "make_params",
     "device_cu_count", "MlaError", "DecodeParams", "KernelTimer", "AppendParams", "append_kv",
     "append_workspace", "append_workspace_size", "make_append_params", "rope_q", "rope_table",
+    "PrefillParams", "make_prefill_params", "prefill", "prefill_workspace_size", "PREFILL_THRESHOLD",
 ]
+
+PREFILL_THRESHOLD = 256
 
 
 def _torch():
@@ -197,6 +200,7 @@ class KernelTimer:
         return self
 
     APPEND_NAMES = ("append_proj", "append_sum")
+    PREFILL_NAMES = ("decompress", "attention")
 
     def __exit__(self, *exc):
         lib = _lib.load()
@@ -206,7 +210,13 @@ class KernelTimer:
         ams = (ctypes.c_double * 2)()
         acalls = ctypes.c_int32(0)
         st2 = lib.mla_profile_collect_append(ams, ctypes.byref(acalls))
+        pms = (ctypes.c_double * 2)()
+        pcalls = ctypes.c_int32(0)
+        st3 = lib.mla_profile_collect_prefill(pms, ctypes.byref(pcalls))
         lib.mla_profile_enable(0)
+        _lib.check(st3, "mla_profile_collect_prefill")
+        self.prefill_ms = dict(zip(self.PREFILL_NAMES, list(pms)))
+        self.prefill_calls = int(pcalls.value)
         _lib.check(st, "mla_profile_collect")
         _lib.check(st2, "mla_profile_collect_append")
         self.ms = dict(zip(self.NAMES, list(ms)))
@@ -310,3 +320,56 @@ def rope_q(q_r, table, seqlens):
                         _ptr(seqlens, "seqlens", _i32(), (B,)), B, s_q, H, max_pos, _stream())
     _lib.check(st, "mla_rope_q")
     return q_r
+
+
+# ------------------------------------------------------------------ prefill
+
+
+def make_prefill_params(batch: int, s_q: int, max_blocks_per_seq: int, num_pages: int, scale: float = DEFAULT_SCALE,
+                        mode: int = 0, threshold: int = 0) -> PrefillParams:
+    p = PrefillParams()
+    p.batch, p.s_q, p.num_heads, p.page_size = batch, s_q, NUM_HEADS, PAGE
+    p.max_blocks_per_seq, p.mode, p.num_pages, p.scale = max_blocks_per_seq, mode, num_pages, scale
+    p.threshold, p.reserved = threshold, 0
+    return p
+
+
+def prefill_workspace_size(params: PrefillParams) -> int:
+    lib = _lib.load()
+    n = lib.mla_prefill_workspace_size(ctypes.byref(params))
+    if n == 0:
+        raise MlaError(_lib.MLA_ERR_INVALID_ARG, "mla_prefill_workspace_size", lib.mla_last_error().decode())
+    return int(n)
+
+
+def prefill(q_c, q_r, w_uk, w_uv, kv_blocks, block_table, seqlens, *, scale=DEFAULT_SCALE, mode=0, threshold=0,
+            out=None, lse=None, want_lse=True, workspace=None):
+    """Attention of a chunk of s_q new tokens per sequence (rows already cached).
+
+    q_c [B, s_q, 128, 128], q_r [B, s_q, 128, 64]; mode 0 picks the decompress branch
+    for s_q >= threshold (256 by default) and absorption below it, 1 forces
+    absorption, 2 forces decompression.  Returns (out [B, s_q, 128, 128] bf16, lse)."""
+    torch = _torch()
+    B, s_q = int(q_c.shape[0]), int(q_c.shape[1])
+    P = int(kv_blocks.shape[0])
+    mb = int(block_table.shape[1])
+    params = make_prefill_params(B, s_q, mb, P, scale, mode, threshold)
+    if out is None:
+        out = torch.empty(B, s_q, NUM_HEADS, D_HC, dtype=torch.bfloat16, device=q_c.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, s_q, NUM_HEADS, dtype=torch.float32, device=q_c.device)
+    if workspace is None:
+        workspace = torch.empty(prefill_workspace_size(params), dtype=torch.uint8, device=q_c.device)
+    lib = _lib.load()
+    st = lib.mla_prefill(
+        _ptr(q_c, "q_c", _bf16_types(), (B, s_q, NUM_HEADS, D_HC)),
+        _ptr(q_r, "q_r", _bf16_types(), (B, s_q, NUM_HEADS, D_R)),
+        _ptr(w_uk, "w_uk", _bf16_types(), (NUM_HEADS, D_HC, D_C)),
+        _ptr(w_uv, "w_uv", _bf16_types(), (NUM_HEADS, D_C, D_HC)),
+        _ptr(kv_blocks, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R)),
+        _ptr(block_table, "block_table", _i32(), (B, mb)), _ptr(seqlens, "seqlens", _i32(), (B,)),
+        _ptr(out, "out", _bf16_types(), (B, s_q, NUM_HEADS, D_HC)),
+        _ptr(lse, "lse", (torch.float32,), (B, s_q, NUM_HEADS)), ctypes.byref(params),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream())
+    _lib.check(st, "mla_prefill")
+    return out, lse

@@ -34,6 +34,9 @@ EXPORTS = (
     "mla_profile_enable",
     "mla_profile_collect",
     "mla_profile_collect_append",
+    "mla_profile_collect_prefill",
+    "mla_prefill_workspace_size",
+    "mla_prefill",
     "mla_device_cu_count",
     "mla_status_string",
     "mla_last_error",
@@ -72,6 +75,23 @@ class AppendParams(ctypes.Structure):
     ]
 
 
+class PrefillParams(ctypes.Structure):
+    """Mirror of ``mla_prefill_params``."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("s_q", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+        ("threshold", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 class MlaError(RuntimeError):
     def __init__(self, status: int, where: str, detail: str):
         super().__init__(f"{where}: status {status} ({detail})")
@@ -94,6 +114,7 @@ def load() -> ctypes.CDLL:
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     pp = ctypes.POINTER(DecodeParams)
     ap = ctypes.POINTER(AppendParams)
+    fp = ctypes.POINTER(PrefillParams)
     sigs = {
         "mla_absorb_q": ([vp, vp, vp, i32, i32, vp], ctypes.c_int),
         "mla_decode_workspace_size": ([pp, i32], sz),
@@ -109,6 +130,9 @@ def load() -> ctypes.CDLL:
         "mla_profile_enable": ([i32], ctypes.c_int),
         "mla_profile_collect": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)], ctypes.c_int),
         "mla_profile_collect_append": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)], ctypes.c_int),
+        "mla_profile_collect_prefill": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)], ctypes.c_int),
+        "mla_prefill_workspace_size": ([fp], sz),
+        "mla_prefill": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, fp, vp, sz, vp], ctypes.c_int),
         "mla_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "mla_last_error": ([], ctypes.c_char_p),
     }

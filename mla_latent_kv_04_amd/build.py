@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla_kv04.so")
-SOURCES = ["mla_api.hip", "decode.hip", "head_gemm.hip", "append.hip"]
+SOURCES = ["mla_api.hip", "decode.hip", "head_gemm.hip", "append.hip", "prefill.hip"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

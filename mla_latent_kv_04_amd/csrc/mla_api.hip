@@ -13,6 +13,7 @@
 #include "mla.h"
 #include "common.h"
 #include "append.h"
+#include "prefill.h"
 
 namespace {
 
@@ -43,10 +44,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Query tokens per sequence the absorbed decode accepts: beyond the prefill
+// threshold the decompress branch (mla_prefill) is the one to use.
+constexpr int kMaxDecodeSq = 256;
+constexpr int kPrefillThreshold = 256;
+
 mla_status check_params(const mla_decode_params* p) {
   if (p == nullptr) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
   if (p->batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch %d < 0", p->batch);
-  if (p->s_q != 1 && p->s_q != 2) return fail(MLA_ERR_UNSUPPORTED, "s_q %d (supported: 1, 2)", p->s_q);
+  if (p->s_q < 1 || p->s_q > kMaxDecodeSq)
+    return fail(MLA_ERR_UNSUPPORTED, "s_q %d (supported: 1 .. %d)", p->s_q, kMaxDecodeSq);
   if (p->num_heads != mla::kHeads) return fail(MLA_ERR_UNSUPPORTED, "num_heads %d (supported: 128)", p->num_heads);
   if (p->page_size != mla::kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size %d (supported: 64)", p->page_size);
   if (p->max_blocks_per_seq < 1) return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", p->max_blocks_per_seq);
@@ -109,6 +116,9 @@ struct Profiler {
   // cache-append calls: 0 start, 1 projection done, 2 partial sums done
   std::vector<std::array<hipEvent_t, 3>> aev;
   size_t aused = 0;
+  // decompress-branch prefill calls: 0 start, 1 decompress done, 2 attention done
+  std::vector<std::array<hipEvent_t, 3>> pev;
+  size_t pused = 0;
 };
 Profiler g_prof;
 constexpr size_t kMaxProfiledCalls = 1 << 16;
@@ -125,17 +135,39 @@ hipEvent_t* prof_slot() {
   return g_prof.ev[g_prof.used++].data();
 }
 
-hipEvent_t* prof_append_slot() {
+hipEvent_t* prof_triple_slot(std::vector<std::array<hipEvent_t, 3>>& v, size_t& used) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
-  if (!g_prof.enabled || g_prof.aused >= kMaxProfiledCalls) return nullptr;
-  if (g_prof.aused == g_prof.aev.size()) {
+  if (!g_prof.enabled || used >= kMaxProfiledCalls) return nullptr;
+  if (used == v.size()) {
     std::array<hipEvent_t, 3> e{};
     for (auto& x : e)
       if (hipEventCreate(&x) != hipSuccess) return nullptr;
-    g_prof.aev.push_back(e);
+    v.push_back(e);
   }
-  return g_prof.aev[g_prof.aused++].data();
+  return v[used++].data();
 }
+
+mla_status collect_triples(std::vector<std::array<hipEvent_t, 3>>& v, size_t& used, double* ms, int32_t* calls) {
+  if (ms == nullptr || calls == nullptr) return fail(MLA_ERR_INVALID_ARG, "NULL output pointer");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  ms[0] = ms[1] = 0.0;
+  for (size_t i = 0; i < used; ++i) {
+    auto& e = v[i];
+    hipError_t r = hipEventSynchronize(e[2]);
+    if (r != hipSuccess) return hip_fail(r, "hipEventSynchronize");
+    for (int k = 0; k < 2; ++k) {
+      float t = 0.f;
+      r = hipEventElapsedTime(&t, e[k], e[k + 1]);
+      if (r != hipSuccess) return hip_fail(r, "hipEventElapsedTime");
+      ms[k] += t;
+    }
+  }
+  *calls = (int32_t)used;
+  used = 0;
+  return ok();
+}
+
+hipEvent_t* prof_append_slot() { return prof_triple_slot(g_prof.aev, g_prof.aused); }
 
 mla_status run_paged(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv, const int32_t* bt,
                      const int32_t* seqlens, uint16_t* out_latent, float* lse, const mla_decode_params* p,
@@ -170,6 +202,54 @@ mla_status check_append(const mla_append_params* p) {
 }
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+mla_status check_prefill(const mla_prefill_params* p) {
+  if (p == nullptr) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch %d < 0", p->batch);
+  if (p->s_q < 1 || p->s_q > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "s_q %d", p->s_q);
+  if ((int64_t)p->batch * p->s_q > (1 << 24)) return fail(MLA_ERR_INVALID_ARG, "batch * s_q too large");
+  if (p->num_heads != mla::kHeads) return fail(MLA_ERR_UNSUPPORTED, "num_heads %d (supported: 128)", p->num_heads);
+  if (p->page_size != mla::kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size %d (supported: 64)", p->page_size);
+  if (p->max_blocks_per_seq < 1 || p->max_blocks_per_seq > (1 << 20))
+    return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_seq %d", p->max_blocks_per_seq);
+  if (p->num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages %lld < 1", (long long)p->num_pages);
+  if (!(p->scale > 0.f) || p->scale > 1e30f) return fail(MLA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (p->mode < 0 || p->mode > 2) return fail(MLA_ERR_INVALID_ARG, "mode %d (0 auto, 1 absorb, 2 decompress)", p->mode);
+  if (p->threshold < 0 || p->threshold > kMaxDecodeSq + 1)
+    return fail(MLA_ERR_INVALID_ARG, "threshold %d (0 .. %d)", p->threshold, kMaxDecodeSq + 1);
+  if (p->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "reserved must be 0");
+  const int thr = p->threshold > 0 ? p->threshold : kPrefillThreshold;
+  const bool absorb = p->mode == 1 || (p->mode == 0 && p->s_q < thr);
+  if (absorb && p->s_q > kMaxDecodeSq)
+    return fail(MLA_ERR_UNSUPPORTED, "s_q %d on the absorbed branch (at most %d)", p->s_q, kMaxDecodeSq);
+  if (!absorb && (int64_t)p->batch * p->max_blocks_per_seq * mla::kPage * mla::kHeads > ((int64_t)1 << 40))
+    return fail(MLA_ERR_INVALID_ARG, "expanded K/V too large");
+  return MLA_OK;
+}
+
+bool prefill_absorbs(const mla_prefill_params* p) {
+  const int thr = p->threshold > 0 ? p->threshold : kPrefillThreshold;
+  return p->mode == 1 || (p->mode == 0 && p->s_q < thr);
+}
+
+mla_decode_params absorbed_params(const mla_prefill_params* p) {
+  mla_decode_params d{};
+  d.batch = p->batch;
+  d.s_q = p->s_q;
+  d.num_heads = p->num_heads;
+  d.page_size = p->page_size;
+  d.max_blocks_per_seq = p->max_blocks_per_seq;
+  d.num_splits = 0;
+  d.num_pages = p->num_pages;
+  d.scale = p->scale;
+  d.reserved = 0;
+  return d;
+}
+
+// Bytes of one expanded tensor (K or V): [batch, max_blocks * 64, 128, 128] bf16.
+size_t expanded_bytes(const mla_prefill_params* p) {
+  return round_up((size_t)p->batch * p->max_blocks_per_seq * mla::kPage * mla::kHeads * mla::kDimC * 2);
+}
 
 }  // namespace
 
@@ -361,11 +441,58 @@ mla_status mla_decode(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* 
   return ok();
 }
 
+size_t mla_prefill_workspace_size(const mla_prefill_params* p) {
+  if (check_prefill(p) != MLA_OK) return 0;
+  if (prefill_absorbs(p)) {
+    const mla_decode_params d = absorbed_params(p);
+    return mla_decode_workspace_size(&d, 1);
+  }
+  return p->batch == 0 ? 16 : 2 * expanded_bytes(p);
+}
+
+mla_status mla_prefill(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* w_uk, const uint16_t* w_uv,
+                       const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens, uint16_t* out,
+                       float* lse, const mla_prefill_params* p, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  mla_status st = check_prefill(p);
+  if (st != MLA_OK) return st;
+  if (prefill_absorbs(p)) {
+    const mla_decode_params d = absorbed_params(p);
+    return mla_decode(q_c, q_r, w_uk, w_uv, kv_blocks, block_table, seqlens, out, lse, &d, workspace,
+                      workspace_bytes, stream);
+  }
+  if (p->batch == 0) return ok();
+  if (!q_c || !q_r || !w_uk || !w_uv || !kv_blocks || !block_table || !seqlens || !out || !workspace)
+    return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q_c) || !aligned16(q_r) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(kv_blocks) ||
+      !aligned16(out) || !aligned16(workspace) || !aligned4(block_table) || !aligned4(seqlens) || !aligned4(lse))
+    return fail(MLA_ERR_MISALIGNED, "tensor or workspace not aligned (16 B; block_table, seqlens and lse 4 B)");
+  const size_t need = mla_prefill_workspace_size(p);
+  if (workspace_bytes < need) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* kbuf = static_cast<uint16_t*>(workspace);
+  uint16_t* vbuf = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(workspace) + expanded_bytes(p));
+  const int max_len = p->max_blocks_per_seq * mla::kPage;
+  hipEvent_t* ev = prof_triple_slot(g_prof.pev, g_prof.pused);
+  hipError_t e;
+  if (ev != nullptr && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = mla::launch_decompress(kv_blocks, block_table, seqlens, w_uk, w_uv, kbuf, vbuf, p->batch,
+                             p->max_blocks_per_seq, max_len, p->num_pages, s);
+  if (e != hipSuccess) return hip_fail(e, "decompress launch");
+  if (ev != nullptr && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = mla::launch_prefill_attention(q_c, q_r, kbuf, vbuf, kv_blocks, block_table, seqlens, out, lse, p->batch,
+                                    p->s_q, p->max_blocks_per_seq, max_len, p->num_pages, p->scale, s);
+  if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  if (ev != nullptr && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return ok();
+}
+
 mla_status mla_profile_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   g_prof.enabled = enable != 0;
   g_prof.used = 0;
   g_prof.aused = 0;
+  g_prof.pused = 0;
   return ok();
 }
 
@@ -390,23 +517,11 @@ mla_status mla_profile_collect(double* ms, int32_t* calls) {
 }
 
 mla_status mla_profile_collect_append(double* ms, int32_t* calls) {
-  if (ms == nullptr || calls == nullptr) return fail(MLA_ERR_INVALID_ARG, "NULL output pointer");
-  std::lock_guard<std::mutex> lk(g_prof.mu);
-  ms[0] = ms[1] = 0.0;
-  for (size_t i = 0; i < g_prof.aused; ++i) {
-    auto& e = g_prof.aev[i];
-    hipError_t r = hipEventSynchronize(e[2]);
-    if (r != hipSuccess) return hip_fail(r, "hipEventSynchronize");
-    for (int k = 0; k < 2; ++k) {
-      float t = 0.f;
-      r = hipEventElapsedTime(&t, e[k], e[k + 1]);
-      if (r != hipSuccess) return hip_fail(r, "hipEventElapsedTime");
-      ms[k] += t;
-    }
-  }
-  *calls = (int32_t)g_prof.aused;
-  g_prof.aused = 0;
-  return ok();
+  return collect_triples(g_prof.aev, g_prof.aused, ms, calls);
+}
+
+mla_status mla_profile_collect_prefill(double* ms, int32_t* calls) {
+  return collect_triples(g_prof.pev, g_prof.pused, ms, calls);
 }
 
 mla_status mla_gather_kv(const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens,

@@ -1,0 +1,449 @@
+// Prefill of absorbed MLA on gfx950: the decompress branch.
+//
+// A chunk of M >= 256 new query tokens per sequence is cheaper to attend with
+// the keys and values expanded per head than with matrix absorption
+// ("撕开 DeepSeek MLA 源码", sheratonhq.com, section 3: kPrefillThresh = 256,
+// absorb below it and decompress above; section 6: the measured gain).  Two
+// kernels:
+//
+//   decompress_kernel  K[b, t, h, :] = c_t . W_UK[h]^T,  V[b, t, h, :] = c_t . W_UV[h]
+//                      for every cached token t < seqlens[b] ("DeepSeek的推理为什么
+//                      比别人便宜一个数量级", leslieaibin.github.io, section "MLA":
+//                      K = c . W_UK, V = c . W_UV), bf16 out, fp32 accumulation.
+//   prefill_attention_kernel
+//                      softmax((q_c . K_h + q_R . k_R) / sqrt(192)) . V_h with the
+//                      chunk's causal rule (query i sees the first L - M + i + 1
+//                      tokens), online softmax in fp32 (sheratonhq.com section 4
+//                      for the score).
+#include "prefill.h"
+
+namespace mla {
+
+namespace {
+
+// ------------------------------------------------------------------ decompress
+
+constexpr int kDTok = 256;        // tokens per decompress workgroup
+constexpr int kDK = 64;           // latent values per K-loop chunk
+constexpr int kDPitchRow = kDK * 2 + 16;      // [row][64 k] tiles: 144 B, 16-byte reads of 8 rows spread over banks
+constexpr int kDPitchV = 2 * kDimC * 2 + 32;  // [64 k][256 n] tile: 544 B = 8 banks mod 32 for transposing reads
+
+struct DecompArgs {
+  const uint16_t* kv;       // [num_pages, 64, 576]
+  const int32_t* bt;        // [B, max_blocks]
+  const int32_t* seqlens;   // [B]
+  const uint16_t* w;        // W_UK [H, 128, 512] or W_UV [H, 512, 128]
+  uint16_t* out;            // [B, max_len, H, 128]
+  int64_t num_pages;
+  int max_blocks, max_len;
+};
+
+__device__ __forceinline__ int clamp_len(int L, int max_blocks) {
+  const int cap = max_blocks * kPage;
+  return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+// Computes the transposed product out^T[n, t] = sum_k W[n, k] c[t, k] for 256 tokens
+// and the 256 output columns of two heads, so that each lane's accumulators hold
+// consecutive output columns of one token (8-byte stores).  Eight waves: wave w
+// owns head 2 hp + w / 4 (128 columns = 4 MFMA row blocks) and tokens
+// 64 (w % 4) .. +63 (2 column blocks) of v_mfma_f32_32x32x16_bf16.  The A
+// operand (weights) comes from LDS: for K row-major [n][k] (16-byte reads), for
+// V [k][n] through transposing reads; the B operand (latent rows) from a
+// [token][k] LDS tile.  Each 64-wide chunk of the latent is loaded into
+// registers while the previous one is multiplied.
+template <bool kIsV>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
+void decompress_kernel(DecompArgs a) {
+  const int hp = blockIdx.x, tb = blockIdx.y, b = blockIdx.z;
+  const int L = clamp_len(a.seqlens[b], a.max_blocks);
+  const int t0 = tb * kDTok;
+  if (t0 >= L) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  constexpr int kWBytes = kIsV ? kDK * kDPitchV : 2 * kDimC * kDPitchRow;
+  __shared__ __attribute__((aligned(16))) unsigned char wt[kWBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char ct[kDTok * kDPitchRow];
+
+  // Latent chunk loads: thread -> token row tid / 8 + 64 i (i < 4), 16 bytes at k 8 (tid % 8).
+  const uint16_t* crow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + tid / 8 + 64 * i;
+    const int tt = t < L ? t : 0;             // rows past the sequence read its token 0, never stored
+    int64_t page = a.bt[(size_t)b * a.max_blocks + tt / kPage];
+    page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+    crow[i] = a.kv + ((size_t)page * kPage + (tt & (kPage - 1))) * kRow + 8 * (tid % 8);
+  }
+  unsigned char* cdst = ct + (tid / 8) * kDPitchRow + (tid % 8) * 16;
+
+  // Weight chunk loads.
+  const uint16_t* wsrc[4];
+  unsigned char* wdst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!kIsV) {
+      // W_UK rows n = tid / 8 + 64 i of the head pair ([n][k], 16 bytes at k 8 (tid % 8))
+      const int n = tid / 8 + 64 * i;
+      wsrc[i] = a.w + ((size_t)(2 * hp + n / kDimC) * kDimC + (n % kDimC)) * kLatent + 8 * (tid % 8);
+      wdst[i] = wt + n * kDPitchRow + (tid % 8) * 16;
+    } else {
+      // W_UV rows k = tid / 32 + 16 i of the chunk, 16 bytes of head 2 hp + (tid % 32) / 16 at e 8 (tid % 16)
+      const int k = tid / 32 + 16 * i, nc = tid % 32;
+      wsrc[i] = a.w + ((size_t)(2 * hp + nc / 16) * kLatent + k) * kDimC + 8 * (nc % 16);
+      wdst[i] = wt + k * kDPitchV + nc * 16;
+    }
+  }
+
+  u32x4 cv[4], wv[4];
+  auto load_chunk = [&](int kc) {
+    const int k0 = kc * kDK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cv[i] = *(const u32x4*)(crow[i] + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[i] = *(const u32x4*)(wsrc[i] + (kIsV ? (size_t)k0 * kDimC : (size_t)k0));
+  };
+
+  const int nh = wave / 4;            // head of the pair this wave computes
+  const int tq = wave % 4;            // token quarter
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[m][n][j] = 0.f;
+
+  load_chunk(0);
+  for (int kc = 0; kc < kLatent / kDK; ++kc) {
+    if (kc > 0) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4*)(cdst + 64 * i * kDPitchRow) = cv[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4*)wdst[i] = wv[i];
+    __syncthreads();
+    if (kc + 1 < kLatent / kDK) load_chunk(kc + 1);
+#pragma unroll
+    for (int ks = 0; ks < kDK / 16; ++ks) {
+      s16x8 bop[2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        bop[n] = *(const s16x8*)(ct + (64 * tq + 32 * n + (lane & 31)) * kDPitchRow + (16 * ks + 8 * (lane >> 5)) * 2);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        s16x8 aop;
+        const int nrow = kDimC * nh + 32 * m;   // first output column of this row block
+        if (!kIsV) {
+          aop = *(const s16x8*)(wt + (nrow + (lane & 31)) * kDPitchRow + (16 * ks + 8 * (lane >> 5)) * 2);
+        } else {
+          // A[n][k] = W_UV[k][n]: rows k 16 ks + 8 (lane / 32) + 0..7 of column n, as two
+          // transposing reads of 4 rows.  Within a 16-lane group, lane s reads row 4 e + s / 4
+          // ... at columns 4 (s % 4): the group covers columns nrow + 16 (lane % 32 / 16) .. +15.
+          const int g = (lane >> 4) & 1, s = lane & 15;
+          const unsigned char* p = wt + (16 * ks + 8 * (lane >> 5) + (s >> 2)) * kDPitchV +
+                                   (nrow + 16 * g + 4 * (s & 3)) * 2;
+          const s16x4 lo = lds_read_tr4(p);
+          const s16x4 hi = lds_read_tr4(p + 4 * kDPitchV);
+          aop = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) acc[m][n] = mfma32(aop, bop[n], acc[m][n]);
+      }
+    }
+  }
+
+  // D layout (32x32): lane l, register j -> row 8 (j / 4) + 4 (l / 32) + j % 4 (output column
+  // within the row block), column l % 32 (token within the column block).
+  const int h = 2 * hp + nh;
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int t = t0 + 64 * tq + 32 * n + (lane & 31);
+    if (t >= L) continue;
+    uint16_t* dst = a.out + (((size_t)b * a.max_len + t) * kHeads + h) * kDimC;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x2 o;
+        o[0] = pack_bf16x2(acc[m][n][4 * q], acc[m][n][4 * q + 1]);
+        o[1] = pack_bf16x2(acc[m][n][4 * q + 2], acc[m][n][4 * q + 3]);
+        *(u32x2*)(dst + 32 * m + 8 * q + 4 * (lane >> 5)) = o;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decompress(const uint16_t* kv, const int32_t* bt, const int32_t* seqlens, const uint16_t* w_uk,
+                             const uint16_t* w_uv, uint16_t* k_out, uint16_t* v_out, int batch, int max_blocks,
+                             int max_len, int64_t num_pages, hipStream_t s) {
+  if (batch <= 0) return hipSuccess;
+  DecompArgs a;
+  a.kv = kv;
+  a.bt = bt;
+  a.seqlens = seqlens;
+  a.num_pages = num_pages;
+  a.max_blocks = max_blocks;
+  a.max_len = max_len;
+  const dim3 grid(kHeads / 2, (max_len + kDTok - 1) / kDTok, batch);
+  a.w = w_uk;
+  a.out = k_out;
+  hipLaunchKernelGGL(decompress_kernel<false>, grid, dim3(512), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  a.w = w_uv;
+  a.out = v_out;
+  hipLaunchKernelGGL(decompress_kernel<true>, grid, dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla
+
+namespace mla {
+
+namespace {
+
+// ------------------------------------------------------------------ attention
+
+constexpr int kAQ = 128;                 // queries per workgroup (4 waves x 32)
+constexpr int kAKeys = 64;               // keys per tile (one page)
+constexpr int kAD = kDimC + kRope;       // 192: score dimension
+constexpr int kKPitch = kAD * 2 + 16;    // 400 B: K tile rows [key][192]
+constexpr int kVPitch = kDimC * 2 + 32;  // 288 B: V tile rows [key][128], 8 banks mod 32
+constexpr int kKTile = kAKeys * kKPitch;
+constexpr int kVTile = kAKeys * kVPitch;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+  const uint16_t* q_c;      // [B, M, H, 128]
+  const uint16_t* q_r;      // [B, M, H, 64]
+  const uint16_t* k;        // [B, max_len, H, 128]
+  const uint16_t* v;        // [B, max_len, H, 128]
+  const uint16_t* kv;       // [num_pages, 64, 576] (k_R = columns 512..575)
+  const int32_t* bt;        // [B, max_blocks]
+  const int32_t* seqlens;   // [B]
+  uint16_t* out;            // [B, M, H, 128]
+  float* lse;               // [B, M, H] or null
+  int64_t num_pages;
+  int M, max_blocks, max_len;
+  float scale_log2;         // softmax scale times log2(e)
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One workgroup per (128-query tile, head, sequence).  Wave w owns queries
+// i0 + 32 w .. +31.  Per 64-key tile (one page) it computes the transposed scores
+// S^T[key, query] = K_tile . Q^T (v_mfma_f32_32x32x16_bf16: 2 key blocks x 12 k-steps
+// over the 192 score dimensions, A = key rows from LDS, B = the wave's queries held
+// in registers), so that each lane's accumulators belong to one query (lane % 32)
+// and the online softmax needs one cross-lane exchange (lane ^ 32).  Then
+// O^T[e, query] += V^T . P^T (4 column blocks x 4 k-steps; A = V columns through
+// transposing LDS reads, B = the probabilities straight from the score registers,
+// with the keys of each MFMA k-slot ordered as the score layout holds them).
+// Key and value tiles are double-buffered in LDS, the next tile's loads in flight
+// during the current tile's MFMAs.
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void prefill_attention_kernel(AttnArgs a) {
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = clamp_len(a.seqlens[b], a.max_blocks);
+  const int i0 = qt * kAQ;
+  const int last_q = min(i0 + kAQ, a.M) - 1;
+  const int p_last = L - a.M + last_q;                 // position of the tile's last query
+  const int n_tiles = p_last >= 0 ? p_last / kAKeys + 1 : 0;
+
+  __shared__ __attribute__((aligned(16))) unsigned char kt[2][kKTile];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[2][kVTile];
+
+  // This lane's query: i0 + 32 wave + lane % 32 (lanes l and l ^ 32 share it).
+  const int qi = i0 + 32 * wave + (lane & 31);
+  const bool q_ok = qi < a.M;
+  const int qpos = L - a.M + qi;                       // keys t <= qpos are visible
+  const int g2 = lane >> 5;
+
+  // Q^T operand: k-step ks covers score dimensions 16 ks + 8 g2 .. +7.
+  s16x8 qop[kAD / 16];
+  {
+    const size_t row = ((size_t)b * a.M + (q_ok ? qi : 0)) * kHeads + h;
+#pragma unroll
+    for (int ks = 0; ks < kAD / 16; ++ks) {
+      const int d = 16 * ks + 8 * g2;
+      qop[ks] = d < kDimC ? *(const s16x8*)(a.q_c + row * kDimC + d)
+                          : *(const s16x8*)(a.q_r + row * kRope + (d - kDimC));
+    }
+  }
+
+  // Tile loads: K part 64 rows x 24 chunks (16 from K_h, 8 from k_R), V part 64 x 16 chunks.
+  // Thread tid takes K chunks tid + 256 i (i < 6) and V chunks tid + 256 i (i < 4).
+  u32x4 kreg[6], vreg[4];
+  auto load_tile = [&](int j) {
+    const int t0 = j * kAKeys;
+    int64_t page = a.bt[(size_t)b * a.max_blocks + j];
+    page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int c = tid + 256 * i, r = c / 24, x = c % 24;
+      const int t = min(t0 + r, L - 1);                 // rows past the sequence: a finite, masked row
+      if (x < 16)
+        kreg[i] = *(const u32x4*)(a.k + (((size_t)b * a.max_len + t) * kHeads + h) * kDimC + 8 * x);
+      else
+        kreg[i] = *(const u32x4*)(a.kv + ((size_t)page * kPage + (t & (kPage - 1))) * kRow + kLatent + 8 * (x - 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, r = c / 16, x = c % 16;
+      const int t = min(t0 + r, L - 1);
+      vreg[i] = *(const u32x4*)(a.v + (((size_t)b * a.max_len + t) * kHeads + h) * kDimC + 8 * x);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int c = tid + 256 * i, r = c / 24, x = c % 24;
+      *(u32x4*)(kt[buf] + r * kKPitch + 16 * x) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, r = c / 16, x = c % 16;
+      *(u32x4*)(vt[buf] + r * kVPitch + 16 * x) = vreg[i];
+    }
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[e][j] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < n_tiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < n_tiles) load_tile(j + 1);
+    const unsigned char* K = kt[buf];
+    const unsigned char* V = vt[buf];
+
+    // S^T for key blocks mb = 0, 1: lane l, register r -> key 32 mb + 8 (r / 4) + 4 g2 + r % 4.
+    f32x16 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kAD / 16; ++ks) {
+        const s16x8 kop = *(const s16x8*)(K + (32 * mb + (lane & 31)) * kKPitch + (16 * ks + 8 * g2) * 2);
+        s[mb] = mfma32(kop, qop[ks], s[mb]);
+      }
+    }
+
+    // Online softmax (base 2) of this lane's query over the tile's keys.
+    const int t0 = j * kAKeys;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = t0 + 32 * mb + 8 * (r >> 2) + 4 * g2 + (r & 3);
+        float x = s[mb][r] * a.scale_log2;
+        x = key <= qpos ? x : -INFINITY;
+        s[mb][r] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float ps = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(s[mb][r] - m_use);
+        s[mb][r] = p;
+        ps += p;
+      }
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[e][r] *= alpha;
+
+    // O^T += V^T . P^T.  k-step ks = (key block mb = ks / 2, half hf = ks % 2): slot i of
+    // lane group g2 holds key 32 mb + 16 hf + 8 (i / 4) + 4 g2 + i % 4, i.e. score register
+    // 8 hf + i.  The V^T operand gathers the same keys: two transposing reads of 4 rows.
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int mb = ks >> 1, hf = ks & 1;
+      s16x8 pop;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w2 = pack_bf16x2(s[mb][8 * hf + 2 * i], s[mb][8 * hf + 2 * i + 1]);
+        pop[2 * i] = (short)(w2 & 0xFFFFu);
+        pop[2 * i + 1] = (short)(w2 >> 16);
+      }
+      const int grp = (lane >> 4) & 1, sl = lane & 15;
+      const int row = 32 * mb + 16 * hf + 4 * g2 + (sl >> 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned char* p = V + row * kVPitch + (32 * e + 16 * grp + 4 * (sl & 3)) * 2;
+        const s16x4 lo = lds_read_tr4(p);
+        const s16x4 hi = lds_read_tr4(p + 8 * kVPitch);
+        const s16x8 vop = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[e] = mfma32(vop, pop, o[e]);
+      }
+    }
+
+    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!q_ok) return;
+  // O^T layout: lane l, register r -> e = 32 blk + 8 (r / 4) + 4 g2 + r % 4, query lane % 32.
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  uint16_t* dst = a.out + (((size_t)b * a.M + qi) * kHeads + h) * kDimC;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x2 w;
+      w[0] = pack_bf16x2(o[e][4 * q] * inv, o[e][4 * q + 1] * inv);
+      w[1] = pack_bf16x2(o[e][4 * q + 2] * inv, o[e][4 * q + 3] * inv);
+      *(u32x2*)(dst + 32 * e + 8 * q + 4 * g2) = w;
+    }
+  if (a.lse != nullptr && g2 == 0)
+    a.lse[((size_t)b * a.M + qi) * kHeads + h] = l_run > 0.f ? (m_run + __log2f(l_run)) / kLog2e : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_attention(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* k, const uint16_t* v,
+                                    const uint16_t* kv, const int32_t* bt, const int32_t* seqlens, uint16_t* out,
+                                    float* lse, int batch, int M, int max_blocks, int max_len, int64_t num_pages,
+                                    float scale, hipStream_t s) {
+  if (batch <= 0 || M <= 0) return hipSuccess;
+  AttnArgs a;
+  a.q_c = q_c;
+  a.q_r = q_r;
+  a.k = k;
+  a.v = v;
+  a.kv = kv;
+  a.bt = bt;
+  a.seqlens = seqlens;
+  a.out = out;
+  a.lse = lse;
+  a.num_pages = num_pages;
+  a.M = M;
+  a.max_blocks = max_blocks;
+  a.max_len = max_len;
+  a.scale_log2 = scale * kLog2e;
+  hipLaunchKernelGGL(prefill_attention_kernel, dim3((M + kAQ - 1) / kAQ, kHeads, batch), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

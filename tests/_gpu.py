@@ -82,3 +82,25 @@ def absorbed_inputs(inp):
 def upload(inp):
     return dict(q_c=dev_bf16(inp.q_c), q_r=dev_bf16(inp.q_r), w_uk=dev_bf16(inp.w_uk), w_uv=dev_bf16(inp.w_uv),
                 pool=dev_bf16(inp.pool), bt=dev_i32(inp.block_table), sl=dev_i32(inp.seqlens))
+
+
+# ---------------------------------------------------------------------------- bf16 results with a derived bound
+
+U = 2.0 ** -24
+
+
+def assert_bf16_match(got_bits, exact, err, what, max_frac=1e-2):
+    """|gpu - exact| <= err + 2^-8 (|exact| + err) everywhere (err: the fp32 error bound of the
+    computation, 2^-8 (|exact| + err): one bf16 rounding); bits equal to RNE(exact) but for max_frac."""
+    ref_bits = oracle.f64_to_bf16_bits(exact)
+    assert got_bits.shape == ref_bits.shape
+    got = oracle.bf16_bits_to_f64(got_bits)
+    bound = err + 2.0 ** -8 * (np.abs(exact) + err)
+    over = np.abs(got - exact) > bound
+    assert not over.any(), f"{what}: {int(over.sum())} elements beyond the bound, worst excess " \
+        f"{float(np.max(np.abs(got - exact) - bound)):.3e}"
+    frac = float(np.count_nonzero(got_bits != ref_bits)) / max(got_bits.size, 1)
+    assert frac <= max_frac, f"{what}: {frac:.2%} of elements differ from the rounded oracle"
+    return frac
+
+

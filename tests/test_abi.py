@@ -65,7 +65,7 @@ def _paged(lib, p, ptrs=None, ws=A, ws_bytes=1 << 30):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("s_q", 3, _lib.MLA_ERR_UNSUPPORTED), ("s_q", 0, _lib.MLA_ERR_UNSUPPORTED),
+    ("s_q", 257, _lib.MLA_ERR_UNSUPPORTED), ("s_q", 0, _lib.MLA_ERR_UNSUPPORTED),
     ("num_heads", 64, _lib.MLA_ERR_UNSUPPORTED), ("page_size", 16, _lib.MLA_ERR_UNSUPPORTED),
     ("batch", -1, _lib.MLA_ERR_INVALID_ARG), ("max_blocks_per_seq", 0, _lib.MLA_ERR_INVALID_ARG),
     ("num_pages", 0, _lib.MLA_ERR_INVALID_ARG), ("scale", 0.0, _lib.MLA_ERR_INVALID_ARG),
@@ -99,7 +99,8 @@ def test_workspace_checks(lib):
     assert fused == need + 2 * (2 * 128 * 512 * 2)
     assert _paged(lib, p, ws=A, ws_bytes=need - 1) == _lib.MLA_ERR_WORKSPACE
     assert _paged(lib, p, ws=None, ws_bytes=need) == _lib.MLA_ERR_WORKSPACE
-    assert lib.mla_decode_workspace_size(ctypes.byref(_params(s_q=5)), 0) == 0
+    assert lib.mla_decode_workspace_size(ctypes.byref(_params(s_q=300)), 0) == 0
+    assert lib.mla_decode_workspace_size(ctypes.byref(_params(s_q=256)), 0) > 0
 
 
 def test_empty_batch_is_a_noop(lib):
@@ -213,3 +214,57 @@ def test_rope_argument_checks(lib):
     assert lib.mla_rope_table(A, 10, float("nan"), None) == _lib.MLA_ERR_INVALID_ARG
     assert lib.mla_rope_table(None, 10, 10000.0, None) == _lib.MLA_ERR_INVALID_ARG
     assert lib.mla_rope_table(MIS, 10, 10000.0, None) == _lib.MLA_ERR_MISALIGNED
+
+
+# ------------------------------------------------------------------ prefill
+
+
+def _pparams(**kw):
+    p = _lib.PrefillParams()
+    p.batch, p.s_q, p.num_heads, p.page_size, p.max_blocks_per_seq = 2, 512, 128, 64, 16
+    p.mode, p.num_pages, p.scale, p.threshold, p.reserved = 0, 64, 0.0721687836, 0, 0
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _prefill(lib, p, ws=A, ws_bytes=1 << 40, ptrs=None):
+    q, r, wk, wv, kv, bt, sl, out, lse = ptrs or (A, A, A, A, A, A, A, A, None)
+    return lib.mla_prefill(q, r, wk, wv, kv, bt, sl, out, lse, ctypes.byref(p), ws, ws_bytes, None)
+
+
+def test_prefill_params_struct_layout():
+    assert ctypes.sizeof(_lib.PrefillParams) == 48 and _lib.PrefillParams.num_pages.offset == 24
+    assert _lib.PrefillParams.threshold.offset == 36 and _lib.PrefillParams.reserved.offset == 40
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_heads", 64, _lib.MLA_ERR_UNSUPPORTED), ("page_size", 32, _lib.MLA_ERR_UNSUPPORTED),
+    ("batch", -1, _lib.MLA_ERR_INVALID_ARG), ("s_q", 0, _lib.MLA_ERR_INVALID_ARG),
+    ("mode", 3, _lib.MLA_ERR_INVALID_ARG), ("threshold", 300, _lib.MLA_ERR_INVALID_ARG),
+    ("scale", 0.0, _lib.MLA_ERR_INVALID_ARG), ("num_pages", 0, _lib.MLA_ERR_INVALID_ARG),
+    ("max_blocks_per_seq", 0, _lib.MLA_ERR_INVALID_ARG), ("reserved", 1, _lib.MLA_ERR_INVALID_ARG),
+])
+def test_prefill_bad_params_rejected(lib, field, value, status):
+    p = _pparams(**{field: value})
+    assert _prefill(lib, p) == status
+    assert lib.mla_prefill_workspace_size(ctypes.byref(p)) == 0
+
+
+def test_prefill_branch_and_workspace(lib):
+    # s_q >= 256: decompress, K and V of 2 x 16 x 64 token slots x 128 heads x 128 bf16 each
+    expanded = 2 * 16 * 64 * 128 * 128 * 2
+    assert lib.mla_prefill_workspace_size(ctypes.byref(_pparams())) == 2 * expanded
+    # s_q < 256: the absorbed decode's workspace
+    d = _params(batch=2, s_q=100, max_blocks_per_seq=16, num_pages=64, num_splits=0)
+    assert lib.mla_prefill_workspace_size(ctypes.byref(_pparams(s_q=100))) == lib.mla_decode_workspace_size(
+        ctypes.byref(d), 1)
+    # forced absorption of a chunk longer than 256 is unsupported; forced decompression of a short one is fine
+    assert _prefill(lib, _pparams(mode=1)) == _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_prefill_workspace_size(ctypes.byref(_pparams(s_q=10, mode=2))) == 2 * expanded
+    # a lower threshold moves short chunks to decompression
+    assert lib.mla_prefill_workspace_size(ctypes.byref(_pparams(s_q=100, threshold=64))) == 2 * expanded
+    assert _prefill(lib, _pparams(), ws_bytes=2 * expanded - 1) == _lib.MLA_ERR_WORKSPACE
+    assert _prefill(lib, _pparams(), ptrs=(A, A, MIS, A, A, A, A, A, None)) == _lib.MLA_ERR_MISALIGNED
+    assert _prefill(lib, _pparams(), ptrs=(A, None, A, A, A, A, A, A, None)) == _lib.MLA_ERR_INVALID_ARG
+    assert _prefill(lib, _pparams(batch=0), ws=None, ws_bytes=0, ptrs=(None,) * 8 + (None,)) == _lib.MLA_OK

@@ -18,7 +18,7 @@ import pytest
 import oracle
 from synth import make_append_inputs, make_custom, make_inputs
 
-from ._gpu import assert_close, dev_bf16, dev_i32, host_bits, require_gpu
+from ._gpu import U, assert_bf16_match, assert_close, dev_bf16, dev_i32, host_bits, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -46,23 +46,6 @@ def _ordered(bits):
     b = bits.astype(np.int32)
     mag = b & 0x7FFF
     return np.where(b & 0x8000, -mag, mag)
-
-
-U = 2.0 ** -24
-
-
-def assert_bf16_match(got_bits, exact, err, what, max_frac=1e-2):
-    """|gpu - exact| <= err + 2^-8 (|exact| + err) everywhere; bits equal to RNE(exact) but for max_frac."""
-    ref_bits = oracle.f64_to_bf16_bits(exact)
-    assert got_bits.shape == ref_bits.shape
-    got = oracle.bf16_bits_to_f64(got_bits)
-    bound = err + 2.0 ** -8 * (np.abs(exact) + err)
-    over = np.abs(got - exact) > bound
-    assert not over.any(), f"{what}: {int(over.sum())} elements beyond the bound, worst excess " \
-        f"{float(np.max(np.abs(got - exact) - bound)):.3e}"
-    frac = float(np.count_nonzero(got_bits != ref_bits)) / max(got_bits.size, 1)
-    assert frac <= max_frac, f"{what}: {frac:.2%} of elements differ from the rounded oracle"
-    return frac
 
 
 def rotation_err(a, b, cos, sin):
