@@ -208,6 +208,85 @@ def run_append(inp, pool_dev, torch, mla, steps, warmup):
     }
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def prefill_flops(B, L, M):
+    """Algorithmic flops of a decompress-branch prefill chunk (M queries over L cached tokens
+    per sequence): the K and V expansion of every cached token (2 x 512 x 128 per head and
+    tensor) and the causal attention (192-wide scores plus 128-wide P.V per visible key)."""
+    expand = 2 * B * L * 512 * 128 * 128 * 2
+    visible = sum(L - M + i + 1 for i in range(M))
+    attn = B * 128 * visible * (192 + 128) * 2
+    return expand, attn
+
+
+def run_prefill(torch, mla, steps, warmup):
+    """Prefill of an 8 x 4096-token prompt in one chunk (M = L = 4096, decompress branch),
+    timed per kernel with the library's HIP events; then absorbed vs decompressed time for
+    shorter chunks at the end of the same 4096-token sequences (the threshold check)."""
+    from synth import make_custom
+    B, L = 8, 4096
+    base = make_custom(102, B, 1, [L] * B)
+    pool = _dev_bf16(base.pool, torch)
+    bt, sl = _dev_i32(base.block_table, torch), _dev_i32(base.seqlens, torch)
+    w_uk, w_uv = _dev_bf16(base.w_uk, torch), _dev_bf16(base.w_uv, torch)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(103)
+
+    def inputs(M):
+        q_c = torch.randn((B, M, 128, 128), device="cuda", generator=g).to(torch.bfloat16)
+        q_r = torch.randn((B, M, 128, 64), device="cuda", generator=g).to(torch.bfloat16)
+        return q_c, q_r
+
+    def timed(M, mode, n, w):
+        q_c, q_r = inputs(M)
+        params = mla.make_prefill_params(B, M, base.max_blocks, base.num_pages, base.scale, mode)
+        ws = torch.empty(mla.prefill_workspace_size(params), dtype=torch.uint8, device="cuda")
+        out = torch.empty(B, M, 128, 128, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(B, M, 128, dtype=torch.float32, device="cuda")
+
+        def call():
+            mla.prefill(q_c, q_r, w_uk, w_uv, pool, bt, sl, scale=base.scale, mode=mode, out=out, lse=lse,
+                        workspace=ws)
+        for _ in range(w):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with mla.KernelTimer() as kt:
+            e0.record()
+            for _ in range(n):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+        per = {k: v / max(kt.prefill_calls, 1) for k, v in kt.prefill_ms.items()}
+        return e0.elapsed_time(e1) / n, per
+
+    ms, per = timed(L, 0, steps, warmup)
+    expand, attn = prefill_flops(B, L, L)
+    achieved = attn / (per["attention"] * 1e-3) / 1e12
+    cross = {}
+    for M in (64, 128, 256):
+        a_ms, _ = timed(M, 1, max(steps // 2, 3), 2)
+        d_ms, _ = timed(M, 2, max(steps // 2, 3), 2)
+        cross[str(M)] = {"absorbed_us": round(a_ms * 1e3, 1), "decompressed_us": round(d_ms * 1e3, 1)}
+    return {
+        "workload": "prefill chunk, 8 sequences x 4096-token prompt (M = L = 4096, all rows cached), "
+                    "128 heads, decompress branch (K/V expansion + causal attention), bf16",
+        "us_per_call": round(ms * 1e3, 1),
+        "kernels_us": {k: round(v * 1e3, 1) for k, v in per.items()},
+        "tokens_per_s": round(B * L / (ms * 1e-3), 1),
+        "tflops": {"expand": round(expand / (per["decompress"] * 1e-3) / 1e12, 1),
+                   "attention": round(achieved, 1),
+                   "whole_call": round((expand + attn) / (ms * 1e-3) / 1e12, 1)},
+        "algorithmic_flops": {"expand": expand, "attention": attn},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_attention_kernel", "algorithmic_flops_per_launch": attn},
+        "absorb_vs_decompress_at_L4096": cross,
+    }
+
+
 def cpu_baseline(inp, seconds):
     """The fp64 oracle (absorbed form), timed on host cores on a bounded sample
     of the same workload's sequences."""
@@ -239,6 +318,7 @@ def main():
                     help="comma list of other workloads timed for the report (c1,c2,c3max,c4,c5 or none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill chunk leg")
     ap.add_argument("--pmc-run", action="store_true",
                     help="only run decode launches and the calibration copy (target of rocprofv3 --pmc passes)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -312,6 +392,11 @@ def main():
     app = run_append(inp, pool, torch, mla, args.steps, args.warmup)
     log(f"[bench] c3 append: {app}")
 
+    pre = None
+    if not args.no_prefill:
+        pre = run_prefill(torch, mla, max(args.steps // 5, 5), 2)
+        log(f"[bench] prefill: {pre}")
+
     cpu = None
     if not args.no_cpu:
         log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f}s ...")
@@ -351,6 +436,7 @@ def main():
         "cpu_baseline": cpu,
         "other_workloads": others,
         "cache_append": app,
+        "prefill": pre,
     }
     print(json.dumps(line), flush=True)
 

@@ -213,6 +213,7 @@ constexpr int kVPitch = kDimC * 2 + 32;  // 288 B: V tile rows [key][128], 8 ban
 constexpr int kKTile = kAKeys * kKPitch;
 constexpr int kVTile = kAKeys * kVPitch;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kDies = 8;                 // MI355X: 8 accelerator dies, each with its own L2
 
 struct AttnArgs {
   const uint16_t* q_c;      // [B, M, H, 128]
@@ -231,6 +232,17 @@ struct AttnArgs {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Uniform load through the scalar data cache (the block table is read-only here).
+__device__ __forceinline__ int ld_scalar(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // One workgroup per (128-query tile, head, sequence).  Wave w owns queries
 // i0 + 32 w .. +31.  Per 64-key tile (one page) it computes the transposed scores
 // S^T[key, query] = K_tile . Q^T (v_mfma_f32_32x32x16_bf16: 2 key blocks x 12 k-steps
@@ -241,10 +253,21 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // transposing LDS reads, B = the probabilities straight from the score registers,
 // with the keys of each MFMA k-slot ordered as the score layout holds them).
 // Key and value tiles are double-buffered in LDS, the next tile's loads in flight
-// during the current tile's MFMAs.
+// during the current tile's MFMAs.  VALU work per tile is kept small: the scale is
+// folded into the exponent's multiply-add, keys are masked only on tiles that
+// reach past some query of the wave, and O is rescaled only when a running
+// maximum of the wave actually grew.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void prefill_attention_kernel(AttnArgs a) {
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Workgroups go round-robin over the 8 dies.  Ordinal o counts die-major, so each
+  // die takes a contiguous run of (sequence, head) pairs with all their query tiles:
+  // those tiles stream the same K/V rows at about the same time through one L2.
+  // Within a pair the longest causal tiles come first.
+  const int n_qt = (a.M + kAQ - 1) / kAQ;
+  const int per_die = gridDim.x / kDies;
+  const int ord = (blockIdx.x % kDies) * per_die + blockIdx.x / kDies;
+  const int qt = n_qt - 1 - ord % n_qt;
+  const int h = (ord / n_qt) % kHeads, b = ord / (n_qt * kHeads);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = clamp_len(a.seqlens[b], a.max_blocks);
   const int i0 = qt * kAQ;
@@ -259,6 +282,7 @@ void prefill_attention_kernel(AttnArgs a) {
   const int qi = i0 + 32 * wave + (lane & 31);
   const bool q_ok = qi < a.M;
   const int qpos = L - a.M + qi;                       // keys t <= qpos are visible
+  const int wave_first_pos = L - a.M + i0 + 32 * wave; // smallest query position of the wave
   const int g2 = lane >> 5;
 
   // Q^T operand: k-step ks covers score dimensions 16 ks + 8 g2 .. +7.
@@ -273,40 +297,59 @@ void prefill_attention_kernel(AttnArgs a) {
     }
   }
 
-  // Tile loads: K part 64 rows x 24 chunks (16 from K_h, 8 from k_R), V part 64 x 16 chunks.
-  // Thread tid takes K chunks tid + 256 i (i < 6) and V chunks tid + 256 i (i < 4).
+  // Tile loads, as buffer loads whose per-lane byte offsets are fixed for the whole
+  // loop (only the scalar base moves with the tile; no address temporaries for the
+  // compiler to recycle while the loads are in flight).  Each buffer covers exactly
+  // the tile's rows inside the sequence, so rows past it read as zeros.
+  //   K_h: 64 rows x 16 chunks, 4 per thread; k_R: 64 rows x 8 chunks, 2 per thread;
+  //   V_h: 64 rows x 16 chunks, 4 per thread.
+  constexpr uint32_t kRowBytesKV = kHeads * kDimC * 2;   // 32 KiB between consecutive keys in K and V
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k) +
+                               ((size_t)b * a.max_len * kHeads + h) * kDimC * 2;
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v) +
+                               ((size_t)b * a.max_len * kHeads + h) * kDimC * 2;
+  uint32_t khoff[4], kroff[2], vvoff[4], khdst[4], krdst[2], vdst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i, r = c / 16, x = c % 16;
+    khoff[i] = r * kRowBytesKV + 16 * x;
+    khdst[i] = r * kKPitch + 16 * x;
+    vvoff[i] = r * kRowBytesKV + 16 * x;
+    vdst[i] = r * kVPitch + 16 * x;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i, r = c / 8, x = c % 8;
+    kroff[i] = r * kRowBytes + 16 * x;
+    krdst[i] = r * kKPitch + kDimC * 2 + 16 * x;
+  }
+  constexpr int kBufFlags = 0x00020000;
   u32x4 kreg[6], vreg[4];
-  auto load_tile = [&](int j) {
+  const int32_t* bt_row = a.bt + (size_t)b * a.max_blocks;
+  auto load_tile = [&](int j, int raw_page) {
     const int t0 = j * kAKeys;
-    int64_t page = a.bt[(size_t)b * a.max_blocks + j];
-    page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+    const int valid = min(kAKeys, L - t0);
+    const int64_t page = raw_page < 0 ? 0 : (raw_page >= a.num_pages ? a.num_pages - 1 : raw_page);
+    const __amdgpu_buffer_rsrc_t kb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (size_t)t0 * kRowBytesKV), (short)0, valid * (int)kRowBytesKV, kBufFlags);
+    const __amdgpu_buffer_rsrc_t vb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + (size_t)t0 * kRowBytesKV), (short)0, valid * (int)kRowBytesKV, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.kv + (size_t)page * kPage * kRow + kLatent), (short)0, valid * kRowBytes, kBufFlags);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int c = tid + 256 * i, r = c / 24, x = c % 24;
-      const int t = min(t0 + r, L - 1);                 // rows past the sequence: a finite, masked row
-      if (x < 16)
-        kreg[i] = *(const u32x4*)(a.k + (((size_t)b * a.max_len + t) * kHeads + h) * kDimC + 8 * x);
-      else
-        kreg[i] = *(const u32x4*)(a.kv + ((size_t)page * kPage + (t & (kPage - 1))) * kRow + kLatent + 8 * (x - 16));
-    }
+    for (int i = 0; i < 4; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(kb, khoff[i], 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, r = c / 16, x = c % 16;
-      const int t = min(t0 + r, L - 1);
-      vreg[i] = *(const u32x4*)(a.v + (((size_t)b * a.max_len + t) * kHeads + h) * kDimC + 8 * x);
-    }
+    for (int i = 0; i < 2; ++i) kreg[4 + i] = __builtin_amdgcn_raw_buffer_load_b128(rb, kroff[i], 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(vb, vvoff[i], 0, 0);
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int c = tid + 256 * i, r = c / 24, x = c % 24;
-      *(u32x4*)(kt[buf] + r * kKPitch + 16 * x) = kreg[i];
-    }
+    for (int i = 0; i < 4; ++i) *(u32x4*)(kt[buf] + khdst[i]) = kreg[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, r = c / 16, x = c % 16;
-      *(u32x4*)(vt[buf] + r * kVPitch + 16 * x) = vreg[i];
-    }
+    for (int i = 0; i < 2; ++i) *(u32x4*)(kt[buf] + krdst[i]) = kreg[4 + i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4*)(vt[buf] + vdst[i]) = vreg[i];
   };
 
   f32x16 o[4];
@@ -314,18 +357,27 @@ void prefill_attention_kernel(AttnArgs a) {
   for (int e = 0; e < 4; ++e)
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[e][j] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;                // in scaled log2 units
+  const float c1 = a.scale_log2;
 
+  // Page ids come through scalar loads, one tile ahead of the loads that use them.
+  int next_page = 0;
   if (n_tiles > 0) {
-    load_tile(0);
+    load_tile(0, ld_scalar(bt_row));
     store_tile(0);
+    if (n_tiles > 1) next_page = ld_scalar(bt_row + 1);
   }
+  // Every load issued so far (queries, first tile) completes here: otherwise the
+  // loop's wait counts, merged with this entry state, would make each tile wait for
+  // the next tile's loads before its first MFMA.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
   for (int j = 0; j < n_tiles; ++j) {
     const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
+    if (j + 1 < n_tiles) load_tile(j + 1, next_page);
     const unsigned char* K = kt[buf];
     const unsigned char* V = vt[buf];
+    const int t0 = j * kAKeys;
 
     // S^T for key blocks mb = 0, 1: lane l, register r -> key 32 mb + 8 (r / 4) + 4 g2 + r % 4.
     f32x16 s[2];
@@ -340,43 +392,53 @@ void prefill_attention_kernel(AttnArgs a) {
       }
     }
 
-    // Online softmax (base 2) of this lane's query over the tile's keys.
-    const int t0 = j * kAKeys;
-    float mt = -INFINITY;
+    // Mask only where some key of the tile lies past some query of the wave.
+    if (t0 + kAKeys - 1 > wave_first_pos) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = t0 + 32 * mb + 8 * (r >> 2) + 4 * g2 + (r & 3);
-        float x = s[mb][r] * a.scale_log2;
-        x = key <= qpos ? x : -INFINITY;
-        s[mb][r] = x;
-        mt = fmaxf(mt, x);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+        for (int r = 0; r < 16; ++r) {
+          const int key = t0 + 32 * mb + 8 * (r >> 2) + 4 * g2 + (r & 3);
+          s[mb][r] = key <= qpos ? s[mb][r] : -INFINITY;
+        }
+    }
+    // Tile maximum of the raw scores (the scale is positive), then in scaled log2 units.
+    float mt = max3f(s[0][0], s[0][1], s[0][2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) mt = max3f(mt, s[0][r], s[0][r + 1]);
+    mt = max3f(mt, s[0][15], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 15; r += 2) mt = max3f(mt, s[1][r], s[1][r + 1]);
+    mt = fmaxf(mt, s[1][15]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c1;
     const float m_new = fmaxf(m_run, mt);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    // Rescale O and l only when a running maximum of the wave grew.
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float alpha = fast_exp2(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[e][r] *= alpha;
+    }
+    m_run = m_new;
     float ps = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(s[mb][r] - m_use);
+        const float p = fast_exp2(__builtin_fmaf(s[mb][r], c1, -m_use));
         s[mb][r] = p;
         ps += p;
       }
     ps += __shfl_xor(ps, 32);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[e][r] *= alpha;
+    l_run += ps;
 
     // O^T += V^T . P^T.  k-step ks = (key block mb = ks / 2, half hf = ks % 2): slot i of
     // lane group g2 holds key 32 mb + 16 hf + 8 (i / 4) + 4 g2 + i % 4, i.e. score register
     // 8 hf + i.  The V^T operand gathers the same keys: two transposing reads of 4 rows.
+    const int grp = (lane >> 4) & 1, sl = lane & 15;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int mb = ks >> 1, hf = ks & 1;
@@ -387,7 +449,6 @@ void prefill_attention_kernel(AttnArgs a) {
         pop[2 * i] = (short)(w2 & 0xFFFFu);
         pop[2 * i + 1] = (short)(w2 >> 16);
       }
-      const int grp = (lane >> 4) & 1, sl = lane & 15;
       const int row = 32 * mb + 16 * hf + 4 * g2 + (sl >> 2);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -399,6 +460,8 @@ void prefill_attention_kernel(AttnArgs a) {
       }
     }
 
+    // the page id two tiles ahead: its scalar load completes under the barrier
+    if (j + 2 < n_tiles) next_page = ld_scalar(bt_row + j + 2);
     if (j + 1 < n_tiles) store_tile(buf ^ 1);
     __syncthreads();
   }
@@ -442,7 +505,8 @@ hipError_t launch_prefill_attention(const uint16_t* q_c, const uint16_t* q_r, co
   a.max_blocks = max_blocks;
   a.max_len = max_len;
   a.scale_log2 = scale * kLog2e;
-  hipLaunchKernelGGL(prefill_attention_kernel, dim3((M + kAQ - 1) / kAQ, kHeads, batch), dim3(256), 0, s, a);
+  // n_qt x 128 heads x batch workgroups: a multiple of the 8 dies since 128 is.
+  hipLaunchKernelGGL(prefill_attention_kernel, dim3((M + kAQ - 1) / kAQ * kHeads * batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
