@@ -232,6 +232,26 @@ struct AttnArgs {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// v_mfma_f32_32x32x16_bf16 with the accumulator in VGPRs (inline asm: a compiler-
+// selected MFMA takes the AGPR form here and every VALU use of its result then costs
+// a copy).  Hazards the asm covers itself: a leading s_nop separates a VALU write of
+// an operand (or of the accumulator) from the MFMA's read; chains accumulate in place;
+// the last MFMA of a chain carries 14 wait states, more than the 12 an 8-pass XDL
+// result needs before a VALU read.
+template <bool kZero, bool kLast>
+__device__ __forceinline__ void mfma_v(f32x16& acc, const s16x8& a, const s16x8& b) {
+  if constexpr (kZero && kLast)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\ts_nop 7\n\ts_nop 5"
+                 : "=v"(acc) : "v"(a), "v"(b));
+  else if constexpr (kZero)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+  else if constexpr (kLast)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 5"
+                 : "+v"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
 // Uniform load through the scalar data cache (the block table is read-only here).
 __device__ __forceinline__ int ld_scalar(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)p;
@@ -380,15 +400,26 @@ void prefill_attention_kernel(AttnArgs a) {
     const int t0 = j * kAKeys;
 
     // S^T for key blocks mb = 0, 1: lane l, register r -> key 32 mb + 8 (r / 4) + 4 g2 + r % 4.
+    // The 24 MFMAs run as one sequence (key block 0, then 1); each key-row operand is
+    // read from LDS two MFMAs ahead of its use (the asm statements keep program order,
+    // so the prefetch is written out).
     f32x16 s[2];
+    {
+      constexpr int kSteps = kAD / 16;
+      const unsigned char* krow = K + (lane & 31) * kKPitch + 16 * g2;
+      auto kread = [&](int n) {     // operand of MFMA n = (mb = n / 12, ks = n % 12)
+        return *(const s16x8*)(krow + (n / kSteps) * 32 * kKPitch + (n % kSteps) * 32);
+      };
+      s16x8 kop[3];
+      kop[0] = kread(0);
+      kop[1] = kread(1);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < kAD / 16; ++ks) {
-        const s16x8 kop = *(const s16x8*)(K + (32 * mb + (lane & 31)) * kKPitch + (16 * ks + 8 * g2) * 2);
-        s[mb] = mfma32(kop, qop[ks], s[mb]);
+      for (int n = 0; n < 2 * kSteps; ++n) {
+        if (n + 2 < 2 * kSteps) kop[(n + 2) % 3] = kread(n + 2);
+        const int mb = n / kSteps, ks = n % kSteps;
+        if (ks == 0) mfma_v<true, false>(s[mb], kop[n % 3], qop[ks]);
+        else if (ks == kSteps - 1) mfma_v<false, true>(s[mb], kop[n % 3], qop[ks]);
+        else mfma_v<false, false>(s[mb], kop[n % 3], qop[ks]);
       }
     }
 
@@ -439,25 +470,35 @@ void prefill_attention_kernel(AttnArgs a) {
     // lane group g2 holds key 32 mb + 16 hf + 8 (i / 4) + 4 g2 + i % 4, i.e. score register
     // 8 hf + i.  The V^T operand gathers the same keys: two transposing reads of 4 rows.
     const int grp = (lane >> 4) & 1, sl = lane & 15;
+    // V^T operand of MFMA n = (ks = n / 4, e = n % 4): rows 32 mb + 16 hf + 4 g2 + s / 4
+    // (+8 for the second read), columns 32 e + 16 grp + 4 (s % 4); read one MFMA ahead.
+    const unsigned char* vrow = V + (4 * g2 + (sl >> 2)) * kVPitch + (16 * grp + 4 * (sl & 3)) * 2;
+    auto vread = [&](int n) {
+      const int ks = n >> 2, e = n & 3;
+      const unsigned char* p = vrow + (16 * ks) * kVPitch + 64 * e;
+      const s16x4 lo = lds_read_tr4(p);
+      const s16x4 hi = lds_read_tr4(p + 8 * kVPitch);
+      return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    s16x8 pops[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int mb = ks >> 1, hf = ks & 1;
-      s16x8 pop;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t w2 = pack_bf16x2(s[mb][8 * hf + 2 * i], s[mb][8 * hf + 2 * i + 1]);
-        pop[2 * i] = (short)(w2 & 0xFFFFu);
-        pop[2 * i + 1] = (short)(w2 >> 16);
+        pops[ks][2 * i] = (short)(w2 & 0xFFFFu);
+        pops[ks][2 * i + 1] = (short)(w2 >> 16);
       }
-      const int row = 32 * mb + 16 * hf + 4 * g2 + (sl >> 2);
+    }
+    s16x8 vop[2];
+    vop[0] = vread(0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned char* p = V + row * kVPitch + (32 * e + 16 * grp + 4 * (sl & 3)) * 2;
-        const s16x4 lo = lds_read_tr4(p);
-        const s16x4 hi = lds_read_tr4(p + 8 * kVPitch);
-        const s16x8 vop = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[e] = mfma32(vop, pop, o[e]);
-      }
+    for (int n = 0; n < 16; ++n) {
+      if (n + 1 < 16) vop[(n + 1) & 1] = vread(n + 1);
+      const int ks = n >> 2, e = n & 3;
+      if (ks == 3) mfma_v<false, true>(o[e], vop[n & 1], pops[ks]);
+      else mfma_v<false, false>(o[e], vop[n & 1], pops[ks]);
     }
 
     // the page id two tiles ahead: its scalar load completes under the barrier
