@@ -123,6 +123,9 @@ void decompress_kernel(DecompArgs a) {
     for (int i = 0; i < 4; ++i) *(u32x4*)wdst[i] = wv[i];
     __syncthreads();
     if (kc + 1 < kLatent / kDK) load_chunk(kc + 1);
+    // keep the next chunk's loads ahead of this chunk's MFMAs (the scheduler would sink
+    // them to their use, exposing the whole memory latency once per chunk)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < kDK / 16; ++ks) {
       s16x8 bop[2];
@@ -272,12 +275,12 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // O^T[e, query] += V^T . P^T (4 column blocks x 4 k-steps; A = V columns through
 // transposing LDS reads, B = the probabilities straight from the score registers,
 // with the keys of each MFMA k-slot ordered as the score layout holds them).
-// Key and value tiles are double-buffered in LDS, the next tile's loads in flight
-// during the current tile's MFMAs.  VALU work per tile is kept small: the scale is
+// The next tile's loads are in flight in registers during the current tile's MFMAs
+// and go to LDS between two barriers.  VALU work per tile is kept small: the scale is
 // folded into the exponent's multiply-add, keys are masked only on tiles that
 // reach past some query of the wave, and O is rescaled only when a running
 // maximum of the wave actually grew.
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void prefill_attention_kernel(AttnArgs a) {
   // Workgroups go round-robin over the 8 dies.  Ordinal o counts die-major, so each
   // die takes a contiguous run of (sequence, head) pairs with all their query tiles:
@@ -295,8 +298,10 @@ void prefill_attention_kernel(AttnArgs a) {
   const int p_last = L - a.M + last_q;                 // position of the tile's last query
   const int n_tiles = p_last >= 0 ? p_last / kAKeys + 1 : 0;
 
-  __shared__ __attribute__((aligned(16))) unsigned char kt[2][kKTile];
-  __shared__ __attribute__((aligned(16))) unsigned char vt[2][kVTile];
+  // One LDS tile (44 KiB) so that two workgroups share a compute unit: while one
+  // waits at a barrier or for its next tile, the other's MFMAs run.
+  __shared__ __attribute__((aligned(16))) unsigned char kt[1][kKTile];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[1][kVTile];
 
   // This lane's query: i0 + 32 wave + lane % 32 (lanes l and l ^ 32 share it).
   const int qi = i0 + 32 * wave + (lane & 31);
@@ -393,7 +398,7 @@ void prefill_attention_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
   for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
+    const int buf = 0;
     if (j + 1 < n_tiles) load_tile(j + 1, next_page);
     const unsigned char* K = kt[buf];
     const unsigned char* V = vt[buf];
@@ -503,7 +508,8 @@ void prefill_attention_kernel(AttnArgs a) {
 
     // the page id two tiles ahead: its scalar load completes under the barrier
     if (j + 2 < n_tiles) next_page = ld_scalar(bt_row + j + 2);
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+    if (j + 1 < n_tiles) store_tile(0);
     __syncthreads();
   }
 
