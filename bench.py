@@ -30,8 +30,21 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 ROW_BYTES = 1152               # one cached token of one layer: 576 bf16
 COPY_BYTES = 512 << 20         # device copy of known size that calibrates the HBM byte counters
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_c3_b64_traffic.md")
-KERNEL_SOURCES = ("mla_latent_kv_04_amd/csrc/decode.hip", "mla_latent_kv_04_amd/csrc/common.h")
+# Counter summaries (HBM bytes per launch): one per measured kernel family, each keyed
+# by a hash of the sources its kernels are built from.
+_CSRC = "mla_latent_kv_04_amd/csrc/"
+TRAFFIC = {
+    "decode": dict(file="decode_kernel_c3_b64_traffic.md", kernels=("decode_kernel",),
+                   sources=(_CSRC + "decode.hip", _CSRC + "common.h"),
+                   title="decode_kernel: paged MLA decode, batch 64, seq_len U[1024,32768]"),
+    "append": dict(file="append_kernel_c3_b64_traffic.md", kernels=("append_kernel", "append_finalize_kernel"),
+                   sources=(_CSRC + "append.hip", _CSRC + "append.h", _CSRC + "common.h"),
+                   title="cache append: 64 new tokens of the batch-64 workload, d = 7168 (both kernels of a call)"),
+    "prefill": dict(file="prefill_attention_b8_4096_traffic.md", kernels=("prefill_attention_kernel",),
+                    sources=(_CSRC + "prefill.hip", _CSRC + "prefill.h", _CSRC + "common.h"),
+                    title="prefill_attention_kernel: 8 sequences x 4096-token prompt, one chunk"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", TRAFFIC["decode"]["file"])
 
 
 def log(*a):
@@ -191,6 +204,7 @@ def run_append(inp, pool_dev, torch, mla, steps, warmup):
     alg = append_algorithmic_bytes(T)
     proj_alg = D_MODEL * 576 * 2 + T * D_MODEL * 2          # W_A and x: what the projection kernel must read
     achieved = alg / (graph_ms * 1e-3) / 1e9
+    traffic = load_traffic("append")
     return {
         "workload": f"{T} new tokens (one per sequence of the batch-64 workload), d={D_MODEL}, "
                     "W_A [7168, 576] bf16, fp32 RoPE table of 131072 rows, rows written into the shared pool",
@@ -201,7 +215,9 @@ def run_append(inp, pool_dev, torch, mla, steps, warmup):
         "host_bound_us_per_call": {"append": round(app_ms * 1e3, 2), "append_with_q": round(appq_ms * 1e3, 2),
                                    "rope_q_alone": round(rope_ms * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic["fetch"] + traffic["write"]),
+                     "traffic_split": traffic,
                      "kernel": "append_kernel<32> + append_finalize_kernel (one call, graph-replayed)",
                      "algorithmic_bytes_per_launch": alg},
         "projection_algorithmic_bytes": proj_alg,
@@ -263,6 +279,7 @@ def run_prefill(torch, mla, steps, warmup):
         return e0.elapsed_time(e1) / n, per
 
     ms, per = timed(L, 0, steps, warmup)
+    traffic = load_traffic("prefill")
     expand, attn = prefill_flops(B, L, L)
     achieved = attn / (per["attention"] * 1e-3) / 1e12
     cross = {}
@@ -281,7 +298,9 @@ def run_prefill(torch, mla, steps, warmup):
                    "whole_call": round((expand + attn) / (ms * 1e-3) / 1e12, 1)},
         "algorithmic_flops": {"expand": expand, "attention": attn},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None if traffic is None else round(traffic["fetch"] + traffic["write"]),
+                     "traffic_split": traffic,
                      "kernel": "prefill_attention_kernel", "algorithmic_flops_per_launch": attn},
         "absorb_vs_decompress_at_L4096": cross,
     }
@@ -319,15 +338,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill chunk leg")
-    ap.add_argument("--pmc-run", action="store_true",
-                    help="only run decode launches and the calibration copy (target of rocprofv3 --pmc passes)")
+    ap.add_argument("--pmc-run", nargs="?", const="decode", default=None, choices=sorted(TRAFFIC),
+                    help="only run launches of one kernel family (default decode) and the calibration copy "
+                         "(target of rocprofv3 --pmc passes)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from the FETCH_SIZE and WRITE_SIZE pass output folders")
+    ap.add_argument("--pmc-kind", default="decode", choices=sorted(TRAFFIC),
+                    help="kernel family of --summarize-pmc")
     ap.add_argument("--pmc-command", action="append", default=[],
                     help="command lines recorded in the traffic summary (repeatable)")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, args.pmc_command)
+        summarize_pmc(*args.summarize_pmc, args.pmc_command, args.pmc_kind)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -335,7 +357,7 @@ def main():
         sys.exit(2)
 
     if args.pmc_run:
-        pmc_run(args.steps, args.warmup)
+        pmc_run(args.steps, args.warmup, args.pmc_run)
         return
 
     import torch
@@ -441,51 +463,79 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def kernel_source_hash():
-    """sha256 over the sources the decode kernel is compiled from: counter readings
-    taken with other sources do not describe the kernel being timed."""
+def kernel_source_hash(kind="decode"):
+    """sha256 over the sources a kernel family is compiled from: counter readings taken
+    with other sources do not describe the kernels being timed."""
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in TRAFFIC[kind]["sources"]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def load_traffic():
-    """HBM bytes per decode launch from the committed counter summary, or None when
-    it is missing or was taken on other kernel sources."""
+def load_traffic(kind="decode"):
+    """HBM bytes per launch (or per call, for the append) from the committed counter
+    summary, or None when it is missing or was taken on other kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", TRAFFIC[kind]["file"])) as f:
             kv = dict(line.split(":", 1) for line in f if line.startswith(("source_sha256:", "fetch_bytes_per_launch:",
                                                                              "write_bytes_per_launch:")))
     except OSError:
         return None
-    if kv.get("source_sha256", "").strip() != kernel_source_hash():
+    if kv.get("source_sha256", "").strip() != kernel_source_hash(kind):
         return None
     return {"fetch": float(kv["fetch_bytes_per_launch"]), "write": float(kv["write_bytes_per_launch"])}
 
 
-def pmc_run(steps, warmup):
-    """Workload for the rocprofv3 --pmc passes: `warmup + steps` paged decode launches
-    on the batch-64 workload, then one device copy of COPY_BYTES bytes whose counter
-    readings calibrate the decode kernel's."""
-    import torch
-    import mla_latent_kv_04_amd as mla
-    inp = _workload_from_synth("c3", torch, with_host_pool=False)
-    pool = _device_pool(inp.num_pages, inp.seed, torch)
-    qa = torch.randn((inp.batch, 1, 128, 512), device="cuda").to(torch.bfloat16)
-    qr = torch.randn((inp.batch, 1, 128, 64), device="cuda").to(torch.bfloat16)
-    bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
-    for _ in range(warmup + steps):
-        mla.decode_paged(qa, qr, pool, bt, sl, scale=inp.scale)
-    torch.cuda.synchronize()
+def _copy_for_calibration(torch):
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"[bench] pmc run: {warmup + steps} decode launches, copy of {COPY_BYTES} B")
+
+
+def pmc_run(steps, warmup, kind="decode"):
+    """Workload for the rocprofv3 --pmc passes: `warmup + steps` launches of one kernel
+    family (decode: the batch-64 paged decode; append: the 64-token cache append;
+    prefill: the 8 x 4096-token prompt), then one device copy of COPY_BYTES bytes whose
+    counter readings calibrate the kernels'."""
+    import torch
+    import mla_latent_kv_04_amd as mla
+    if kind == "decode":
+        inp = _workload_from_synth("c3", torch, with_host_pool=False)
+        pool = _device_pool(inp.num_pages, inp.seed, torch)
+        qa = torch.randn((inp.batch, 1, 128, 512), device="cuda").to(torch.bfloat16)
+        qr = torch.randn((inp.batch, 1, 128, 64), device="cuda").to(torch.bfloat16)
+        bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
+        for _ in range(warmup + steps):
+            mla.decode_paged(qa, qr, pool, bt, sl, scale=inp.scale)
+    elif kind == "append":
+        from synth import make_append_inputs
+        inp = _workload_from_synth("c3", torch, with_host_pool=False)
+        pool = _device_pool(inp.num_pages, inp.seed, torch)
+        x_bits, w_bits = make_append_inputs(80, inp.batch, inp.s_q)
+        x, w_a = _dev_bf16(x_bits, torch), _dev_bf16(w_bits, torch)
+        table = mla.rope_table(131072)
+        bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
+        for _ in range(warmup + steps):
+            mla.append_kv(x, w_a, table, pool, bt, sl)
+    elif kind == "prefill":
+        from synth import make_custom
+        B, L = 8, 4096
+        base = make_custom(102, B, 1, [L] * B)
+        q_c = torch.randn((B, L, 128, 128), device="cuda").to(torch.bfloat16)
+        q_r = torch.randn((B, L, 128, 64), device="cuda").to(torch.bfloat16)
+        args = (q_c, q_r, _dev_bf16(base.w_uk, torch), _dev_bf16(base.w_uv, torch), _dev_bf16(base.pool, torch),
+                _dev_i32(base.block_table, torch), _dev_i32(base.seqlens, torch))
+        for _ in range(warmup + steps):
+            mla.prefill(*args, scale=base.scale)
+    else:
+        raise SystemExit(f"unknown --pmc-run kind {kind!r}")
+    torch.cuda.synchronize()
+    _copy_for_calibration(torch)
+    log(f"[bench] pmc run ({kind}): {warmup + steps} calls, copy of {COPY_BYTES} B")
 
 
 def _pmc_per_dispatch(run_dir, counter):
@@ -502,49 +552,78 @@ def _pmc_per_dispatch(run_dir, counter):
     return {k: list(v.values()) for k, v in vals.items()}
 
 
-def summarize_pmc(fetch_dir, write_dir, command):
-    """Writes the traffic summary: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the
-    decode kernel, each scaled by COPY_BYTES over what the same counter reads for the
-    copy (the copy fetches and writes COPY_BYTES exactly)."""
+def _prefill_algorithmic_bytes():
+    """HBM bytes the prefill attention kernel must move once (8 x 4096 tokens, 128 heads):
+    expanded K and V read, q_c and q_R read, the output and lse written, k_R read."""
+    B, L, M = 8, 4096, 4096
+    return (2 * B * L * 128 * 128 * 2 + B * M * 128 * 192 * 2 + B * M * 128 * 128 * 2 + B * M * 128 * 4
+            + B * L * 64 * 2)
+
+
+def summarize_pmc(fetch_dir, write_dir, command, kind="decode"):
+    """Writes the traffic summary of a kernel family: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of its kernels, each scaled by COPY_BYTES over what the same counter reads
+    for the copy (the copy fetches and writes COPY_BYTES exactly).  For a family of two
+    kernels per call (the append) the per-call bytes are the sum of their averages."""
+    t = TRAFFIC[kind]
     out = {}
+    per_kernel = {}
     for name, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _pmc_per_dispatch(run_dir, name)
-        dec = [v for k, vs in per.items() if "decode_kernel" in k for v in vs]
-        cop = [v for k, vs in per.items() if "decode_kernel" not in k and "copy" in k.lower() for v in vs]
-        if not dec or not cop:
-            raise SystemExit(f"summarize-pmc: no decode or copy dispatches with {name} in {run_dir}: {list(per)}")
+        # the calibration copy is the runtime's blit kernel (torch's dtype conversions are "copy" kernels too)
+        cop = [v for k, vs in per.items() if "rocclr_copyBuffer" in k for v in vs]
+        if not cop:
+            raise SystemExit(f"summarize-pmc: no copy dispatches with {name} in {run_dir}: {list(per)}")
         cop_kib = max(cop)
         factor = COPY_BYTES / (cop_kib * 1024.0)
-        dec_kib = sum(dec[1:]) / max(len(dec) - 1, 1) if len(dec) > 1 else dec[0]   # first launch is cold
-        out[name] = {"decode_kib": dec_kib, "copy_kib": cop_kib, "factor": factor, "bytes": dec_kib * 1024.0 * factor,
-                     "dispatches": len(dec)}
-    alg = 1166687 * ROW_BYTES
+        total = 0.0
+        for kern in t["kernels"]:
+            vals = [v for k, vs in per.items() if (kern + "(" in k or kern + "<" in k) for v in vs]
+            if not vals:
+                raise SystemExit(f"summarize-pmc: no {kern} dispatches with {name} in {run_dir}: {list(per)}")
+            kib = sum(vals[1:]) / max(len(vals) - 1, 1) if len(vals) > 1 else vals[0]   # first launch is cold
+            per_kernel.setdefault(kern, {})[name] = (kib, len(vals))
+            total += kib
+        out[name] = {"kib": total, "copy_kib": cop_kib, "factor": factor, "bytes": total * 1024.0 * factor}
+    if kind == "decode":
+        alg, alg_note = 1166687 * ROW_BYTES, "cache rows read once"
+    elif kind == "append":
+        alg, alg_note = append_algorithmic_bytes(64), "W_A, x, rows written, table rows, table entries and lengths"
+    else:
+        alg, alg_note = _prefill_algorithmic_bytes(), "expanded K and V, q_c and q_R read once, output and lse written"
     fetch, write = out["FETCH_SIZE"]["bytes"], out["WRITE_SIZE"]["bytes"]
     lines = [
-        "# HBM traffic of decode_kernel: paged MLA decode, batch 64, seq_len U[1024,32768]",
+        f"# HBM traffic of {t['title']}",
         "",
-        "Two rocprofv3 counter passes over `python3 bench.py --pmc-run` (decode launches, then a",
+        f"Two rocprofv3 counter passes over `python3 bench.py --pmc-run {kind}` ({kind} calls, then a",
         f"device copy of {COPY_BYTES} B that calibrates the counters), run from /tmp:",
         "",
         "```",
         *command,
         "```",
         "",
-        "| counter | decode KiB/dispatch | copy KiB | calibration (copy bytes / copy reading) | decode bytes/launch |",
+        "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | dispatches |",
+        "|---|---|---|---|",
+        *[f"| {k} | {v['FETCH_SIZE'][0]:.0f} | {v['WRITE_SIZE'][0]:.0f} | {v['FETCH_SIZE'][1]} |"
+          for k, v in per_kernel.items()],
+        "",
+        "| counter | KiB per launch | copy KiB | calibration (copy bytes / copy reading) | bytes per launch |",
         "|---|---|---|---|---|",
-        *[f"| {n} | {v['decode_kib']:.0f} | {v['copy_kib']:.0f} | {v['factor']:.4f} | {v['bytes']:.0f} |"
+        *[f"| {n} | {v['kib']:.0f} | {v['copy_kib']:.0f} | {v['factor']:.4f} | {v['bytes']:.0f} |"
           for n, v in out.items()],
         "",
-        f"Algorithmic bytes per launch (cache rows read once): {alg}; fetched / algorithmic = {fetch / alg:.4f}.",
+        f"Algorithmic bytes per launch ({alg_note}): {alg}; fetched / algorithmic = {fetch / alg:.4f};"
+        f" fetched + written / algorithmic = {(fetch + write) / alg:.4f}.",
         "",
-        f"source_sha256: {kernel_source_hash()}",
+        f"source_sha256: {kernel_source_hash(kind)}",
         f"fetch_bytes_per_launch: {fetch:.0f}",
         f"write_bytes_per_launch: {write:.0f}",
         "",
     ]
-    with open(TRAFFIC_FILE, "w") as f:
+    path = os.path.join(ROOT, "profiles", t["file"])
+    with open(path, "w") as f:
         f.write("\n".join(lines))
-    log(f"[bench] wrote {TRAFFIC_FILE}: fetch {fetch:.0f} B, write {write:.0f} B per launch")
+    log(f"[bench] wrote {path}: fetch {fetch:.0f} B, write {write:.0f} B per launch")
 
 
 def device_cus(mla):
