@@ -208,7 +208,7 @@ namespace {
 
 // ------------------------------------------------------------------ attention
 
-constexpr int kAQ = 128;                 // queries per workgroup (4 waves x 32)
+constexpr int kAQW = 32;                 // queries per wave
 constexpr int kAKeys = 64;               // keys per tile (one page)
 constexpr int kAD = kDimC + kRope;       // 192: score dimension
 constexpr int kKPitch = kAD * 2 + 16;    // 400 B: K tile rows [key][192]
@@ -217,6 +217,12 @@ constexpr int kKTile = kAKeys * kKPitch;
 constexpr int kVTile = kAKeys * kVPitch;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kDies = 8;                 // MI355X: 8 accelerator dies, each with its own L2
+// Attention workgroup shape: waves (32 queries each) and LDS tile buffers.
+constexpr int kAttnWaves = 8;
+constexpr int kAttnBufs = 2;
+// LDS operand reads issued this many MFMAs ahead of their use (key rows; value columns).
+constexpr int kKeyAhead = 4;
+constexpr int kValueAhead = 3;
 
 struct AttnArgs {
   const uint16_t* q_c;      // [B, M, H, 128]
@@ -280,8 +286,12 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // folded into the exponent's multiply-add, keys are masked only on tiles that
 // reach past some query of the wave, and O is rescaled only when a running
 // maximum of the wave actually grew.
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+template <int kW, int kBufs>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kW, 64 * kW), amdgpu_waves_per_eu(2, 2)))
 void prefill_attention_kernel(AttnArgs a) {
+  constexpr int kAQ = kAQW * kW;           // queries per workgroup
+  constexpr int kT = 64 * kW;              // threads
+  constexpr int kKH = 1024 / kT, kKR = 512 / kT, kVC = 1024 / kT;   // tile chunks per thread
   // Workgroups go round-robin over the 8 dies.  Ordinal o counts die-major, so each
   // die takes a contiguous run of (sequence, head) pairs with all their query tiles:
   // those tiles stream the same K/V rows at about the same time through one L2.
@@ -300,8 +310,8 @@ void prefill_attention_kernel(AttnArgs a) {
 
   // One LDS tile (44 KiB) so that two workgroups share a compute unit: while one
   // waits at a barrier or for its next tile, the other's MFMAs run.
-  __shared__ __attribute__((aligned(16))) unsigned char kt[1][kKTile];
-  __shared__ __attribute__((aligned(16))) unsigned char vt[1][kVTile];
+  __shared__ __attribute__((aligned(16))) unsigned char kt[kBufs][kKTile];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[kBufs][kVTile];
 
   // This lane's query: i0 + 32 wave + lane % 32 (lanes l and l ^ 32 share it).
   const int qi = i0 + 32 * wave + (lane & 31);
@@ -333,23 +343,24 @@ void prefill_attention_kernel(AttnArgs a) {
                                ((size_t)b * a.max_len * kHeads + h) * kDimC * 2;
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v) +
                                ((size_t)b * a.max_len * kHeads + h) * kDimC * 2;
-  uint32_t khoff[4], kroff[2], vvoff[4], khdst[4], krdst[2], vdst[4];
+  uint32_t khoff[kKH], kroff[kKR], vvoff[kVC], khdst[kKH], krdst[kKR], vdst[kVC];
+  static_assert(kKH == kVC, "K and V chunks share the loop below");
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, r = c / 16, x = c % 16;
+  for (int i = 0; i < kKH; ++i) {
+    const int c = tid + kT * i, r = c / 16, x = c % 16;
     khoff[i] = r * kRowBytesKV + 16 * x;
     khdst[i] = r * kKPitch + 16 * x;
     vvoff[i] = r * kRowBytesKV + 16 * x;
     vdst[i] = r * kVPitch + 16 * x;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i, r = c / 8, x = c % 8;
+  for (int i = 0; i < kKR; ++i) {
+    const int c = tid + kT * i, r = c / 8, x = c % 8;
     kroff[i] = r * kRowBytes + 16 * x;
     krdst[i] = r * kKPitch + kDimC * 2 + 16 * x;
   }
   constexpr int kBufFlags = 0x00020000;
-  u32x4 kreg[6], vreg[4];
+  u32x4 kreg[kKH + kKR], vreg[kVC];
   const int32_t* bt_row = a.bt + (size_t)b * a.max_blocks;
   auto load_tile = [&](int j, int raw_page) {
     const int t0 = j * kAKeys;
@@ -362,19 +373,19 @@ void prefill_attention_kernel(AttnArgs a) {
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.kv + (size_t)page * kPage * kRow + kLatent), (short)0, valid * kRowBytes, kBufFlags);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(kb, khoff[i], 0, 0);
+    for (int i = 0; i < kKH; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(kb, khoff[i], 0, 0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) kreg[4 + i] = __builtin_amdgcn_raw_buffer_load_b128(rb, kroff[i], 0, 0);
+    for (int i = 0; i < kKR; ++i) kreg[kKH + i] = __builtin_amdgcn_raw_buffer_load_b128(rb, kroff[i], 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(vb, vvoff[i], 0, 0);
+    for (int i = 0; i < kVC; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(vb, vvoff[i], 0, 0);
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)(kt[buf] + khdst[i]) = kreg[i];
+    for (int i = 0; i < kKH; ++i) *(u32x4*)(kt[buf] + khdst[i]) = kreg[i];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *(u32x4*)(kt[buf] + krdst[i]) = kreg[4 + i];
+    for (int i = 0; i < kKR; ++i) *(u32x4*)(kt[buf] + krdst[i]) = kreg[kKH + i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)(vt[buf] + vdst[i]) = vreg[i];
+    for (int i = 0; i < kVC; ++i) *(u32x4*)(vt[buf] + vdst[i]) = vreg[i];
   };
 
   f32x16 o[4];
@@ -398,7 +409,7 @@ void prefill_attention_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
   for (int j = 0; j < n_tiles; ++j) {
-    const int buf = 0;
+    const int buf = kBufs == 2 ? (j & 1) : 0;
     if (j + 1 < n_tiles) load_tile(j + 1, next_page);
     const unsigned char* K = kt[buf];
     const unsigned char* V = vt[buf];
@@ -415,16 +426,18 @@ void prefill_attention_kernel(AttnArgs a) {
       auto kread = [&](int n) {     // operand of MFMA n = (mb = n / 12, ks = n % 12)
         return *(const s16x8*)(krow + (n / kSteps) * 32 * kKPitch + (n % kSteps) * 32);
       };
-      s16x8 kop[3];
-      kop[0] = kread(0);
-      kop[1] = kread(1);
+      constexpr int kAhead = kKeyAhead;
+      s16x8 kop[kAhead + 1];
+#pragma unroll
+      for (int n = 0; n < kAhead; ++n) kop[n] = kread(n);
 #pragma unroll
       for (int n = 0; n < 2 * kSteps; ++n) {
-        if (n + 2 < 2 * kSteps) kop[(n + 2) % 3] = kread(n + 2);
+        if (n + kAhead < 2 * kSteps) kop[(n + kAhead) % (kAhead + 1)] = kread(n + kAhead);
         const int mb = n / kSteps, ks = n % kSteps;
-        if (ks == 0) mfma_v<true, false>(s[mb], kop[n % 3], qop[ks]);
-        else if (ks == kSteps - 1) mfma_v<false, true>(s[mb], kop[n % 3], qop[ks]);
-        else mfma_v<false, false>(s[mb], kop[n % 3], qop[ks]);
+        const s16x8& ko = kop[n % (kAhead + 1)];
+        if (ks == 0) mfma_v<true, false>(s[mb], ko, qop[ks]);
+        else if (ks == kSteps - 1) mfma_v<false, true>(s[mb], ko, qop[ks]);
+        else mfma_v<false, false>(s[mb], ko, qop[ks]);
       }
     }
 
@@ -496,21 +509,28 @@ void prefill_attention_kernel(AttnArgs a) {
         pops[ks][2 * i + 1] = (short)(w2 >> 16);
       }
     }
-    s16x8 vop[2];
-    vop[0] = vread(0);
+    constexpr int kVA = kValueAhead;
+    s16x8 vop[kVA + 1];
+#pragma unroll
+    for (int n = 0; n < kVA; ++n) vop[n] = vread(n);
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
-      if (n + 1 < 16) vop[(n + 1) & 1] = vread(n + 1);
+      if (n + kVA < 16) vop[(n + kVA) % (kVA + 1)] = vread(n + kVA);
       const int ks = n >> 2, e = n & 3;
-      if (ks == 3) mfma_v<false, true>(o[e], vop[n & 1], pops[ks]);
-      else mfma_v<false, false>(o[e], vop[n & 1], pops[ks]);
+      if (ks == 3) mfma_v<false, true>(o[e], vop[n % (kVA + 1)], pops[ks]);
+      else mfma_v<false, false>(o[e], vop[n % (kVA + 1)], pops[ks]);
     }
 
     // the page id two tiles ahead: its scalar load completes under the barrier
     if (j + 2 < n_tiles) next_page = ld_scalar(bt_row + j + 2);
-    __syncthreads();
-    if (j + 1 < n_tiles) store_tile(0);
-    __syncthreads();
+    if constexpr (kBufs == 2) {
+      if (j + 1 < n_tiles) store_tile(buf ^ 1);
+      __syncthreads();
+    } else {
+      __syncthreads();
+      if (j + 1 < n_tiles) store_tile(0);
+      __syncthreads();
+    }
   }
 
   if (!q_ok) return;
@@ -553,7 +573,9 @@ hipError_t launch_prefill_attention(const uint16_t* q_c, const uint16_t* q_r, co
   a.max_len = max_len;
   a.scale_log2 = scale * kLog2e;
   // n_qt x 128 heads x batch workgroups: a multiple of the 8 dies since 128 is.
-  hipLaunchKernelGGL(prefill_attention_kernel, dim3((M + kAQ - 1) / kAQ * kHeads * batch), dim3(256), 0, s, a);
+  constexpr int kW = kAttnWaves, kBufs = kAttnBufs;
+  hipLaunchKernelGGL((prefill_attention_kernel<kW, kBufs>), dim3((M + kAQW * kW - 1) / (kAQW * kW) * kHeads * batch),
+                     dim3(64 * kW), 0, s, a);
   return hipGetLastError();
 }
 
