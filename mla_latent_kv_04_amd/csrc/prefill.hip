@@ -25,7 +25,10 @@ namespace {
 
 constexpr int kDTok = 256;        // tokens per decompress workgroup
 constexpr int kDK = 64;           // latent values per K-loop chunk
-constexpr int kDPitchRow = kDK * 2 + 16;      // [row][64 k] tiles: 144 B, 16-byte reads of 8 rows spread over banks
+constexpr int kDPitchRow = kDK * 2 + 16;      // [row][k] tiles: rows 4 banks apart mod 64 for 16-byte reads
+constexpr int kCCPR = kDK * 2 / 16;           // 16-byte chunks per [row][k] tile row
+constexpr int kCRows = 512 / kCCPR;           // rows one pass of 512 threads covers
+constexpr int kCP = kDTok / kCRows;           // passes per chunk (equal to kDK / 16, the V tile's)
 constexpr int kDPitchV = 2 * kDimC * 2 + 32;  // [64 k][256 n] tile: 544 B = 8 banks mod 32 for transposing reads
 
 struct DecompArgs {
@@ -50,7 +53,7 @@ __device__ __forceinline__ int clamp_len(int L, int max_blocks) {
 // 64 (w % 4) .. +63 (2 column blocks) of v_mfma_f32_32x32x16_bf16.  The A
 // operand (weights) comes from LDS: for K row-major [n][k] (16-byte reads), for
 // V [k][n] through transposing reads; the B operand (latent rows) from a
-// [token][k] LDS tile.  Each 64-wide chunk of the latent is loaded into
+// [token][k] LDS tile.  Each kDK-wide chunk of the latent is loaded into
 // registers while the previous one is multiplied.
 template <bool kIsV>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
@@ -65,28 +68,29 @@ void decompress_kernel(DecompArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char wt[kWBytes];
   __shared__ __attribute__((aligned(16))) unsigned char ct[kDTok * kDPitchRow];
 
-  // Latent chunk loads: thread -> token row tid / 8 + 64 i (i < 4), 16 bytes at k 8 (tid % 8).
-  const uint16_t* crow[4];
+  static_assert(kCP == kDK / 16, "latent and weight chunks take the same number of passes");
+  // Latent chunk loads: thread -> token row tid / kCCPR + kCRows i, 16 bytes at k 8 (tid % kCCPR).
+  const uint16_t* crow[kCP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + tid / 8 + 64 * i;
+  for (int i = 0; i < kCP; ++i) {
+    const int t = t0 + tid / kCCPR + kCRows * i;
     const int tt = t < L ? t : 0;             // rows past the sequence read its token 0, never stored
     int64_t page = a.bt[(size_t)b * a.max_blocks + tt / kPage];
     page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
-    crow[i] = a.kv + ((size_t)page * kPage + (tt & (kPage - 1))) * kRow + 8 * (tid % 8);
+    crow[i] = a.kv + ((size_t)page * kPage + (tt & (kPage - 1))) * kRow + 8 * (tid % kCCPR);
   }
-  unsigned char* cdst = ct + (tid / 8) * kDPitchRow + (tid % 8) * 16;
+  unsigned char* cdst = ct + (tid / kCCPR) * kDPitchRow + (tid % kCCPR) * 16;
 
   // Weight chunk loads.
-  const uint16_t* wsrc[4];
-  unsigned char* wdst[4];
+  const uint16_t* wsrc[kCP];
+  unsigned char* wdst[kCP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kCP; ++i) {
     if (!kIsV) {
-      // W_UK rows n = tid / 8 + 64 i of the head pair ([n][k], 16 bytes at k 8 (tid % 8))
-      const int n = tid / 8 + 64 * i;
-      wsrc[i] = a.w + ((size_t)(2 * hp + n / kDimC) * kDimC + (n % kDimC)) * kLatent + 8 * (tid % 8);
-      wdst[i] = wt + n * kDPitchRow + (tid % 8) * 16;
+      // W_UK rows n = tid / kCCPR + kCRows i of the head pair ([n][k], 16 bytes at k 8 (tid % kCCPR))
+      const int n = tid / kCCPR + kCRows * i;
+      wsrc[i] = a.w + ((size_t)(2 * hp + n / kDimC) * kDimC + (n % kDimC)) * kLatent + 8 * (tid % kCCPR);
+      wdst[i] = wt + n * kDPitchRow + (tid % kCCPR) * 16;
     } else {
       // W_UV rows k = tid / 32 + 16 i of the chunk, 16 bytes of head 2 hp + (tid % 32) / 16 at e 8 (tid % 16)
       const int k = tid / 32 + 16 * i, nc = tid % 32;
@@ -95,13 +99,13 @@ void decompress_kernel(DecompArgs a) {
     }
   }
 
-  u32x4 cv[4], wv[4];
+  u32x4 cv[kCP], wv[kCP];
   auto load_chunk = [&](int kc) {
     const int k0 = kc * kDK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cv[i] = *(const u32x4*)(crow[i] + k0);
+    for (int i = 0; i < kCP; ++i) cv[i] = *(const u32x4*)(crow[i] + k0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wv[i] = *(const u32x4*)(wsrc[i] + (kIsV ? (size_t)k0 * kDimC : (size_t)k0));
+    for (int i = 0; i < kCP; ++i) wv[i] = *(const u32x4*)(wsrc[i] + (kIsV ? (size_t)k0 * kDimC : (size_t)k0));
   };
 
   const int nh = wave / 4;            // head of the pair this wave computes
@@ -118,9 +122,9 @@ void decompress_kernel(DecompArgs a) {
   for (int kc = 0; kc < kLatent / kDK; ++kc) {
     if (kc > 0) __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)(cdst + 64 * i * kDPitchRow) = cv[i];
+    for (int i = 0; i < kCP; ++i) *(u32x4*)(cdst + kCRows * i * kDPitchRow) = cv[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)wdst[i] = wv[i];
+    for (int i = 0; i < kCP; ++i) *(u32x4*)wdst[i] = wv[i];
     __syncthreads();
     if (kc + 1 < kLatent / kDK) load_chunk(kc + 1);
     // keep the next chunk's loads ahead of this chunk's MFMAs (the scheduler would sink
