@@ -43,3 +43,16 @@ from .mla_oracle import (  # noqa: F401
     split_decode_absorbed,
     up_proj,
 )
+from .fp8_cache import (  # noqa: F401
+    append_to_pool_mxfp8,
+    dequantize_pool,
+    e4m3_round,
+    e4m3_value,
+    mx_dequantize,
+    mx_quantize,
+    mx_scale_exponent,
+    pack_rows,
+    quantize_pool,
+    unpack_rows,
+)
+from . import fp8_cache  # noqa: F401,E402

@@ -14,6 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ATTENTION = ("mla_oracle.py", "test_oracle_attention.py")
 APPEND = ("cache_append.py", "test_oracle_append.py")
 PREFILL = ("prefill.py", "test_oracle_prefill.py")
+FP8 = ("fp8_cache.py", "test_oracle_fp8.py")
 
 MUTATIONS = {
     "dropped RoPE term": ("s = (K[:n] @ q_c[b, i, h] + r[:n] @ q_r[b, i, h]) * scale",
@@ -56,6 +57,20 @@ MUTATIONS.update({name: (PREFILL, old, new) for name, (old, new) in {
                                           "c = _as_f64(gather_rows(pool, block_table, b, n))[:, 1:d_c + 1]"),
     "decompress key transposed": ('K[b, :, :n] = np.einsum("tc,hdc->htd", c, w_uk)',
                                   'K[b, :, :n] = np.einsum("tc,hdc->htd", c[::-1], w_uk)'),
+}.items()})
+MUTATIONS.update({name: (FP8, old, new) for name, (old, new) in {
+    "E4M3 exponent bias 8": ("np.ldexp(1.0 + m / 8.0, e - 7)", "np.ldexp(1.0 + m / 8.0, e - 8)"),
+    "E4M3 subnormal step halved": ("np.ldexp(m / 8.0, -6)", "np.ldexp(m / 8.0, -7)"),
+    "E4M3 ties away from zero": ("((d_hi == d_lo) & (_POS_CODES[hi] % 2 == 0))", "(d_hi == d_lo)"),
+    "E4M3 sign dropped": ("code = np.where(np.signbit(x), code | 0x80, code)", "code = code"),
+    "MX scale clips like floor(log2 amax) - 8": ("x = np.where(amax > E4M3_MAX * np.ldexp(1.0, x0), x0 + 1, x0)",
+                                                 "x = x0"),
+    "MX scale from the block mean": ("np.abs(blocks).max(axis=-1)", "np.abs(blocks).mean(axis=-1)"),
+    "MX scale bias off by one": ("np.ldexp(vals, (s - SCALE_BIAS)[..., None])",
+                                 "np.ldexp(vals, (s - SCALE_BIAS - 1)[..., None])"),
+    "MX blocks of 16": ("MX_BLOCK = 32", "MX_BLOCK = 16"),
+    "k_R bytes big-endian": ('rope.astype("<u2").view(np.uint8)', 'rope.astype(">u2").view(np.uint8)'),
+    "MXFP8 append ignores max_pos": ("if p < 0 or p >= max_pos:", "if p < 0:"),
 }.items()})
 
 
