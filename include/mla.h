@@ -169,10 +169,10 @@ typedef struct mla_append_params {
   int32_t reserved;           /* must be 0 */
 } mla_append_params;
 
-/* Workspace bytes needed by mla_append_kv: the fp32 partial sums of the split
- * projection, splits x tokens x 576 x 4 bytes (2 MiB for 64 tokens and
- * d = 7168; 16 bytes when the token count alone fills the device and the
- * projection is not split).  Returns 0 when p is invalid.  No HIP call. */
+/* Workspace bytes needed by mla_append_kv and mla_append_kv_mxfp8: the fp32
+ * partial sums of the split projection, splits x tokens x 576 x 4 bytes (2 MiB
+ * for 64 tokens and d = 7168; with the projection not split, tokens x 576 x 4,
+ * which only the MXFP8 cache uses).  Returns 0 when p is invalid.  No HIP call. */
 size_t mla_append_workspace_size(const mla_append_params* p);
 
 /* Writes the new tokens' cache rows (and, optionally, rotates their RoPE query):
@@ -263,8 +263,58 @@ mla_status mla_prefill(const uint16_t* q_c, const uint16_t* q_r, const uint16_t*
                        float* lse, const mla_prefill_params* p, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* ---------------------------------------------------------------- MXFP8 latent cache
+ *
+ * The pages keep the latent cache at four bits (NVFP4) and gather it with
+ * 16-byte vector loads at byte offsets of half the element index, which needs a
+ * 16-byte aligned page-table base ("撕开 DeepSeek MLA 源码", sheratonhq.com,
+ * section 5); they give neither the element code nor the scale layout.  This
+ * library's low-precision cache is the CDNA4-native analogue, OCP MXFP8:
+ *   - latent codes: OCP E4M3 (bias 7, no infinities, largest 448, 0x7F/0xFF NaN);
+ *   - blocks of 32 consecutive latent values share one E8M0 scale byte s,
+ *     value 2^(s - 127); a block's scale is the smallest power of two 2^X with
+ *     max |v| <= 448 * 2^X (no element saturates), X in [-127, 127], s = 0 for an
+ *     all-zero block; codes are v / 2^X rounded to nearest, ties to even;
+ *   - k_R stays bf16.
+ * Row of one token, MLA_MXFP8_ROW_BYTES = 656 bytes (every part 16-byte aligned):
+ *   bytes [0, 512) codes, [512, 528) the 16 scale bytes, [528, 656) k_R as 64 bf16.
+ * A page is 64 rows (41 984 bytes, against 73 728 for bf16: 41/72); paging and
+ * block tables are the bf16 cache's.  kv_mxfp8 pointers are 16-byte aligned.
+ * Dequantisation (code value times 2^(s - 127)) is exact in bf16 for normal
+ * results, so the decode over an MXFP8 cache is the bf16 decode over the
+ * dequantised cache, with the same accumulation and the same outputs contract. */
+#define MLA_MXFP8_ROW_BYTES 656
+
+/* kv_mxfp8 [num_pages, 64, 656] from kv_blocks [num_pages, 64, 576] bf16, every
+ * row (finite inputs; the result for a row holding NaN or Inf is unspecified).
+ * num_pages >= 0 (0 is a no-op).  Deterministic: a pure function of the row. */
+mla_status mla_quantize_kv_mxfp8(const uint16_t* kv_blocks, uint8_t* kv_mxfp8, int64_t num_pages, void* stream);
+
+/* mla_decode_paged over an MXFP8 cache: same arguments, parameters, workspace
+ * (mla_decode_workspace_size(p, 0)) and outputs; kv_mxfp8 [num_pages, 64, 656]. */
+mla_status mla_decode_paged_mxfp8(const uint16_t* q_abs, const uint16_t* q_r, const uint8_t* kv_mxfp8,
+                                  const int32_t* block_table, const int32_t* seqlens, uint16_t* out_latent,
+                                  float* lse, const mla_decode_params* p, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* mla_decode (fused step) over an MXFP8 cache: same arguments and workspace
+ * (mla_decode_workspace_size(p, 1)). */
+mla_status mla_decode_mxfp8(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* w_uk,
+                            const uint16_t* w_uv, const uint8_t* kv_mxfp8, const int32_t* block_table,
+                            const int32_t* seqlens, uint16_t* out, float* lse, const mla_decode_params* p,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_append_kv into an MXFP8 cache: the same rows (fp32 sums in the same fixed
+ * order, k_R rotated in fp32 and rounded once to bf16), with the latent of each
+ * row quantised from its fp32 values as above.  Always two kernel launches;
+ * workspace >= mla_append_workspace_size(p) bytes. */
+mla_status mla_append_kv_mxfp8(const uint16_t* x, const uint16_t* w_a, const float* rope_table,
+                               const int32_t* block_table, const int32_t* seqlens, uint8_t* kv_mxfp8,
+                               uint16_t* q_r, const mla_append_params* p, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Benchmark timing hook.  After mla_profile_enable(1), every mla_decode_paged
- * and mla_decode call on any stream records HIP events around each of its
+ * and mla_decode call (either cache format) on any stream records HIP events around each of its
  * kernels (up to 65536 calls; the library creates those events once and keeps
  * them).  mla_profile_collect waits for the recorded calls, writes the summed
  * milliseconds of [absorb, plan, decode, combine, up-projection] to ms[0..4]
@@ -274,7 +324,7 @@ mla_status mla_prefill(const uint16_t* q_c, const uint16_t* q_r, const uint16_t*
 mla_status mla_profile_enable(int32_t enable);
 mla_status mla_profile_collect(double* ms, int32_t* calls);
 
-/* The same hook for mla_append_kv calls (recorded while mla_profile_enable(1) is
+/* The same hook for mla_append_kv and mla_append_kv_mxfp8 calls (recorded while mla_profile_enable(1) is
  * in force, up to 65536 calls): writes the summed milliseconds of [projection
  * kernel, partial-sum kernel] to ms[0..1] (host array of 2; the second is 0 for
  * calls whose projection is not split) and the number of calls to *calls, and

@@ -27,7 +27,10 @@ __all__ = [
     "device_cu_count", "MlaError", "DecodeParams", "KernelTimer", "AppendParams", "append_kv",
     "append_workspace", "append_workspace_size", "make_append_params", "rope_q", "rope_table",
     "PrefillParams", "make_prefill_params", "prefill", "prefill_workspace_size", "PREFILL_THRESHOLD",
+    "MXFP8_ROW_BYTES", "quantize_kv_mxfp8", "decode_paged_mxfp8", "decode_mxfp8", "append_kv_mxfp8",
 ]
+
+MXFP8_ROW_BYTES = 656    # MXFP8 cache row: 512 E4M3 codes, 16 E8M0 scale bytes, 64 bf16 of k_R
 
 PREFILL_THRESHOLD = 256
 
@@ -128,14 +131,18 @@ def up_proj(out_latent, w_uv, out=None):
     return out
 
 
-def decode_paged(q_abs, q_r, kv_blocks, block_table, seqlens, *, scale=DEFAULT_SCALE, num_splits=0,
-                 out_latent=None, lse=None, want_lse=True, workspace=None):
-    """Paged latent-space decode.  q_abs [B, s_q, 128, 512], q_r [B, s_q, 128, 64],
-    kv_blocks [P, 64, 576], block_table [B, max_blocks] int32, seqlens [B] int32.
-    Returns (out_latent [B, s_q, 128, 512] bf16, lse [B, s_q, 128] fp32 or None)."""
+def _kv_arg(kv, P, mxfp8):
+    torch = _torch()
+    if mxfp8:
+        return _ptr(kv, "kv_mxfp8", (torch.uint8,), (P, PAGE, MXFP8_ROW_BYTES))
+    return _ptr(kv, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R))
+
+
+def _decode_paged(q_abs, q_r, kv, block_table, seqlens, scale, num_splits, out_latent, lse, want_lse, workspace,
+                  mxfp8):
     torch = _torch()
     B, s_q = int(q_abs.shape[0]), int(q_abs.shape[1])
-    P = int(kv_blocks.shape[0])
+    P = int(kv.shape[0])
     mb = int(block_table.shape[1])
     params = make_params(B, s_q, mb, P, scale, num_splits)
     if out_latent is None:
@@ -144,25 +151,41 @@ def decode_paged(q_abs, q_r, kv_blocks, block_table, seqlens, *, scale=DEFAULT_S
         lse = torch.empty(B, s_q, NUM_HEADS, dtype=torch.float32, device=q_abs.device)
     workspace, need = _workspace(params, False, workspace)
     lib = _lib.load()
-    st = lib.mla_decode_paged(
+    fn, name = (lib.mla_decode_paged_mxfp8, "mla_decode_paged_mxfp8") if mxfp8 else \
+        (lib.mla_decode_paged, "mla_decode_paged")
+    st = fn(
         _ptr(q_abs, "q_abs", _bf16_types(), (B, s_q, NUM_HEADS, D_C)),
         _ptr(q_r, "q_r", _bf16_types(), (B, s_q, NUM_HEADS, D_R)),
-        _ptr(kv_blocks, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R)),
+        _kv_arg(kv, P, mxfp8),
         _ptr(block_table, "block_table", _i32(), (B, mb)), _ptr(seqlens, "seqlens", _i32(), (B,)),
         _ptr(out_latent, "out_latent", _bf16_types(), (B, s_q, NUM_HEADS, D_C)),
         _ptr(lse, "lse", (torch.float32,), (B, s_q, NUM_HEADS)), ctypes.byref(params),
         _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream())
-    _lib.check(st, "mla_decode_paged")
+    _lib.check(st, name)
     return out_latent, lse
 
 
-def decode(q_c, q_r, w_uk, w_uv, kv_blocks, block_table, seqlens, *, scale=DEFAULT_SCALE, num_splits=0, out=None,
-           lse=None, want_lse=True, workspace=None):
-    """Fused decode step (absorb -> paged decode -> merge -> up-projection).
-    Returns (out [B, s_q, 128, 128] bf16, lse [B, s_q, 128] fp32 or None)."""
+def decode_paged(q_abs, q_r, kv_blocks, block_table, seqlens, *, scale=DEFAULT_SCALE, num_splits=0,
+                 out_latent=None, lse=None, want_lse=True, workspace=None):
+    """Paged latent-space decode.  q_abs [B, s_q, 128, 512], q_r [B, s_q, 128, 64],
+    kv_blocks [P, 64, 576], block_table [B, max_blocks] int32, seqlens [B] int32.
+    Returns (out_latent [B, s_q, 128, 512] bf16, lse [B, s_q, 128] fp32 or None)."""
+    return _decode_paged(q_abs, q_r, kv_blocks, block_table, seqlens, scale, num_splits, out_latent, lse, want_lse,
+                         workspace, False)
+
+
+def decode_paged_mxfp8(q_abs, q_r, kv_mxfp8, block_table, seqlens, *, scale=DEFAULT_SCALE, num_splits=0,
+                       out_latent=None, lse=None, want_lse=True, workspace=None):
+    """decode_paged over an MXFP8 cache: kv_mxfp8 [P, 64, 656] uint8 (rows of mla.h)."""
+    return _decode_paged(q_abs, q_r, kv_mxfp8, block_table, seqlens, scale, num_splits, out_latent, lse, want_lse,
+                         workspace, True)
+
+
+def _decode(q_c, q_r, w_uk, w_uv, kv, block_table, seqlens, scale, num_splits, out, lse, want_lse, workspace,
+            mxfp8):
     torch = _torch()
     B, s_q = int(q_c.shape[0]), int(q_c.shape[1])
-    P = int(kv_blocks.shape[0])
+    P = int(kv.shape[0])
     mb = int(block_table.shape[1])
     params = make_params(B, s_q, mb, P, scale, num_splits)
     if out is None:
@@ -171,18 +194,47 @@ def decode(q_c, q_r, w_uk, w_uv, kv_blocks, block_table, seqlens, *, scale=DEFAU
         lse = torch.empty(B, s_q, NUM_HEADS, dtype=torch.float32, device=q_c.device)
     workspace, need = _workspace(params, True, workspace)
     lib = _lib.load()
-    st = lib.mla_decode(
+    fn, name = (lib.mla_decode_mxfp8, "mla_decode_mxfp8") if mxfp8 else (lib.mla_decode, "mla_decode")
+    st = fn(
         _ptr(q_c, "q_c", _bf16_types(), (B, s_q, NUM_HEADS, D_HC)),
         _ptr(q_r, "q_r", _bf16_types(), (B, s_q, NUM_HEADS, D_R)),
         _ptr(w_uk, "w_uk", _bf16_types(), (NUM_HEADS, D_HC, D_C)),
         _ptr(w_uv, "w_uv", _bf16_types(), (NUM_HEADS, D_C, D_HC)),
-        _ptr(kv_blocks, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R)),
+        _kv_arg(kv, P, mxfp8),
         _ptr(block_table, "block_table", _i32(), (B, mb)), _ptr(seqlens, "seqlens", _i32(), (B,)),
         _ptr(out, "out", _bf16_types(), (B, s_q, NUM_HEADS, D_HC)),
         _ptr(lse, "lse", (torch.float32,), (B, s_q, NUM_HEADS)), ctypes.byref(params),
         _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream())
-    _lib.check(st, "mla_decode")
+    _lib.check(st, name)
     return out, lse
+
+
+def decode(q_c, q_r, w_uk, w_uv, kv_blocks, block_table, seqlens, *, scale=DEFAULT_SCALE, num_splits=0, out=None,
+           lse=None, want_lse=True, workspace=None):
+    """Fused decode step (absorb -> paged decode -> merge -> up-projection).
+    Returns (out [B, s_q, 128, 128] bf16, lse [B, s_q, 128] fp32 or None)."""
+    return _decode(q_c, q_r, w_uk, w_uv, kv_blocks, block_table, seqlens, scale, num_splits, out, lse, want_lse,
+                   workspace, False)
+
+
+def decode_mxfp8(q_c, q_r, w_uk, w_uv, kv_mxfp8, block_table, seqlens, *, scale=DEFAULT_SCALE, num_splits=0,
+                 out=None, lse=None, want_lse=True, workspace=None):
+    """The fused decode step over an MXFP8 cache (kv_mxfp8 [P, 64, 656] uint8)."""
+    return _decode(q_c, q_r, w_uk, w_uv, kv_mxfp8, block_table, seqlens, scale, num_splits, out, lse, want_lse,
+                   workspace, True)
+
+
+def quantize_kv_mxfp8(kv_blocks, out=None):
+    """MXFP8 cache [P, 64, 656] uint8 from a bf16 cache [P, 64, 576] (every row)."""
+    torch = _torch()
+    P = int(kv_blocks.shape[0])
+    if out is None:
+        out = torch.empty(P, PAGE, MXFP8_ROW_BYTES, dtype=torch.uint8, device=kv_blocks.device)
+    lib = _lib.load()
+    st = lib.mla_quantize_kv_mxfp8(_ptr(kv_blocks, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R)),
+                                   _ptr(out, "kv_mxfp8", (torch.uint8,), (P, PAGE, MXFP8_ROW_BYTES)), P, _stream())
+    _lib.check(st, "mla_quantize_kv_mxfp8")
+    return out
 
 
 class KernelTimer:
@@ -280,6 +332,29 @@ def append_workspace(params: AppendParams):
     return _torch().empty(append_workspace_size(params), dtype=_torch().uint8, device="cuda")
 
 
+def _append(x, w_a, table, kv, block_table, seqlens, q_r, workspace, mxfp8):
+    torch = _torch()
+    B, s_q, d = (int(v) for v in x.shape)
+    P = int(kv.shape[0])
+    mb = int(block_table.shape[1])
+    max_pos = int(table.shape[0])
+    H = int(q_r.shape[2]) if q_r is not None else NUM_HEADS
+    params = make_append_params(B, s_q, d, mb, P, max_pos, H)
+    if workspace is None:
+        workspace = append_workspace(params)
+    lib = _lib.load()
+    fn, name = (lib.mla_append_kv_mxfp8, "mla_append_kv_mxfp8") if mxfp8 else (lib.mla_append_kv, "mla_append_kv")
+    st = fn(
+        _ptr(x, "x", _bf16_types(), (B, s_q, d)), _ptr(w_a, "w_a", _bf16_types(), (d, D_C + D_R)),
+        _ptr(table, "table", (torch.float32,), (max_pos, D_R)),
+        _ptr(block_table, "block_table", _i32(), (B, mb)), _ptr(seqlens, "seqlens", _i32(), (B,)),
+        _kv_arg(kv, P, mxfp8),
+        _ptr(q_r, "q_r", _bf16_types(), (B, s_q, H, D_R)), ctypes.byref(params),
+        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream())
+    _lib.check(st, name)
+    return kv
+
+
 def append_kv(x, w_a, table, kv_blocks, block_table, seqlens, *, q_r=None, workspace=None):
     """Writes the rows of the new tokens into the paged cache (in place).
 
@@ -288,25 +363,12 @@ def append_kv(x, w_a, table, kv_blocks, block_table, seqlens, *, q_r=None, works
     (including the new tokens).  q_r [B, s_q, H, 64] bf16, when given, is rotated in
     place by the same call.  A workspace passed in is reused only on one stream.
     Returns kv_blocks."""
-    torch = _torch()
-    B, s_q, d = (int(v) for v in x.shape)
-    P = int(kv_blocks.shape[0])
-    mb = int(block_table.shape[1])
-    max_pos = int(table.shape[0])
-    H = int(q_r.shape[2]) if q_r is not None else NUM_HEADS
-    params = make_append_params(B, s_q, d, mb, P, max_pos, H)
-    if workspace is None:
-        workspace = append_workspace(params)
-    lib = _lib.load()
-    st = lib.mla_append_kv(
-        _ptr(x, "x", _bf16_types(), (B, s_q, d)), _ptr(w_a, "w_a", _bf16_types(), (d, D_C + D_R)),
-        _ptr(table, "table", (torch.float32,), (max_pos, D_R)),
-        _ptr(block_table, "block_table", _i32(), (B, mb)), _ptr(seqlens, "seqlens", _i32(), (B,)),
-        _ptr(kv_blocks, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R)),
-        _ptr(q_r, "q_r", _bf16_types(), (B, s_q, H, D_R)), ctypes.byref(params),
-        _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream())
-    _lib.check(st, "mla_append_kv")
-    return kv_blocks
+    return _append(x, w_a, table, kv_blocks, block_table, seqlens, q_r, workspace, False)
+
+
+def append_kv_mxfp8(x, w_a, table, kv_mxfp8, block_table, seqlens, *, q_r=None, workspace=None):
+    """append_kv into an MXFP8 cache (kv_mxfp8 [P, 64, 656] uint8, in place)."""
+    return _append(x, w_a, table, kv_mxfp8, block_table, seqlens, q_r, workspace, True)
 
 
 def rope_q(q_r, table, seqlens):

@@ -38,6 +38,10 @@ EXPORTS = (
     "mla_prefill_workspace_size",
     "mla_prefill",
     "mla_device_cu_count",
+    "mla_quantize_kv_mxfp8",
+    "mla_decode_paged_mxfp8",
+    "mla_decode_mxfp8",
+    "mla_append_kv_mxfp8",
     "mla_status_string",
     "mla_last_error",
 )
@@ -133,6 +137,10 @@ def load() -> ctypes.CDLL:
         "mla_profile_collect_prefill": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)], ctypes.c_int),
         "mla_prefill_workspace_size": ([fp], sz),
         "mla_prefill": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, fp, vp, sz, vp], ctypes.c_int),
+        "mla_quantize_kv_mxfp8": ([vp, vp, ctypes.c_int64, vp], ctypes.c_int),
+        "mla_decode_paged_mxfp8": ([vp, vp, vp, vp, vp, vp, vp, pp, vp, sz, vp], ctypes.c_int),
+        "mla_decode_mxfp8": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, sz, vp], ctypes.c_int),
+        "mla_append_kv_mxfp8": ([vp, vp, vp, vp, vp, vp, vp, ap, vp, sz, vp], ctypes.c_int),
         "mla_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "mla_last_error": ([], ctypes.c_char_p),
     }

@@ -22,6 +22,7 @@
 // than the second launch.)  When the token count alone fills the device the
 // contraction is not split and the first kernel writes the rows itself.
 #include "append.h"
+#include "mxfp8.h"
 
 namespace mla {
 
@@ -39,12 +40,14 @@ struct AppendArgs {
   const float* table;       // [max_pos, 64]
   const int32_t* bt;        // [B, max_blocks]
   const int32_t* seqlens;   // [B]
-  uint16_t* kv;             // [num_pages, 64, 576]
+  uint16_t* kv;             // [num_pages, 64, 576] (bf16 cache) or null
+  unsigned char* kv8;       // [num_pages, 64, 656] (MXFP8 cache) or null
   uint16_t* q_r;            // [T, heads, 64] or null
   float* part;              // [splits, T, 576] when splits > 1
   int64_t num_pages;
   int T, d, s_q, max_blocks, max_pos, heads;
   int splits, slabs_per_split, units, per_die;
+  int direct;               // the projection kernel writes the rows itself (bf16 cache, one split)
 };
 
 // Position of token t (p = seqlens[b] - s_q + i) and its cache row index
@@ -207,7 +210,7 @@ void append_kernel(AppendArgs a) {
   }
 
   // D layout of a 16x16 tile: lane l, register j -> row 4 (l / 16) + j, column l % 16.
-  if (a.splits == 1) {
+  if (a.direct) {
     // The sum is complete: rotate key pairs (columns 2i, 2i + 1 sit in lanes l, l ^ 1) and
     // store each pair of bf16 from its even lane.
 #pragma unroll
@@ -257,6 +260,7 @@ void append_kernel(AppendArgs a) {
 // the first addition; in the last block (the key) lanes 2i and 2i + 1 hold pair
 // i, exchange values and rotate it with the position's fp32 table row; then the
 // value is rounded to bf16 and each pair is stored from its even lane.
+template <bool kF8>
 __global__ __attribute__((amdgpu_flat_work_group_size(64, 64)))
 void append_finalize_kernel(AppendArgs a) {
   constexpr int kBatch = 16;
@@ -284,7 +288,27 @@ void append_finalize_kernel(AppendArgs a) {
     acc = (lane & 1) ? other * sn + acc * c : acc * c - other * sn;
     other = __shfl_xor(acc, 1);
   }
-  if (!(lane & 1)) *(uint32_t*)(a.kv + dst * kRow + col) = pack_bf16x2(acc, other);
+  if constexpr (!kF8) {
+    if (!(lane & 1)) *(uint32_t*)(a.kv + dst * kRow + col) = pack_bf16x2(acc, other);
+  } else {
+    unsigned char* row = a.kv8 + dst * kF8RowBytes;
+    if (col >= kLatent) {
+      if (!(lane & 1)) *(uint32_t*)(row + kF8Rope + 2 * (col - kLatent)) = pack_bf16x2(acc, other);
+      return;
+    }
+    // MXFP8 latent: each half-wave is one block of 32 values; its largest magnitude
+    // sets the scale, then pairs are coded in the even lanes and four codes are
+    // stored as one dword from every fourth lane.
+    float amax = fabsf(acc);
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    const int sb = mx_scale_byte(amax);
+    const float x = ldexpf(acc, 127 - sb), xo = ldexpf(other, 127 - sb);
+    const uint32_t pk = e4m3_pack2<false>(0u, x, xo);          // even lanes: (this, next) codes
+    const uint32_t pk2 = __shfl_xor(pk, 2);
+    if ((lane & 3) == 0) *(uint32_t*)(row + kF8Codes + col) = (pk & 0xFFFFu) | (pk2 << 16);
+    if ((lane & 31) == 0) row[kF8Scales + col / 32] = (unsigned char)sb;
+  }
 }
 
 // q_r [T, H, 64] rotated in place.  One workgroup per token; thread tid always owns
@@ -323,9 +347,44 @@ __global__ void rope_table_kernel(float* __restrict__ table, int max_pos, double
   table[(size_t)p * kRope + kRope / 2 + i] = (float)sin(ang);
 }
 
+// bf16 cache rows -> MXFP8 cache rows.  One wave per row: lane l holds latent values
+// 8l .. 8l+7 (block l / 4), so a block's four lanes find its largest magnitude with
+// two exchanges; every lane stores its 8 codes (the wave writes the 512-byte code
+// run), the first lane of each block its scale byte, lanes 0..7 the 128 bytes of k_R.
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void quantize_mxfp8_kernel(const uint16_t* __restrict__ kv, unsigned char* __restrict__ kv8, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* src = kv + row * kRow;
+  unsigned char* dst = kv8 + row * kF8RowBytes;
+  const u32x4 v = *(const u32x4*)(src + 8 * lane);
+  float f[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f[2 * k] = bf2f((uint16_t)(v[k] & 0xFFFFu));
+    f[2 * k + 1] = bf2f((uint16_t)(v[k] >> 16));
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int sb = mx_scale_byte(amax);
+  uint32_t c[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    c[h] = e4m3_pack2<false>(0u, ldexpf(f[4 * h], 127 - sb), ldexpf(f[4 * h + 1], 127 - sb));
+    c[h] = e4m3_pack2<true>(c[h], ldexpf(f[4 * h + 2], 127 - sb), ldexpf(f[4 * h + 3], 127 - sb));
+  }
+  *(u32x2*)(dst + kF8Codes + 8 * lane) = u32x2{c[0], c[1]};
+  if ((lane & 3) == 0) dst[kF8Scales + lane / 4] = (unsigned char)sb;
+  if (lane < 8) *(u32x4*)(dst + kF8Rope + 16 * lane) = *(const u32x4*)(src + kLatent + 8 * lane);
+}
+
 }  // namespace
 
-AppendPlan plan_append(int tokens, int d_model) {
+AppendPlan plan_append(int tokens, int d_model, bool mxfp8) {
   AppendPlan pl{};
   const int groups = (tokens + kTokens - 1) / kTokens;
   // One token group (decode): 32-column blocks halve the fp32 partials of 64-column
@@ -345,17 +404,19 @@ AppendPlan plan_append(int tokens, int d_model) {
   pl.splits = splits;
   pl.slabs_per_split = slabs / splits;
   pl.units = base_units * splits;
-  pl.part_bytes = splits > 1 ? (size_t)splits * tokens * kRow * sizeof(float) : 0;
+  // the MXFP8 cache always takes the partial-sum kernel (it holds the block quantiser)
+  pl.part_bytes = splits > 1 || mxfp8 ? (size_t)splits * tokens * kRow * sizeof(float) : 0;
   return pl;
 }
 
 hipError_t launch_append(const uint16_t* x, const uint16_t* w_a, const float* table, const int32_t* bt,
-                         const int32_t* seqlens, uint16_t* kv, uint16_t* q_r, int heads, unsigned char* ws,
-                         int batch, int s_q, int d_model, int max_blocks, int64_t num_pages, int max_pos,
-                         hipStream_t s, hipEvent_t ev_proj_done) {
+                         const int32_t* seqlens, uint16_t* kv, unsigned char* kv8, uint16_t* q_r, int heads,
+                         unsigned char* ws, int batch, int s_q, int d_model, int max_blocks, int64_t num_pages,
+                         int max_pos, hipStream_t s, hipEvent_t ev_proj_done) {
   const int T = batch * s_q;
   if (T <= 0) return ev_proj_done != nullptr ? hipEventRecord(ev_proj_done, s) : hipSuccess;
-  const AppendPlan pl = plan_append(T, d_model);
+  const bool f8 = kv8 != nullptr;
+  const AppendPlan pl = plan_append(T, d_model, f8);
   AppendArgs a;
   a.x = x;
   a.w = w_a;
@@ -363,6 +424,7 @@ hipError_t launch_append(const uint16_t* x, const uint16_t* w_a, const float* ta
   a.bt = bt;
   a.seqlens = seqlens;
   a.kv = kv;
+  a.kv8 = kv8;
   a.q_r = q_r;
   a.part = reinterpret_cast<float*>(ws);
   a.num_pages = num_pages;
@@ -376,6 +438,7 @@ hipError_t launch_append(const uint16_t* x, const uint16_t* w_a, const float* ta
   a.slabs_per_split = pl.slabs_per_split;
   a.units = pl.units;
   a.per_die = (pl.units + kXcds - 1) / kXcds;
+  a.direct = pl.splits == 1 && !f8;
   const dim3 grid(a.per_die * kXcds);
   if (pl.cols == 32)
     hipLaunchKernelGGL(append_kernel<32>, grid, dim3(256), 0, s, a);
@@ -383,8 +446,11 @@ hipError_t launch_append(const uint16_t* x, const uint16_t* w_a, const float* ta
     hipLaunchKernelGGL(append_kernel<64>, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev_proj_done != nullptr) e = hipEventRecord(ev_proj_done, s);
-  if (e != hipSuccess || pl.splits == 1) return e;
-  hipLaunchKernelGGL(append_finalize_kernel, dim3(T, kRow / 64), dim3(64), 0, s, a);
+  if (e != hipSuccess || a.direct) return e;
+  if (f8)
+    hipLaunchKernelGGL(append_finalize_kernel<true>, dim3(T, kRow / 64), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_finalize_kernel<false>, dim3(T, kRow / 64), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -400,6 +466,13 @@ hipError_t launch_rope_table(float* table, int max_pos, double base, hipStream_t
   if (max_pos <= 0) return hipSuccess;
   const int n = max_pos * (kRope / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, table, max_pos, base);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp8(const uint16_t* kv, unsigned char* kv8, int64_t num_pages, hipStream_t s) {
+  const int64_t rows = num_pages * kPage;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, kv, kv8, rows);
   return hipGetLastError();
 }
 

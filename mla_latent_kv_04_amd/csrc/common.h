@@ -90,9 +90,10 @@ struct DecodePlanView {
 hipError_t launch_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_abs, int tokens,
                            hipStream_t s);
 hipError_t launch_up_proj(const uint16_t* ol, const uint16_t* w_uv, uint16_t* out, int tokens, hipStream_t s);
-hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv, const int32_t* bt,
-                         const int32_t* seqlens, uint16_t* out_latent, float* lse, int batch, int s_q,
-                         int max_blocks, int64_t num_pages, float scale, int wgs, const DecodePlanView& plan,
+// Exactly one of kv (bf16 cache) and kv8 (MXFP8 cache) is non-null.
+hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv, const unsigned char* kv8,
+                         const int32_t* bt, const int32_t* seqlens, uint16_t* out_latent, float* lse, int batch,
+                         int s_q, int max_blocks, int64_t num_pages, float scale, int wgs, const DecodePlanView& plan,
                          hipStream_t s, hipEvent_t ev_plan_done = nullptr, hipEvent_t ev_decode_done = nullptr);
 hipError_t launch_gather(const uint16_t* kv, const int32_t* bt, const int32_t* seqlens, uint16_t* dense, int batch,
                          int max_blocks, int64_t num_pages, hipStream_t s);

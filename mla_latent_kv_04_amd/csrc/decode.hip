@@ -26,6 +26,7 @@
 // index that keeps both the row reads of QK (16 tokens, one chunk) and the
 // 4-row transposing reads of PV free of bank conflicts.
 #include "common.h"
+#include "mxfp8.h"
 
 namespace mla {
 
@@ -37,7 +38,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct DecodeArgs {
   const uint16_t* q_abs;
   const uint16_t* q_r;
-  const uint16_t* kv;
+  const uint16_t* kv;        // bf16 cache [num_pages, 64, 576], or
+  const unsigned char* kv8;  // MXFP8 cache [num_pages, 64, 656] (rows of mxfp8.h)
   const int32_t* bt;
   const int32_t* seqlens;
   uint16_t* out_latent;
@@ -120,6 +122,23 @@ constexpr int kPBytes = kHeads * kTile * 2;          // 8192: P of one tile, [12
 constexpr int kLoadsPerTile = kTileBytes / 16 / kThreads;   // 9 direct loads per thread per tile
 static_assert(kTileBytes % (16 * kThreads) == 0, "tile must split evenly over the workgroup");
 
+// MXFP8 cache: a 32-token tile is 20 992 bytes in HBM.  LDS holds a ring of 3
+// bf16 tile slots (the dequantised latent and the RoPE rows, laid out and swizzled
+// as above) and a two-deep staging of the tile's codes and scale bytes.  Wave w
+// loads the codes, scales and RoPE rows of tokens 8w .. 8w+7 and dequantises
+// those rows itself, so staging needs no barrier: 4 code loads (two 512-byte rows
+// each), 1 RoPE load, 1 four-byte-per-lane scale load.
+constexpr int kF8Slots = 3;
+constexpr int kF8TileBytes = kTile * kF8RowBytes;             // 20992
+constexpr int kF8Stage = kTile * kLatent;                     // 16384 code bytes of a tile
+constexpr int kF8ScaleStage = 4 * 256;                        // per wave: 32 lanes x 4 B, then a copy
+constexpr int kF8StageOff = kF8Slots * kTileBytes;            // 110592
+constexpr int kF8ScaleOff = kF8StageOff + 2 * kF8Stage;       // 143360
+constexpr int kF8LdsBytes = kF8ScaleOff + 2 * kF8ScaleStage;  // 145408
+constexpr int kF8LoadsPerTile = 6;   // the "s_waitcnt vmcnt(6)" below count these
+static_assert(kF8LoadsPerTile == 6, "vmcnt literal");
+static_assert(kF8LdsBytes % 1024 == 0 && kF8LdsBytes + 2 * kHeads * kTile * 2 <= 163840, "LDS budget");
+
 // Tile copy HBM -> LDS: wave w copies the latent rows of tokens w, w+4, ...,
 // w+28 (one 64-lane direct load per row, lane l = chunk position l) and the
 // RoPE rows of tokens 8w .. 8w+7 (one load; lane l -> token 8w + l/8, chunk
@@ -150,6 +169,11 @@ __device__ __forceinline__ TileLoadOffsets tile_load_offsets(int lane, int wave_
 // tile barrier, and a volatile asm is never moved across that barrier.
 __device__ __forceinline__ void dma_b128(const unsigned char* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds));
+}
+
+// The same with 4 bytes per lane (global_load_lds_dword): lane l's bytes land at lds + 4 l.
+__device__ __forceinline__ void dma_b32(const unsigned char* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -221,11 +245,12 @@ struct Flag {
 //   P of tile k (bf16) -> LDS P buffer k%2.
 // P is shared through LDS so that PV can be split by latent columns; that halves
 // the PV operand traffic compared with every wave reading all 512 columns.
+template <bool kF8>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(DecodeArgs a) {
   // 1024-byte alignment: tile slots and P buffers then start at multiples of 1024, so
   // adding a slot base never changes the low ten bits of an offset (see below).
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[kSlots * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kF8 ? kF8LdsBytes : kSlots * kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char pbuf[2 * kPBytes];
 
   const int U = a.batch * a.s_q;
@@ -251,6 +276,8 @@ void decode_kernel(DecodeArgs a) {
   //   latl[k]: direct-load source offset of latent chunk position `lane` of a row t with
   //     t % 4 == w and (t / 4) % 4 == k;  ropel: RoPE source offset of this lane's row
   //     (token 8w + lane/8) and chunk position relative to the tile.
+  // Byte offset of the tile slot of tile k (the bf16 cache rings 4 slots, the MXFP8 cache 3).
+  auto slot_off = [](int k) -> uint32_t { return (uint32_t)((kF8 ? k % kF8Slots : (k & 3)) * kTileBytes); };
   uint32_t aql, arl, latl[4], ropel;
   {
     aql = l32 * 1024 + 16 * (hi ^ swz_lat(l32));
@@ -259,6 +286,17 @@ void decode_kernel(DecodeArgs a) {
     for (int k = 0; k < 4; ++k) latl[k] = (uint32_t)((lane ^ swz_lat(wave_u + 4 * k)) * 16);
     ropel = (uint32_t)((8 * wave_u + (lane >> 3)) * kRowBytes + kLatent * 2 +
                        ((lane & 7) ^ ((4 * wave_u + (lane >> 4)) & 7)) * 16);
+  }
+  //   f8r, f8c, f8s (MXFP8 cache): tile source offsets of this lane's RoPE chunk (token
+  //     8w + lane/8, chunk position lane%8, swizzled as the bf16 RoPE rows), code chunk
+  //     (token 8w + lane/32, chunk lane%32; load i adds rows 2i: 1312 i bytes) and scale
+  //     dword (token 8w + (lane%32)/4, bytes 4 (lane%4) .. +3; lanes 32..63 repeat 0..31).
+  uint32_t f8r = 0, f8c = 0, f8s = 0;
+  if constexpr (kF8) {
+    f8r = (uint32_t)((8 * wave_u + (lane >> 3)) * kF8RowBytes + kF8Rope +
+                     ((lane & 7) ^ ((4 * wave_u + (lane >> 4)) & 7)) * 16);
+    f8c = (uint32_t)((8 * wave_u + (lane >> 5)) * kF8RowBytes + kF8Codes + 16 * (lane & 31));
+    f8s = (uint32_t)((8 * wave_u + ((lane & 31) >> 2)) * kF8RowBytes + kF8Scales + 4 * (lane & 3));
   }
   //   offP0: PV A operand (P) of head l32, tokens 8hi .. +7 in a P buffer (k-step st:
   //     XOR 32st);  offV0: PV B operand (transposing reads) of column block 0, half 0,
@@ -301,12 +339,76 @@ void decode_kernel(DecodeArgs a) {
     auto tile_src = [&](int k) -> const unsigned char* {
       int64_t phys = ld_uniform(a.bt, bt_row + p0 + (k >> 1));
       phys = phys < 0 ? 0 : (phys >= a.num_pages ? a.num_pages - 1 : phys);
-      return (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + (k & 1) * kTileBytes;
+      if constexpr (kF8) return a.kv8 + phys * (int64_t)kF8PageBytes + (k & 1) * kF8TileBytes;
+      else return (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + (k & 1) * kTileBytes;
     };
     auto tile_valid = [&](int k) { return min(kTile, n_vis - tok_begin - k * kTile); };
     auto issue = [&](int k) {
-      const TileLoadOffsets ldo = tile_load_offsets(opaque_lane(), wave_u);
-      issue_tile(tile_src(k), lbase + (k & 3) * kTileBytes, ldo, wave_u, lane, tile_valid(k));
+      if constexpr (kF8) {
+        // RoPE rows straight into the bf16 slot; codes and scales into staging k & 1.
+        // Rows past the sequence are loaded as they are (they lie in the same page) and
+        // never reach a product: their latent is zeroed when dequantised and their
+        // scores are masked.
+        const unsigned char* src = tile_src(k);
+        dma_b128(src, f8r, lbase + slot_off(k) + kRopeRegion + 1024 * wave_u);
+        const uint32_t cd = lbase + kF8StageOff + (k & 1) * kF8Stage + 4096 * wave_u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma_b128(src + 2 * i * kF8RowBytes, f8c, cd + 1024 * i);
+        dma_b32(src, f8s, lbase + kF8ScaleOff + (k & 1) * kF8ScaleStage + 256 * wave_u);
+      } else {
+        const TileLoadOffsets ldo = tile_load_offsets(opaque_lane(), wave_u);
+        issue_tile(tile_src(k), lbase + (k & 3) * kTileBytes, ldo, wave_u, lane, tile_valid(k));
+      }
+    };
+    // MXFP8: dequantise this wave's rows (tokens 8w .. 8w+7) of tile kc from staging
+    // into the tile's bf16 slot; rows past the sequence become zeros.  Part j (0..3)
+    // is staging load j: lane l holds row t = 8w + 2j + l/32, code chunk q = l%32
+    // (latent values 16q .. 16q+15, block q/2), written as bf16 chunks 2q and 2q+1 of
+    // row t.  With h = l/32, swz_lat(t) = 4 (2 (j & 1) + h) + ((2w + j/2) & 3), so the
+    // byte offset of chunk 2q within the tile is 1024 (8w + 2j) + (f8l ^ u_j), where
+    // f8l = 1024 h + (32q ^ 64h) is a lane constant and u_j = 128 (j & 1) + 16 ((2w + j/2) & 3)
+    // is uniform; chunk 2q + 1 sits at that offset XOR 16.
+    u32x4 f8v[4];
+    uint32_t f8sc[4], f8l = 0;
+    auto f8_read = [&](int kc, int j) {
+      const uint32_t ln = (uint32_t)opaque_lane();
+      if (j == 0) f8l = ((ln >> 5) << 10) | ((32u * (ln & 31)) ^ ((ln >> 5) << 6));
+      const uint32_t cb = lbase + kF8StageOff + (kc & 1) * kF8Stage + 4096 * wave_u + 16 * ln;
+      f8v[j] = __builtin_bit_cast(u32x4, lds_read_b128_at(cb + 1024 * j));
+      const uint32_t sbase = lbase + kF8ScaleOff + (kc & 1) * kF8ScaleStage + 256 * wave_u + 16 * (ln >> 5) +
+                             ((ln & 31) >> 1);
+      f8sc[j] = *(MLA_LDS const unsigned char*)(sbase + 32 * j);
+    };
+    auto f8_write = [&](uint32_t slot_base, int j) {
+      const uint32_t u = 128u * (j & 1) + 16u * ((2 * wave_u + (j >> 1)) & 3);
+      const uint32_t lo_addr = slot_base + 1024 * (8 * wave_u + 2 * j) + (f8l ^ u);
+      const float sc = mx_scale_f32(f8sc[j]);
+      const u32x2 d0 = e4m3x4_to_bf16(f8v[j][0], sc), d1 = e4m3x4_to_bf16(f8v[j][1], sc);
+      const u32x2 d2 = e4m3x4_to_bf16(f8v[j][2], sc), d3 = e4m3x4_to_bf16(f8v[j][3], sc);
+      *(MLA_LDS u32x4*)lo_addr = u32x4{d0[0], d0[1], d1[0], d1[1]};
+      *(MLA_LDS u32x4*)(lo_addr ^ 16u) = u32x4{d2[0], d2[1], d3[0], d3[1]};
+    };
+    // Rows at or past `valid` (only in a segment's last tile) are overwritten with zeros.
+    auto f8_zero_tail = [&](uint32_t slot_base, int valid) {
+      const uint32_t ln = (uint32_t)opaque_lane();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 8 * wave_u + 2 * j + (int)(ln >> 5);
+        const uint32_t u = 128u * (j & 1) + 16u * ((2 * wave_u + (j >> 1)) & 3);
+        const uint32_t lo_addr = slot_base + 1024 * (8 * wave_u + 2 * j) + (f8l ^ u);
+        if (t >= valid) {
+          *(MLA_LDS u32x4*)lo_addr = u32x4{0u, 0u, 0u, 0u};
+          *(MLA_LDS u32x4*)(lo_addr ^ 16u) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    };
+    auto f8_convert_all = [&](int kc) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f8_read(kc, j);
+      const uint32_t sb = lbase + slot_off(kc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f8_write(sb, j);
+      if (tile_valid(kc) < kTile) f8_zero_tail(sb, tile_valid(kc));
     };
 
     // P buffer 1 stands for "P of tile -1" in the first step: zero it.  Its last
@@ -319,6 +421,13 @@ void decode_kernel(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // earlier stores of this workgroup
     issue(0);
     if (n_tiles > 1) issue(1);
+    if constexpr (kF8) {
+      // tile 0 must be in bf16 before the first step; tile 1 may stay in flight
+      if (n_tiles > 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      f8_convert_all(0);
+      asm volatile("" ::: "memory");
+    }
 
     // Queries of this wave's 32 heads as the MFMA B operand: lane l holds head
     // 32w + l32, columns 16ks + 8hi .. +7 (k-steps 0..31 latent, 32..35 RoPE).
@@ -352,11 +461,11 @@ void decode_kernel(DecodeArgs a) {
     // loads of tile kn (source tile base, per-lane offsets, first LDS address).
     uint32_t aq[8], ar[4], dv[9];
     const unsigned char* dsrc;
-    uint32_t m0n;
+    uint32_t m0n, m0c = 0, m0s = 0;   // LDS targets of the next tile's loads (m0c, m0s: MXFP8 codes, scales)
     int32_t bt_pref;
     // Each preparation comes in three parts so that it can be spread over stages.
     auto prep_qk = [&](int kk, int part) {
-      const uint32_t cur_addr = lbase + (kk & 3) * kTileBytes;
+      const uint32_t cur_addr = lbase + slot_off(kk);
       // cur_addr is a multiple of 1024: the XOR after the add only touches bits 5..7
       if (part < 2) {
         const uint32_t a0 = cur_addr + aql;
@@ -369,6 +478,17 @@ void decode_kernel(DecodeArgs a) {
       }
     };
     auto prep_dma = [&](int kn, int32_t raw, int part) {
+      if constexpr (kF8) {
+        // per-lane source offsets are kernel constants: only bases change
+        if (part != 0) return;
+        const int32_t r = __builtin_amdgcn_readfirstlane(raw);
+        const int64_t phys = r < 0 ? 0 : (r >= a.num_pages ? a.num_pages - 1 : r);
+        dsrc = a.kv8 + phys * (int64_t)kF8PageBytes + (kn & 1) * kF8TileBytes;
+        m0n = lbase + slot_off(kn) + kRopeRegion + 1024 * wave_u;
+        m0c = lbase + kF8StageOff + (kn & 1) * kF8Stage + 4096 * wave_u;
+        m0s = lbase + kF8ScaleOff + (kn & 1) * kF8ScaleStage + 256 * wave_u;
+        return;
+      }
       // past the end of the segment (valid <= 0) every row maps to row 0 of the page
       const int valid = tile_valid(kn);
       if (part == 0) {
@@ -402,8 +522,14 @@ void decode_kernel(DecodeArgs a) {
     auto step = [&](const int k, auto first, auto last) __attribute__((always_inline)) {
       constexpr bool kFirst = decltype(first)::value;
       constexpr bool kMasked = decltype(last)::value;
-      if (kMasked || kFirst) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerTile));   // tile k+1 may still be in flight
+      if constexpr (kF8) {
+        // tile k was dequantised in the previous step (or before the first); the last
+        // step drains the dummy loads issued past the end
+        if (kMasked) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      } else {
+        if (kMasked || kFirst) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerTile));   // tile k+1 may still be in flight
+      }
       __syncthreads();   // tile k in LDS for all; P(k-1) visible; slot of tile k+2 and P buffer k%2 free
 
       // ---- scores S^T: 36 k-steps accumulated in one chain (dependent MFMAs on the same
@@ -437,61 +563,120 @@ void decode_kernel(DecodeArgs a) {
           const int bto = 4 * min(p0 + ((k + 3) >> 1), p1 - 1);
           int32_t bt_next;
           uint32_t m0v = m0n;
-          asm volatile(
-              "s_nop 1\n\t"
-              "s_load_dword %[btn], %[btp], %[bto]\n\t"
-              "ds_read_b128 %[t0], %[a0] offset:0\n\t"
-              "ds_read_b128 %[t1], %[a1] offset:0\n\t"
-              "ds_read_b128 %[t2], %[a2] offset:0\n\t"
-              "ds_read_b128 %[t3], %[a3] offset:0\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q0], 0\n\tds_read_b128 %[t0], %[a4] offset:0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d0], %[src] nt\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q1], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:0\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q2], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:0\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q3], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:0\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q4], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:256\n\ts_add_u32 m0, m0, 0xffff8000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d1], %[src] nt\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q5], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:256\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q6], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:256\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q7], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:256\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q8], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:256\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d2], %[src] nt\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q9], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:256\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q10], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:256\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q11], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:256\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q12], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:512\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d3], %[src] nt\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q13], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:512\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q14], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:512\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q15], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:512\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q16], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:512\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d4], %[src] nt\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q17], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:512\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q18], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:512\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q19], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:512\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q20], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:768\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d5], %[src] nt\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q21], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:768\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q22], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:768\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q23], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:768\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q24], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:768\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d6], %[src] nt\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q25], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:768\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q26], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:768\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q27], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:768\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q28], %[sa]\n\tds_read_b128 %[t0], %[r0] offset:0\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d7], %[src] nt\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q29], %[sa]\n\tds_read_b128 %[t1], %[r1] offset:0\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q30], %[sa]\n\tds_read_b128 %[t2], %[r2] offset:0\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q31], %[sa]\n\tds_read_b128 %[t3], %[r3] offset:0\n\t"
-              "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q32], %[sa]\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d8], %[src] nt\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q33], %[sa]\n\t"
-              "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q34], %[sa]\n\t"
-              "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q35], %[sa]\n\t"
-              "s_nop 7\n\ts_nop 5"
-              : [sa] "=&v"(sa), [t0] "=&v"(tq[0]), [t1] "=&v"(tq[1]), [t2] "=&v"(tq[2]), [t3] "=&v"(tq[3]), [btn] "=&s"(bt_next), "+{m0}"(m0v)
-              : [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]),
-                [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]),
-                [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]),
-                [q18] "v"(q[18]), [q19] "v"(q[19]), [q20] "v"(q[20]), [q21] "v"(q[21]), [q22] "v"(q[22]), [q23] "v"(q[23]),
-                [q24] "v"(q[24]), [q25] "v"(q[25]), [q26] "v"(q[26]), [q27] "v"(q[27]), [q28] "v"(q[28]), [q29] "v"(q[29]),
-                [q30] "v"(q[30]), [q31] "v"(q[31]), [q32] "v"(q[32]), [q33] "v"(q[33]), [q34] "v"(q[34]), [q35] "v"(q[35]),
-                [a0] "v"(aq[0]), [a1] "v"(aq[1]), [a2] "v"(aq[2]), [a3] "v"(aq[3]), [a4] "v"(aq[4]), [a5] "v"(aq[5]), [a6] "v"(aq[6]), [a7] "v"(aq[7]),
-                [r0] "v"(ar[0]), [r1] "v"(ar[1]), [r2] "v"(ar[2]), [r3] "v"(ar[3]),
-                [src] "s"(dsrc), [btp] "s"(btp), [bto] "s"(bto), [d0] "v"(dv[0]), [d1] "v"(dv[1]), [d2] "v"(dv[2]), [d3] "v"(dv[3]), [d4] "v"(dv[4]), [d5] "v"(dv[5]), [d6] "v"(dv[6]), [d7] "v"(dv[7]), [d8] "v"(dv[8])
-              : "memory");
+          if constexpr (kF8) {
+            uint32_t vtmp;   // source offset of code loads 1..3 (rows 2i further: 1312 i bytes)
+            asm volatile(
+                  "s_nop 1\n\t"
+                  "s_load_dword %[btn], %[btp], %[bto]\n\t"
+                  "ds_read_b128 %[t0], %[a0] offset:0\n\t"
+                  "ds_read_b128 %[t1], %[a1] offset:0\n\t"
+                  "ds_read_b128 %[t2], %[a2] offset:0\n\t"
+                  "ds_read_b128 %[t3], %[a3] offset:0\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q0], 0\n\tds_read_b128 %[t0], %[a4] offset:0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[vr], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q1], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:0\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q2], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:0\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q3], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:0\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q4], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:256\n\ts_mov_b32 m0, %[mc]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[vc], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q5], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:256\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q6], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:256\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q7], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:256\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q8], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:256\n\tv_add_u32 %[vt], 0x520, %[vc]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[vt], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q9], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:256\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q10], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:256\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q11], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:256\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q12], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:512\n\tv_add_u32 %[vt], 0xa40, %[vc]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[vt], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q13], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:512\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q14], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:512\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q15], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:512\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q16], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:512\n\tv_add_u32 %[vt], 0xf60, %[vc]\n\ts_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[vt], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q17], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:512\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q18], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:512\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q19], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:512\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q20], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:768\n\ts_mov_b32 m0, %[ms]\n\ts_nop 0\n\tglobal_load_lds_dword %[vs], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q21], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:768\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q22], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:768\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q23], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:768\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q24], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:768\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q25], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:768\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q26], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:768\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q27], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:768\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q28], %[sa]\n\tds_read_b128 %[t0], %[r0] offset:0\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q29], %[sa]\n\tds_read_b128 %[t1], %[r1] offset:0\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q30], %[sa]\n\tds_read_b128 %[t2], %[r2] offset:0\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q31], %[sa]\n\tds_read_b128 %[t3], %[r3] offset:0\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q32], %[sa]\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q33], %[sa]\n\t"
+                  "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q34], %[sa]\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q35], %[sa]\n\t"
+                  "s_nop 7\n\ts_nop 5"
+                  : [sa] "=&v"(sa), [t0] "=&v"(tq[0]), [t1] "=&v"(tq[1]), [t2] "=&v"(tq[2]), [t3] "=&v"(tq[3]), [btn] "=&s"(bt_next), "+{m0}"(m0v), [vt] "=&v"(vtmp)
+                  : [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]),
+                    [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]),
+                    [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]),
+                    [q18] "v"(q[18]), [q19] "v"(q[19]), [q20] "v"(q[20]), [q21] "v"(q[21]), [q22] "v"(q[22]), [q23] "v"(q[23]),
+                    [q24] "v"(q[24]), [q25] "v"(q[25]), [q26] "v"(q[26]), [q27] "v"(q[27]), [q28] "v"(q[28]), [q29] "v"(q[29]),
+                    [q30] "v"(q[30]), [q31] "v"(q[31]), [q32] "v"(q[32]), [q33] "v"(q[33]), [q34] "v"(q[34]), [q35] "v"(q[35]),
+                    [a0] "v"(aq[0]), [a1] "v"(aq[1]), [a2] "v"(aq[2]), [a3] "v"(aq[3]), [a4] "v"(aq[4]), [a5] "v"(aq[5]), [a6] "v"(aq[6]), [a7] "v"(aq[7]),
+                    [r0] "v"(ar[0]), [r1] "v"(ar[1]), [r2] "v"(ar[2]), [r3] "v"(ar[3]),
+                    [src] "s"(dsrc), [btp] "s"(btp), [bto] "s"(bto), [vr] "v"(f8r), [vc] "v"(f8c), [vs] "v"(f8s), [mc] "s"(m0c), [ms] "s"(m0s)
+                  : "memory");
+          } else {
+            asm volatile(
+                  "s_nop 1\n\t"
+                  "s_load_dword %[btn], %[btp], %[bto]\n\t"
+                  "ds_read_b128 %[t0], %[a0] offset:0\n\t"
+                  "ds_read_b128 %[t1], %[a1] offset:0\n\t"
+                  "ds_read_b128 %[t2], %[a2] offset:0\n\t"
+                  "ds_read_b128 %[t3], %[a3] offset:0\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q0], 0\n\tds_read_b128 %[t0], %[a4] offset:0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d0], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q1], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:0\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q2], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:0\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q3], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:0\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q4], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:256\n\ts_add_u32 m0, m0, 0xffff8000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d1], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q5], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:256\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q6], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:256\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q7], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:256\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q8], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:256\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d2], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q9], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:256\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q10], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:256\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q11], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:256\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q12], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:512\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d3], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q13], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:512\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q14], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:512\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q15], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:512\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q16], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:512\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d4], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q17], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:512\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q18], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:512\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q19], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:512\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q20], %[sa]\n\tds_read_b128 %[t0], %[a0] offset:768\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d5], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q21], %[sa]\n\tds_read_b128 %[t1], %[a1] offset:768\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q22], %[sa]\n\tds_read_b128 %[t2], %[a2] offset:768\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q23], %[sa]\n\tds_read_b128 %[t3], %[a3] offset:768\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q24], %[sa]\n\tds_read_b128 %[t0], %[a4] offset:768\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d6], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q25], %[sa]\n\tds_read_b128 %[t1], %[a5] offset:768\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q26], %[sa]\n\tds_read_b128 %[t2], %[a6] offset:768\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q27], %[sa]\n\tds_read_b128 %[t3], %[a7] offset:768\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q28], %[sa]\n\tds_read_b128 %[t0], %[r0] offset:0\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d7], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q29], %[sa]\n\tds_read_b128 %[t1], %[r1] offset:0\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q30], %[sa]\n\tds_read_b128 %[t2], %[r2] offset:0\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q31], %[sa]\n\tds_read_b128 %[t3], %[r3] offset:0\n\t"
+                  "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t0], %[q32], %[sa]\n\ts_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[d8], %[src] nt\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t1], %[q33], %[sa]\n\t"
+                  "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_32x32x16_bf16 %[sa], %[t2], %[q34], %[sa]\n\t"
+                  "v_mfma_f32_32x32x16_bf16 %[sa], %[t3], %[q35], %[sa]\n\t"
+                  "s_nop 7\n\ts_nop 5"
+                  : [sa] "=&v"(sa), [t0] "=&v"(tq[0]), [t1] "=&v"(tq[1]), [t2] "=&v"(tq[2]), [t3] "=&v"(tq[3]), [btn] "=&s"(bt_next), "+{m0}"(m0v)
+                  : [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]),
+                    [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]),
+                    [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]),
+                    [q18] "v"(q[18]), [q19] "v"(q[19]), [q20] "v"(q[20]), [q21] "v"(q[21]), [q22] "v"(q[22]), [q23] "v"(q[23]),
+                    [q24] "v"(q[24]), [q25] "v"(q[25]), [q26] "v"(q[26]), [q27] "v"(q[27]), [q28] "v"(q[28]), [q29] "v"(q[29]),
+                    [q30] "v"(q[30]), [q31] "v"(q[31]), [q32] "v"(q[32]), [q33] "v"(q[33]), [q34] "v"(q[34]), [q35] "v"(q[35]),
+                    [a0] "v"(aq[0]), [a1] "v"(aq[1]), [a2] "v"(aq[2]), [a3] "v"(aq[3]), [a4] "v"(aq[4]), [a5] "v"(aq[5]), [a6] "v"(aq[6]), [a7] "v"(aq[7]),
+                    [r0] "v"(ar[0]), [r1] "v"(ar[1]), [r2] "v"(ar[2]), [r3] "v"(ar[3]),
+                    [src] "s"(dsrc), [btp] "s"(btp), [bto] "s"(bto), [d0] "v"(dv[0]), [d1] "v"(dv[1]), [d2] "v"(dv[2]), [d3] "v"(dv[3]), [d4] "v"(dv[4]), [d5] "v"(dv[5]), [d6] "v"(dv[6]), [d7] "v"(dv[7]), [d8] "v"(dv[8])
+                  : "memory");
+          }
           bt_pref = bt_next;
         } else {
           asm volatile(
@@ -557,7 +742,7 @@ void decode_kernel(DecodeArgs a) {
       //     -> (pprev + offP0) XOR 32st, + 2048 hb
       //   B (c_KV columns, transposing reads), half r, column block c: token 16st + 8hi + 4r + e,
       //     chunk 16w + 4c + cb, byte 8 (lane & 1) -> (vprev + offV0) XOR (64c + 16r), + 16384 st + 4096 r
-      const unsigned char* vprev = lds + ((k == 0 ? 0 : k - 1) & 3) * kTileBytes;
+      const unsigned char* vprev = lds + slot_off(k == 0 ? 0 : k - 1);
       const unsigned char* pprev = pbuf + ((k - 1) & 1) * kPBytes;
       const uint32_t vb = lds_addr(vprev) + offV0, pb = lds_addr(pprev) + offP0;
       auto ld_v = [&](int st, int c) -> s16x8 {
@@ -639,9 +824,27 @@ void decode_kernel(DecodeArgs a) {
         if (!kFirst && st == 21) m_seen = fmaxf(m_seen, mx * a.scale_log2);
         if constexpr (!kMasked) {
           if (st >= 22 && st < 25) prep_qk(k + 1, st - 22);
-          if (st >= 25 && st < 28) prep_dma(k + 3, bt_pref, st - 25);
+          if constexpr (kF8) {
+            // dequantise tile k+1 (its loads went out one step ago; tile k+2's six are newer)
+            if (st == 24) {
+              asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+              f8_read(k + 1, 0);
+              f8_read(k + 1, 1);
+            }
+            if (st == 25) prep_dma(k + 3, bt_pref, 0);
+            if (st == 26) {
+              f8_read(k + 1, 2);
+              f8_read(k + 1, 3);
+            }
+            if (st >= 27 && st < 31) f8_write(lbase + slot_off(k + 1), st - 27);
+          } else {
+            if (st >= 25 && st < 28) prep_dma(k + 3, bt_pref, st - 25);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (kF8 && !kMasked) {
+        if (tile_valid(k + 1) < kTile) f8_zero_tail(lbase + slot_off(k + 1), tile_valid(k + 1));
       }
     };
 
@@ -657,7 +860,7 @@ void decode_kernel(DecodeArgs a) {
     // PV of the last tile.
     __syncthreads();   // P of the last tile visible
     {
-      const unsigned char* vlast = lds + (k & 3) * kTileBytes;
+      const unsigned char* vlast = lds + slot_off(k);
       const unsigned char* plast = pbuf + (k & 1) * kPBytes;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -846,13 +1049,13 @@ void gather_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv, const int32_t* bt,
-                         const int32_t* seqlens, uint16_t* out_latent, float* lse, int batch, int s_q, int max_blocks,
-                         int64_t num_pages, float scale, int wgs, const DecodePlanView& plan, hipStream_t s,
-                         hipEvent_t ev_plan_done, hipEvent_t ev_decode_done) {
+hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv, const unsigned char* kv8,
+                         const int32_t* bt, const int32_t* seqlens, uint16_t* out_latent, float* lse, int batch,
+                         int s_q, int max_blocks, int64_t num_pages, float scale, int wgs, const DecodePlanView& plan,
+                         hipStream_t s, hipEvent_t ev_plan_done, hipEvent_t ev_decode_done) {
   if (batch <= 0) return hipSuccess;
   DecodeArgs a;
-  a.q_abs = q_abs; a.q_r = q_r; a.kv = kv; a.bt = bt; a.seqlens = seqlens;
+  a.q_abs = q_abs; a.q_r = q_r; a.kv = kv; a.kv8 = kv8; a.bt = bt; a.seqlens = seqlens;
   a.out_latent = out_latent; a.lse = lse; a.cum = plan.cum; a.part_o = plan.part_o; a.part_lse = plan.part_lse;
   a.num_pages = num_pages; a.batch = batch; a.s_q = s_q; a.max_blocks = max_blocks;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -860,7 +1063,10 @@ hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint1
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_plan_done != nullptr && (e = hipEventRecord(ev_plan_done, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_kernel, dim3(wgs), dim3(kThreads), 0, s, a);
+  if (kv8 != nullptr)
+    hipLaunchKernelGGL(decode_kernel<true>, dim3(wgs), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_kernel<false>, dim3(wgs), dim3(kThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_decode_done != nullptr && (e = hipEventRecord(ev_decode_done, s)) != hipSuccess) return e;

@@ -169,14 +169,15 @@ mla_status collect_triples(std::vector<std::array<hipEvent_t, 3>>& v, size_t& us
 
 hipEvent_t* prof_append_slot() { return prof_triple_slot(g_prof.aev, g_prof.aused); }
 
-mla_status run_paged(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv, const int32_t* bt,
-                     const int32_t* seqlens, uint16_t* out_latent, float* lse, const mla_decode_params* p,
-                     unsigned char* ws, const WsLayout& L, int wgs, hipStream_t s, hipEvent_t* ev) {
+mla_status run_paged(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv, const unsigned char* kv8,
+                     const int32_t* bt, const int32_t* seqlens, uint16_t* out_latent, float* lse,
+                     const mla_decode_params* p, unsigned char* ws, const WsLayout& L, int wgs, hipStream_t s,
+                     hipEvent_t* ev) {
   mla::DecodePlanView plan;
   plan.cum = reinterpret_cast<int32_t*>(ws + L.cum);
   plan.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
   plan.part_o = reinterpret_cast<float*>(ws + L.part_o);
-  hipError_t e = mla::launch_decode(q_abs, q_r, kv, bt, seqlens, out_latent, lse, p->batch, p->s_q,
+  hipError_t e = mla::launch_decode(q_abs, q_r, kv, kv8, bt, seqlens, out_latent, lse, p->batch, p->s_q,
                                     p->max_blocks_per_seq, p->num_pages, p->scale, wgs, plan, s,
                                     ev ? ev[2] : nullptr, ev ? ev[3] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -258,20 +259,25 @@ extern "C" {
 size_t mla_append_workspace_size(const mla_append_params* p) {
   if (check_append(p) != MLA_OK) return 0;
   const int T = p->batch * p->s_q;
-  const size_t part = T > 0 ? round_up(mla::plan_append(T, p->d_model).part_bytes) : 0;
+  // the MXFP8 plan always has partials and is otherwise the bf16 one: enough for both
+  const size_t part = T > 0 ? round_up(mla::plan_append(T, p->d_model, true).part_bytes) : 0;
   return part > 0 ? part : 16;
 }
 
-mla_status mla_append_kv(const uint16_t* x, const uint16_t* w_a, const float* rope_table,
-                         const int32_t* block_table, const int32_t* seqlens, uint16_t* kv_blocks, uint16_t* q_r,
-                         const mla_append_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+mla_status append_impl(const uint16_t* x, const uint16_t* w_a, const float* rope_table, const int32_t* block_table,
+                       const int32_t* seqlens, uint16_t* kv_blocks, unsigned char* kv8, uint16_t* q_r,
+                       const mla_append_params* p, void* workspace, size_t workspace_bytes, void* stream) {
   mla_status st = check_append(p);
   if (st != MLA_OK) return st;
   if (p->batch == 0) return ok();
-  if (!x || !w_a || !rope_table || !block_table || !seqlens || !kv_blocks || !workspace)
+  if (!x || !w_a || !rope_table || !block_table || !seqlens || (!kv_blocks && !kv8) || !workspace)
     return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
-  if (!aligned16(x) || !aligned16(w_a) || !aligned16(rope_table) || !aligned16(kv_blocks) || !aligned16(workspace) ||
-      !aligned4(block_table) || !aligned4(seqlens) || !aligned16(q_r))
+  if (!aligned16(x) || !aligned16(w_a) || !aligned16(rope_table) || !aligned16(kv_blocks) || !aligned16(kv8) ||
+      !aligned16(workspace) || !aligned4(block_table) || !aligned4(seqlens) || !aligned16(q_r))
     return fail(MLA_ERR_MISALIGNED, "tensor or workspace not aligned (16 B; block_table and seqlens 4 B)");
   const size_t need = mla_append_workspace_size(p);
   if (workspace_bytes < need) return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
@@ -279,11 +285,41 @@ mla_status mla_append_kv(const uint16_t* x, const uint16_t* w_a, const float* ro
   hipEvent_t* ev = prof_append_slot();
   hipError_t e;
   if (ev != nullptr && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = mla::launch_append(x, w_a, rope_table, block_table, seqlens, kv_blocks, q_r, p->num_heads,
+  e = mla::launch_append(x, w_a, rope_table, block_table, seqlens, kv_blocks, kv8, q_r, p->num_heads,
                          static_cast<unsigned char*>(workspace), p->batch, p->s_q, p->d_model,
                          p->max_blocks_per_seq, p->num_pages, p->max_pos, s, ev ? ev[1] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   if (ev != nullptr && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_append_kv(const uint16_t* x, const uint16_t* w_a, const float* rope_table,
+                         const int32_t* block_table, const int32_t* seqlens, uint16_t* kv_blocks, uint16_t* q_r,
+                         const mla_append_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+  return append_impl(x, w_a, rope_table, block_table, seqlens, kv_blocks, nullptr, q_r, p, workspace,
+                     workspace_bytes, stream);
+}
+
+mla_status mla_append_kv_mxfp8(const uint16_t* x, const uint16_t* w_a, const float* rope_table,
+                               const int32_t* block_table, const int32_t* seqlens, uint8_t* kv_mxfp8,
+                               uint16_t* q_r, const mla_append_params* p, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return append_impl(x, w_a, rope_table, block_table, seqlens, nullptr, kv_mxfp8, q_r, p, workspace,
+                     workspace_bytes, stream);
+}
+
+mla_status mla_quantize_kv_mxfp8(const uint16_t* kv_blocks, uint8_t* kv_mxfp8, int64_t num_pages, void* stream) {
+  if (num_pages < 0 || num_pages > ((int64_t)1 << 31) / mla::kPage)
+    return fail(MLA_ERR_INVALID_ARG, "num_pages %lld", (long long)num_pages);
+  if (num_pages == 0) return ok();
+  if (!kv_blocks || !kv_mxfp8) return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(kv_blocks) || !aligned16(kv_mxfp8)) return fail(MLA_ERR_MISALIGNED, "tensor not 16-byte aligned");
+  hipError_t e = mla::launch_quantize_mxfp8(kv_blocks, kv_mxfp8, num_pages, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return ok();
 }
 
@@ -370,15 +406,20 @@ size_t mla_decode_workspace_size(const mla_decode_params* p, int32_t fused) {
   return layout(p, wgs, fused != 0).total;
 }
 
-mla_status mla_decode_paged(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv_blocks,
-                            const int32_t* block_table, const int32_t* seqlens, uint16_t* out_latent, float* lse,
-                            const mla_decode_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+mla_status decode_paged_impl(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv_blocks,
+                             const unsigned char* kv8, const int32_t* block_table, const int32_t* seqlens,
+                             uint16_t* out_latent, float* lse, const mla_decode_params* p, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   mla_status st = check_params(p);
   if (st != MLA_OK) return st;
   if (p->batch == 0) return ok();
-  if (!q_abs || !q_r || !kv_blocks || !block_table || !seqlens || !out_latent)
+  if (!q_abs || !q_r || (!kv_blocks && !kv8) || !block_table || !seqlens || !out_latent)
     return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
-  if (!aligned16(q_abs) || !aligned16(q_r) || !aligned16(kv_blocks) || !aligned16(block_table) ||
+  if (!aligned16(q_abs) || !aligned16(q_r) || !aligned16(kv_blocks) || !aligned16(kv8) || !aligned16(block_table) ||
       !aligned16(out_latent) || !aligned16(workspace) || (reinterpret_cast<uintptr_t>(seqlens) & 3u) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(MLA_ERR_MISALIGNED, "tensor or workspace not aligned (16 B; seqlens and lse 4 B)");
@@ -395,7 +436,7 @@ mla_status mla_decode_paged(const uint16_t* q_abs, const uint16_t* q_r, const ui
     if (e == hipSuccess) e = hipEventRecord(ev[1], s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
-  st = run_paged(q_abs, q_r, kv_blocks, block_table, seqlens, out_latent, lse, p,
+  st = run_paged(q_abs, q_r, kv_blocks, kv8, block_table, seqlens, out_latent, lse, p,
                  static_cast<unsigned char*>(workspace), L, wgs, s, ev);
   if (st == MLA_OK && ev != nullptr) {
     hipError_t e = hipEventRecord(ev[5], s);
@@ -404,15 +445,17 @@ mla_status mla_decode_paged(const uint16_t* q_abs, const uint16_t* q_r, const ui
   return st == MLA_OK ? ok() : st;
 }
 
-mla_status mla_decode(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* w_uk, const uint16_t* w_uv,
-                      const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens, uint16_t* out,
-                      float* lse, const mla_decode_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+mla_status decode_fused_impl(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* w_uk, const uint16_t* w_uv,
+                             const uint16_t* kv_blocks, const unsigned char* kv8, const int32_t* block_table,
+                             const int32_t* seqlens, uint16_t* out, float* lse, const mla_decode_params* p,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   mla_status st = check_params(p);
   if (st != MLA_OK) return st;
   if (p->batch == 0) return ok();
-  if (!q_c || !q_r || !w_uk || !w_uv || !kv_blocks || !block_table || !seqlens || !out)
+  if (!q_c || !q_r || !w_uk || !w_uv || (!kv_blocks && !kv8) || !block_table || !seqlens || !out)
     return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!aligned16(q_c) || !aligned16(q_r) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(kv_blocks) ||
+      !aligned16(kv8) ||
       !aligned16(block_table) || !aligned16(out) || !aligned16(workspace) ||
       (reinterpret_cast<uintptr_t>(seqlens) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(MLA_ERR_MISALIGNED, "tensor or workspace not aligned (16 B; seqlens and lse 4 B)");
@@ -433,12 +476,46 @@ mla_status mla_decode(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* 
   e = mla::launch_absorb_q(q_c, w_uk, q_abs, tokens, s);
   if (e != hipSuccess) return hip_fail(e, "absorb_q launch");
   if (ev != nullptr && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  st = run_paged(q_abs, q_r, kv_blocks, block_table, seqlens, ol, lse, p, ws, L, wgs, s, ev);
+  st = run_paged(q_abs, q_r, kv_blocks, kv8, block_table, seqlens, ol, lse, p, ws, L, wgs, s, ev);
   if (st != MLA_OK) return st;
   e = mla::launch_up_proj(ol, w_uv, out, tokens, s);
   if (e != hipSuccess) return hip_fail(e, "up_proj launch");
   if (ev != nullptr && (e = hipEventRecord(ev[5], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_paged(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv_blocks,
+                            const int32_t* block_table, const int32_t* seqlens, uint16_t* out_latent, float* lse,
+                            const mla_decode_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_paged_impl(q_abs, q_r, kv_blocks, nullptr, block_table, seqlens, out_latent, lse, p, workspace,
+                           workspace_bytes, stream);
+}
+
+mla_status mla_decode_paged_mxfp8(const uint16_t* q_abs, const uint16_t* q_r, const uint8_t* kv_mxfp8,
+                                  const int32_t* block_table, const int32_t* seqlens, uint16_t* out_latent,
+                                  float* lse, const mla_decode_params* p, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return decode_paged_impl(q_abs, q_r, nullptr, kv_mxfp8, block_table, seqlens, out_latent, lse, p, workspace,
+                           workspace_bytes, stream);
+}
+
+mla_status mla_decode(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* w_uk, const uint16_t* w_uv,
+                      const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens, uint16_t* out,
+                      float* lse, const mla_decode_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_fused_impl(q_c, q_r, w_uk, w_uv, kv_blocks, nullptr, block_table, seqlens, out, lse, p, workspace,
+                           workspace_bytes, stream);
+}
+
+mla_status mla_decode_mxfp8(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* w_uk, const uint16_t* w_uv,
+                            const uint8_t* kv_mxfp8, const int32_t* block_table, const int32_t* seqlens,
+                            uint16_t* out, float* lse, const mla_decode_params* p, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return decode_fused_impl(q_c, q_r, w_uk, w_uv, nullptr, kv_mxfp8, block_table, seqlens, out, lse, p, workspace,
+                           workspace_bytes, stream);
 }
 
 size_t mla_prefill_workspace_size(const mla_prefill_params* p) {

@@ -104,3 +104,33 @@ def assert_bf16_match(got_bits, exact, err, what, max_frac=1e-2):
     return frac
 
 
+# ---------------------------------------------------------------------------- cache-append rows
+
+
+def rotation_err(a, b, cos, sin):
+    """fp32 rounding bound of out = (a cos - b sin, a sin + b cos) on pairs (a, b)."""
+    m = np.abs(a) * np.abs(cos) + np.abs(b) * np.abs(sin)
+    n = np.abs(a) * np.abs(sin) + np.abs(b) * np.abs(cos)
+    out = np.empty(np.broadcast_shapes(a.shape, cos.shape)[:-1] + (2 * a.shape[-1],))
+    out[..., 0::2], out[..., 1::2] = 4 * U * m, 4 * U * n
+    return out
+
+
+def projection_err(x, w_a, table, positions):
+    """Error bound E of the appended rows [..., 576] before their final rounding: the
+    split fp32 sum of d products with 16x16x32 MFMAs (each output a chain of d/32
+    four-term dot products, and the partial-sum additions) is within
+    (d/32 + 64) * 2^-24 * sum|x w| of the exact sum; the k_R pairs add the fp32 rotation's
+    error, two products and a sum per output."""
+    d = x.shape[-1]
+    S = np.abs(oracle.bf16_bits_to_f64(x)) @ np.abs(oracle.bf16_bits_to_f64(w_a))
+    k = (d / 32 + 64) * U
+    pre = np.abs(oracle.down_project(x, w_a))[..., 512:]
+    t = np.asarray(table, dtype=np.float64)[np.asarray(positions)]
+    cos, sin = np.abs(t[..., :32]), np.abs(t[..., 32:])
+    E = k * S
+    sa, sb = S[..., 512::2], S[..., 513::2]
+    E[..., 512::2] = k * (sa * cos + sb * sin)
+    E[..., 513::2] = k * (sa * sin + sb * cos)
+    E[..., 512:] += rotation_err(pre[..., 0::2], pre[..., 1::2], cos, sin)
+    return E

@@ -177,8 +177,10 @@ def test_append_workspace_size(lib):
     assert size(d_model=768) == C + 3 * 4 * 576 * 4
     # 1024 tokens: 16 groups x 9 = 144 workgroups, two splits (a divisor of 28) reach 256
     assert size(batch=1, s_q=1024) == C + 2 * 1024 * 576 * 4
-    # prefill-sized: 64 token groups x 9 column blocks fill the chip, one split and no partials
-    assert size(batch=1, s_q=4096) == 16
+    # prefill-sized: 64 token groups x 9 column blocks fill the chip, one split; the bf16
+    # cache then needs no partials, the MXFP8 cache one set (its quantiser runs in the
+    # partial-sum kernel), and the size covers both
+    assert size(batch=1, s_q=4096) == 1 * 4096 * 576 * 4
     assert size(batch=0) == 16
     assert lib.mla_append_workspace_size(None) == 0
 
@@ -198,6 +200,31 @@ def test_append_argument_checks(lib):
     assert _append(lib, p, ws=MIS) == _lib.MLA_ERR_MISALIGNED
     assert _append(lib, p, q_r=MIS) == _lib.MLA_ERR_MISALIGNED
     assert _append(lib, _aparams(batch=0), (None,) * 6, ws=None, ws_bytes=0) == _lib.MLA_OK
+
+
+def test_mxfp8_argument_checks(lib):
+    q = lib.mla_quantize_kv_mxfp8
+    assert q(A, A, -1, None) == _lib.MLA_ERR_INVALID_ARG
+    assert q(None, None, 0, None) == _lib.MLA_OK
+    assert q(None, A, 4, None) == _lib.MLA_ERR_INVALID_ARG
+    assert q(A, MIS, 4, None) == _lib.MLA_ERR_MISALIGNED
+    p = _params()
+    dp = lib.mla_decode_paged_mxfp8
+    assert dp(A, A, A, A, A, A, None, ctypes.byref(_params(s_q=257)), A, 1 << 30, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert dp(A, A, None, A, A, A, None, ctypes.byref(p), A, 1 << 30, None) == _lib.MLA_ERR_INVALID_ARG
+    assert dp(A, A, MIS, A, A, A, None, ctypes.byref(p), A, 1 << 30, None) == _lib.MLA_ERR_MISALIGNED
+    assert dp(A, A, A, A, A, A, None, ctypes.byref(p), A, 16, None) == _lib.MLA_ERR_WORKSPACE
+    assert dp(None, None, None, None, None, None, None, ctypes.byref(_params(batch=0)), None, 0, None) == _lib.MLA_OK
+    fd = lib.mla_decode_mxfp8
+    assert fd(A, A, A, A, None, A, A, A, None, ctypes.byref(p), A, 1 << 30, None) == _lib.MLA_ERR_INVALID_ARG
+    assert fd(A, A, A, A, MIS, A, A, A, None, ctypes.byref(p), A, 1 << 30, None) == _lib.MLA_ERR_MISALIGNED
+    assert fd(A, A, A, A, A, A, A, A, None, ctypes.byref(p), A, 16, None) == _lib.MLA_ERR_WORKSPACE
+    ap = _aparams()
+    aq = lib.mla_append_kv_mxfp8
+    assert aq(A, A, A, A, A, None, None, ctypes.byref(ap), A, 1 << 30, None) == _lib.MLA_ERR_INVALID_ARG
+    assert aq(A, A, A, A, A, MIS, None, ctypes.byref(ap), A, 1 << 30, None) == _lib.MLA_ERR_MISALIGNED
+    assert aq(A, A, A, A, A, A, None, ctypes.byref(_aparams(d_model=100)), A, 1 << 30, None) == \
+        _lib.MLA_ERR_UNSUPPORTED
 
 
 def test_rope_argument_checks(lib):

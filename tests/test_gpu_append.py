@@ -18,7 +18,8 @@ import pytest
 import oracle
 from synth import make_append_inputs, make_custom, make_inputs
 
-from ._gpu import U, assert_bf16_match, assert_close, dev_bf16, dev_i32, host_bits, require_gpu
+from ._gpu import (U, assert_bf16_match, assert_close, dev_bf16, dev_i32, host_bits, projection_err,
+                   require_gpu, rotation_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -46,31 +47,6 @@ def _ordered(bits):
     b = bits.astype(np.int32)
     mag = b & 0x7FFF
     return np.where(b & 0x8000, -mag, mag)
-
-
-def rotation_err(a, b, cos, sin):
-    """fp32 rounding bound of out = (a cos - b sin, a sin + b cos) on pairs (a, b)."""
-    m = np.abs(a) * np.abs(cos) + np.abs(b) * np.abs(sin)
-    n = np.abs(a) * np.abs(sin) + np.abs(b) * np.abs(cos)
-    out = np.empty(np.broadcast_shapes(a.shape, cos.shape)[:-1] + (2 * a.shape[-1],))
-    out[..., 0::2], out[..., 1::2] = 4 * U * m, 4 * U * n
-    return out
-
-
-def projection_err(x, w_a, table, positions):
-    """Error bound E of the appended rows (see the module docstring), [..., 576]."""
-    d = x.shape[-1]
-    S = np.abs(oracle.bf16_bits_to_f64(x)) @ np.abs(oracle.bf16_bits_to_f64(w_a))
-    k = (d / 32 + 64) * U
-    pre = np.abs(oracle.down_project(x, w_a))[..., 512:]
-    t = np.asarray(table, dtype=np.float64)[np.asarray(positions)]
-    cos, sin = np.abs(t[..., :32]), np.abs(t[..., 32:])
-    E = k * S
-    sa, sb = S[..., 512::2], S[..., 513::2]
-    E[..., 512::2] = k * (sa * cos + sb * sin)
-    E[..., 513::2] = k * (sa * sin + sb * cos)
-    E[..., 512:] += rotation_err(pre[..., 0::2], pre[..., 1::2], cos, sin)
-    return E
 
 
 def test_rope_table_matches_oracle(tables):
