@@ -35,8 +35,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 _CSRC = "mla_latent_kv_04_amd/csrc/"
 TRAFFIC = {
     "decode": dict(file="decode_kernel_c3_b64_traffic.md", kernels=("decode_kernel",),
-                   sources=(_CSRC + "decode.hip", _CSRC + "common.h"),
+                   sources=(_CSRC + "decode.hip", _CSRC + "common.h", _CSRC + "mxfp8.h"),
                    title="decode_kernel: paged MLA decode, batch 64, seq_len U[1024,32768]"),
+    "mxfp8": dict(file="decode_kernel_mxfp8_c3_b64_traffic.md", kernels=("decode_kernel",),
+                  sources=(_CSRC + "decode.hip", _CSRC + "common.h", _CSRC + "mxfp8.h"),
+                  title="decode_kernel over the MXFP8 cache: paged MLA decode, batch 64, seq_len U[1024,32768]"),
     "append": dict(file="append_kernel_c3_b64_traffic.md", kernels=("append_kernel", "append_finalize_kernel"),
                    sources=(_CSRC + "append.hip", _CSRC + "append.h", _CSRC + "common.h"),
                    title="cache append: 64 new tokens of the batch-64 workload, d = 7168 (both kernels of a call)"),
@@ -100,6 +103,31 @@ def _device_pool(num_pages, seed, torch):
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
     return torch.randn((num_pages, 64, 576), dtype=torch.bfloat16, device="cuda", generator=g)
+
+
+MXFP8_ROW_BYTES = 656   # MXFP8 cache row: 512 E4M3 codes + 16 E8M0 scale bytes + 64 bf16 of k_R
+
+
+def run_mxfp8(inp, pool_dev, torch, mla, steps, warmup):
+    """Time the paged decode of a workload over its MXFP8 cache (made on the device from
+    the bf16 cache); returns a result dict like run_paged's."""
+    pool8 = mla.quantize_kv_mxfp8(pool_dev)
+    q_abs = mla.absorb_q(_dev_bf16(inp.q_c, torch), _dev_bf16(inp.w_uk, torch))
+    q_r = _dev_bf16(inp.q_r, torch)
+    sl, bt = _dev_i32(inp.seqlens, torch), _dev_i32(inp.block_table, torch)
+    B, s_q = inp.batch, inp.s_q
+    out = torch.empty(B, s_q, 128, 512, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, s_q, 128, dtype=torch.float32, device="cuda")
+    params = mla.make_params(B, s_q, inp.max_blocks, int(pool8.shape[0]), inp.scale)
+    ws = torch.empty(mla.workspace_size(params), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        mla.decode_paged_mxfp8(q_abs, q_r, pool8, bt, sl, scale=inp.scale, out_latent=out, lse=lse, workspace=ws)
+
+    ms, per = _time_calls(step, steps, warmup, torch, mla)
+    del pool8
+    cache_bytes = int(inp.seqlens.astype(np.int64).sum()) * MXFP8_ROW_BYTES
+    return dict(ms=ms, per=per, cache_bytes=cache_bytes, tokens=int(inp.seqlens.sum()), queries=B * s_q)
 
 
 def run_paged(inp, pool_dev, torch, mla, steps, warmup, layers=1, pages_per_layer=None):
@@ -392,6 +420,28 @@ def main():
     log(f"[bench] c3 fused: {fms * 1e3:.1f} us/step; kernels us: "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in fper.items()))
 
+    # ---- the same workload over its MXFP8 cache
+    f8 = run_mxfp8(inp, pool, torch, mla, args.steps, args.warmup)
+    f8_dec = f8["per"]["decode"]
+    f8_ach = f8["cache_bytes"] / (f8_dec * 1e-3) / 1e9
+    traffic8 = load_traffic("mxfp8")
+    mx = {
+        "workload": "the batch-64 workload above, cache in MXFP8 (E4M3 codes, one E8M0 scale per 32 latent "
+                    "values, bf16 k_R: 656 B per token)",
+        "us_per_step": round(f8["ms"] * 1e3, 2),
+        "kernels_us": {k: round(v * 1e3, 2) for k, v in f8["per"].items() if v > 0},
+        "cache_bytes_per_step": f8["cache_bytes"],
+        "cache_GBps": round(f8["cache_bytes"] / (f8["ms"] * 1e-3) / 1e9, 1),
+        "kv_tokens_per_s": round(f8["tokens"] / (f8["ms"] * 1e-3), 1),
+        "step_speedup_vs_bf16_cache": round(ms / f8["ms"], 4),
+        "roofline": {"bound": "hbm", "achieved": round(f8_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(f8_ach / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic8 is None else round(traffic8["fetch"] + traffic8["write"]),
+                     "traffic_split": traffic8, "kernel": "decode_kernel (MXFP8 variant)",
+                     "algorithmic_bytes_per_launch": f8["cache_bytes"]},
+    }
+    log(f"[bench] c3 mxfp8: {mx}")
+
     # ---- other workloads (timing only; parity is in the tests)
     others = {}
     for name in [x for x in args.extra.split(",") if x and x != "none"]:
@@ -459,6 +509,7 @@ def main():
         "other_workloads": others,
         "cache_append": app,
         "prefill": pre,
+        "mxfp8_cache": mx,
     }
     print(json.dumps(line), flush=True)
 
@@ -511,6 +562,14 @@ def pmc_run(steps, warmup, kind="decode"):
         bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
         for _ in range(warmup + steps):
             mla.decode_paged(qa, qr, pool, bt, sl, scale=inp.scale)
+    elif kind == "mxfp8":
+        inp = _workload_from_synth("c3", torch, with_host_pool=False)
+        pool8 = mla.quantize_kv_mxfp8(_device_pool(inp.num_pages, inp.seed, torch))
+        qa = torch.randn((inp.batch, 1, 128, 512), device="cuda").to(torch.bfloat16)
+        qr = torch.randn((inp.batch, 1, 128, 64), device="cuda").to(torch.bfloat16)
+        bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
+        for _ in range(warmup + steps):
+            mla.decode_paged_mxfp8(qa, qr, pool8, bt, sl, scale=inp.scale)
     elif kind == "append":
         from synth import make_append_inputs
         inp = _workload_from_synth("c3", torch, with_host_pool=False)
@@ -587,6 +646,8 @@ def summarize_pmc(fetch_dir, write_dir, command, kind="decode"):
         out[name] = {"kib": total, "copy_kib": cop_kib, "factor": factor, "bytes": total * 1024.0 * factor}
     if kind == "decode":
         alg, alg_note = 1166687 * ROW_BYTES, "cache rows read once"
+    elif kind == "mxfp8":
+        alg, alg_note = 1166687 * MXFP8_ROW_BYTES, "MXFP8 cache rows read once"
     elif kind == "append":
         alg, alg_note = append_algorithmic_bytes(64), "W_A, x, rows written, table rows, table entries and lengths"
     else:
