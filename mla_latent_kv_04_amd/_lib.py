@@ -114,6 +114,11 @@ def load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -m mla_latent_kv_04_amd.build` "
             "(the MLA decode path has no CPU fallback)")
+    # torch first: the library registers its kernels with the HIP runtime when it is
+    # opened, and the process must use one runtime -- the one torch brings for the
+    # device memory and streams the library works on.  Opened the other way round
+    # (library, then torch) the library's calls found no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     pp = ctypes.POINTER(DecodeParams)
