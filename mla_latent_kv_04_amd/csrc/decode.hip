@@ -369,24 +369,28 @@ void decode_kernel(DecodeArgs a) {
     // f8l = 1024 h + (32q ^ 64h) is a lane constant and u_j = 128 (j & 1) + 16 ((2w + j/2) & 3)
     // is uniform; chunk 2q + 1 sits at that offset XOR 16.
     u32x4 f8v[4];
-    uint32_t f8sc[4], f8l = 0;
-    auto f8_read = [&](int kc, int j) {
+    uint32_t f8sc[4];
+    // Per-tile lane addresses (set by f8_lanes, kept through the tile's dequantisation):
+    // this lane's code chunk in the wave's staging, its scale byte (row l/32, block
+    // (l%32)/2 of the wave's scale group) and f8l.
+    uint32_t f8cb = 0, f8sb = 0, f8l = 0;
+    auto f8_lanes = [&](int kc) {
       const uint32_t ln = (uint32_t)opaque_lane();
-      if (j == 0) f8l = ((ln >> 5) << 10) | ((32u * (ln & 31)) ^ ((ln >> 5) << 6));
-      const uint32_t cb = lbase + kF8StageOff + (kc & 1) * kF8Stage + 4096 * wave_u + 16 * ln;
-      f8v[j] = __builtin_bit_cast(u32x4, lds_read_b128_at(cb + 1024 * j));
-      const uint32_t sbase = lbase + kF8ScaleOff + (kc & 1) * kF8ScaleStage + 256 * wave_u + 16 * (ln >> 5) +
-                             ((ln & 31) >> 1);
-      f8sc[j] = *(MLA_LDS const unsigned char*)(sbase + 32 * j);
+      f8cb = lbase + kF8StageOff + (kc & 1) * kF8Stage + 4096 * wave_u + 16u * ln;
+      f8sb = lbase + kF8ScaleOff + (kc & 1) * kF8ScaleStage + 256 * wave_u + 16u * (ln >> 5) + ((ln & 31) >> 1);
+      f8l = ((ln >> 5) << 10) | ((32u * (ln & 31)) ^ ((ln >> 5) << 6));
     };
-    auto f8_write = [&](uint32_t slot_base, int j) {
+    auto f8_read = [&](int j) {
+      f8v[j] = __builtin_bit_cast(u32x4, lds_read_b128_at(f8cb + 1024 * j));
+      f8sc[j] = *(MLA_LDS const unsigned char*)(f8sb + 32 * j);
+    };
+    // Half h of part j: codes 8h .. 8h+7 of the lane's chunk -> bf16 chunk 2q + h.
+    auto f8_write = [&](uint32_t slot_base, int j, int h) {
       const uint32_t u = 128u * (j & 1) + 16u * ((2 * wave_u + (j >> 1)) & 3);
-      const uint32_t lo_addr = slot_base + 1024 * (8 * wave_u + 2 * j) + (f8l ^ u);
+      const uint32_t addr = (slot_base + 1024 * (8 * wave_u + 2 * j) + (f8l ^ u)) ^ (16u * h);
       const float sc = mx_scale_f32(f8sc[j]);
-      const u32x2 d0 = e4m3x4_to_bf16(f8v[j][0], sc), d1 = e4m3x4_to_bf16(f8v[j][1], sc);
-      const u32x2 d2 = e4m3x4_to_bf16(f8v[j][2], sc), d3 = e4m3x4_to_bf16(f8v[j][3], sc);
-      *(MLA_LDS u32x4*)lo_addr = u32x4{d0[0], d0[1], d1[0], d1[1]};
-      *(MLA_LDS u32x4*)(lo_addr ^ 16u) = u32x4{d2[0], d2[1], d3[0], d3[1]};
+      const u32x2 d0 = e4m3x4_to_bf16(f8v[j][2 * h], sc), d1 = e4m3x4_to_bf16(f8v[j][2 * h + 1], sc);
+      *(MLA_LDS u32x4*)addr = u32x4{d0[0], d0[1], d1[0], d1[1]};
     };
     // Rows at or past `valid` (only in a segment's last tile) are overwritten with zeros.
     auto f8_zero_tail = [&](uint32_t slot_base, int valid) {
@@ -403,11 +407,15 @@ void decode_kernel(DecodeArgs a) {
       }
     };
     auto f8_convert_all = [&](int kc) {
+      f8_lanes(kc);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) f8_read(kc, j);
+      for (int j = 0; j < 4; ++j) f8_read(j);
       const uint32_t sb = lbase + slot_off(kc);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) f8_write(sb, j);
+      for (int j = 0; j < 4; ++j) {
+        f8_write(sb, j, 0);
+        f8_write(sb, j, 1);
+      }
       if (tile_valid(kc) < kTile) f8_zero_tail(sb, tile_valid(kc));
     };
 
@@ -825,18 +833,24 @@ void decode_kernel(DecodeArgs a) {
         if constexpr (!kMasked) {
           if (st >= 22 && st < 25) prep_qk(k + 1, st - 22);
           if constexpr (kF8) {
-            // dequantise tile k+1 (its loads went out one step ago; tile k+2's six are newer)
+            // Dequantisation of tile k+1 (its loads went out early in step k-1; tile k+2's
+            // six are newer): lane addresses at stage 23, parts 0, 1 read at 24, parts 2, 3
+            // at 26, each part's two halves converted and stored at stages 27 .. 30.
+            if (st == 23) f8_lanes(k + 1);
             if (st == 24) {
               asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-              f8_read(k + 1, 0);
-              f8_read(k + 1, 1);
+              f8_read(0);
+              f8_read(1);
             }
             if (st == 25) prep_dma(k + 3, bt_pref, 0);
             if (st == 26) {
-              f8_read(k + 1, 2);
-              f8_read(k + 1, 3);
+              f8_read(2);
+              f8_read(3);
             }
-            if (st >= 27 && st < 31) f8_write(lbase + slot_off(k + 1), st - 27);
+            if (st >= 27 && st < 31) {
+              f8_write(lbase + slot_off(k + 1), st - 27, 0);
+              f8_write(lbase + slot_off(k + 1), st - 27, 1);
+            }
           } else {
             if (st >= 25 && st < 28) prep_dma(k + 3, bt_pref, st - 25);
           }
