@@ -83,7 +83,7 @@ __device__ __forceinline__ s16x8 lds_read_b128_at(uint32_t addr) {
 // Host-side launch helpers (defined in the kernel translation units).
 struct DecodePlanView {
   int32_t* cum;       // [units + 1] prefix sums of pages per work unit
-  float* part_o;      // [2 * wgs, 128, 512] normalised partial outputs
+  uint16_t* part_o;   // [2 * wgs, 128, 512] normalised partial outputs, bf16
   float* part_lse;    // [2 * wgs, 128] log2-domain lse of the partials
 };
 

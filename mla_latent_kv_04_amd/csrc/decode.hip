@@ -45,7 +45,7 @@ struct DecodeArgs {
   uint16_t* out_latent;
   float* lse;
   const int32_t* cum;
-  float* part_o;
+  uint16_t* part_o;    // [2W, 128, 512] bf16 normalised partial outputs
   float* part_lse;
   int64_t num_pages;
   int batch, s_q, max_blocks;
@@ -474,13 +474,20 @@ void decode_kernel(DecodeArgs a) {
     // Each preparation comes in three parts so that it can be spread over stages.
     auto prep_qk = [&](int kk, int part) {
       const uint32_t cur_addr = lbase + slot_off(kk);
+      // the MXFP8 variant has fewer registers to spare: it recomputes the lane offsets
+      uint32_t ql = aql, rl = arl;
+      if constexpr (kF8) {
+        const int ln = opaque_lane(), t = ln & 31, h = ln >> 5;
+        ql = t * 1024 + 16 * (h ^ swz_lat(t));
+        rl = kRopeRegion + t * 128 + 16 * (h ^ swz_rope(t));
+      }
       // cur_addr is a multiple of 1024: the XOR after the add only touches bits 5..7
       if (part < 2) {
-        const uint32_t a0 = cur_addr + aql;
+        const uint32_t a0 = cur_addr + ql;
 #pragma unroll
         for (int q2 = 4 * part; q2 < 4 * part + 4; ++q2) aq[q2] = a0 ^ (32u * q2);
       } else {
-        const uint32_t r0 = cur_addr + arl;
+        const uint32_t r0 = cur_addr + rl;
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) ar[q2] = r0 ^ (32u * q2);
       }
@@ -834,19 +841,12 @@ void decode_kernel(DecodeArgs a) {
           if (st >= 22 && st < 25) prep_qk(k + 1, st - 22);
           if constexpr (kF8) {
             // Dequantisation of tile k+1 (its loads went out early in step k-1; tile k+2's
-            // six are newer): lane addresses at stage 23, parts 0, 1 read at 24, parts 2, 3
-            // at 26, each part's two halves converted and stored at stages 27 .. 30.
+            // six are newer): lane addresses at stage 23, part j read at stage 24 + j and
+            // its two halves converted and stored at stage 27 + j.
             if (st == 23) f8_lanes(k + 1);
-            if (st == 24) {
-              asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-              f8_read(0);
-              f8_read(1);
-            }
+            if (st == 24) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+            if (st >= 24 && st < 28) f8_read(st - 24);
             if (st == 25) prep_dma(k + 3, bt_pref, 0);
-            if (st == 26) {
-              f8_read(2);
-              f8_read(3);
-            }
             if (st >= 27 && st < 31) {
               f8_write(lbase + slot_off(k + 1), st - 27, 0);
               f8_write(lbase + slot_off(k + 1), st - 27, 1);
@@ -921,9 +921,12 @@ void decode_kernel(DecodeArgs a) {
         const float* lrow = lsum + 4 * hi;   // head 32hb + 8(j/4) + (j%4) from here
         constexpr int kStagePitch = 544;
         unsigned char* stage = lds + 1024 + wave_u * (32 * kStagePitch);
-        const size_t obase = (size_t)hi * kLatent + wave_u * 128 + 4 * l32;
+        const int eln = opaque_lane();      // lane values recomputed here, not kept live
+        const size_t obase = (size_t)(eln >> 5) * kLatent + wave_u * 128 + 4 * (eln & 31);
+        // complete units go straight to out_latent, pieces of split units to their
+        // partial slot; both as bf16
         uint16_t* ob16 = a.out_latent + (size_t)u * kHeads * kLatent + obase;
-        float* ob32 = a.part_o + (size_t)(slot < 0 ? 0 : slot) * kHeads * kLatent + obase;
+        uint16_t* obp = a.part_o + (size_t)(slot < 0 ? 0 : slot) * kHeads * kLatent + obase;
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
           f32x16 il;
@@ -941,10 +944,11 @@ void decode_kernel(DecodeArgs a) {
           for (int i = 0; i < 16; ++i) {
             const f32x4 x = *(const f32x4*)(stage + (2 * i + hi) * kStagePitch + 16 * l32);
             const size_t row = (size_t)(32 * hb + 2 * i) * kLatent;
+            const u32x2 w = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
             if (slot < 0) {
-              *(u32x2*)(ob16 + row) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+              *(u32x2*)(ob16 + row) = w;
             } else {
-              *(f32x4*)(ob32 + row) = x;
+              *(u32x2*)(obp + row) = w;
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -1003,24 +1007,31 @@ void combine_kernel(DecodeArgs a, int W) {
   const int g0 = ubeg / chunk, g1 = (uend - 1) / chunk;
   if (g0 == g1) return;
 
-  auto load = [&](int gg, f32x4 (&x)[4], float& l) {
+  auto load = [&](int gg, u32x2 (&x)[4], float& l) {
     const int slot = fragment_slot(gg, g0, chunk, ubeg);
-    const float* src = a.part_o + ((size_t)slot * kHeads + head) * kLatent + col;
+    const uint16_t* src = a.part_o + ((size_t)slot * kHeads + head) * kLatent + col;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) x[v] = __builtin_nontemporal_load((const f32x4*)(src + 128 * v));
+    for (int v = 0; v < 4; ++v) x[v] = __builtin_nontemporal_load((const u32x2*)(src + 128 * v));
     l = a.part_lse[(size_t)slot * kHeads + head];
   };
-  f32x4 acc[4], fa[4], fb[4];
+  auto widen = [](const u32x2& x) {
+    return f32x4{bf2f((uint16_t)(x[0] & 0xFFFFu)), bf2f((uint16_t)(x[0] >> 16)), bf2f((uint16_t)(x[1] & 0xFFFFu)),
+                 bf2f((uint16_t)(x[1] >> 16))};
+  };
+  f32x4 acc[4];
+  u32x2 a0[4], fa[4], fb[4];
   float m, la, lb;
-  load(g0, acc, m);
+  load(g0, a0, m);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) acc[v] = widen(a0[v]);
   float wsum = 1.f;
-  auto merge = [&](const f32x4 (&x)[4], float l) {
+  auto merge = [&](const u32x2 (&x)[4], float l) {
     // rescale the running sum to the new maximum (base 2), add fragment x
     const float mn = fmaxf(m, l);
     const float s_old = exp2f(m - mn), s_new = exp2f(l - mn);
     wsum = wsum * s_old + s_new;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = acc[v] * s_old + x[v] * s_new;
+    for (int v = 0; v < 4; ++v) acc[v] = acc[v] * s_old + widen(x[v]) * s_new;
     m = mn;
   };
   // two register buffers: the load of fragment gg+1 is in flight while gg merges

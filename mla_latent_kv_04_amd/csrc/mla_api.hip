@@ -95,7 +95,7 @@ WsLayout layout(const mla_decode_params* p, int wgs, bool fused) {
   L.part_lse = off;
   off += round_up((size_t)2 * wgs * mla::kHeads * sizeof(float));
   L.part_o = off;
-  off += round_up((size_t)2 * wgs * mla::kHeads * mla::kLatent * sizeof(float));
+  off += round_up((size_t)2 * wgs * mla::kHeads * mla::kLatent * 2);
   L.q_abs = off;
   if (fused) off += round_up(units * mla::kHeads * mla::kLatent * 2);
   L.out_latent = off;
@@ -176,7 +176,7 @@ mla_status run_paged(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t*
   mla::DecodePlanView plan;
   plan.cum = reinterpret_cast<int32_t*>(ws + L.cum);
   plan.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
-  plan.part_o = reinterpret_cast<float*>(ws + L.part_o);
+  plan.part_o = reinterpret_cast<uint16_t*>(ws + L.part_o);
   hipError_t e = mla::launch_decode(q_abs, q_r, kv, kv8, bt, seqlens, out_latent, lse, p->batch, p->s_q,
                                     p->max_blocks_per_seq, p->num_pages, p->scale, wgs, plan, s,
                                     ev ? ev[2] : nullptr, ev ? ev[3] : nullptr);

@@ -92,9 +92,9 @@ def test_misaligned_tensors(lib, which):
 def test_workspace_checks(lib):
     p = _params()
     need = lib.mla_decode_workspace_size(ctypes.byref(p), 0)
-    # cum [B*s_q+1] int32, partial lse [2W,128] fp32, partial O [2W,128,512] fp32 (each 256-B aligned)
+    # cum [B*s_q+1] int32, partial lse [2W,128] fp32, partial O [2W,128,512] bf16 (each 256-B aligned)
     W = p.num_splits
-    assert need == 256 + 2 * W * 128 * 4 + 2 * W * 128 * 512 * 4
+    assert need == 256 + 2 * W * 128 * 4 + 2 * W * 128 * 512 * 2
     fused = lib.mla_decode_workspace_size(ctypes.byref(p), 1)
     assert fused == need + 2 * (2 * 128 * 512 * 2)
     assert _paged(lib, p, ws=A, ws_bytes=need - 1) == _lib.MLA_ERR_WORKSPACE
