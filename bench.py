@@ -68,7 +68,9 @@ WARM_SECONDS = 1.5   # untimed decode work before each timed region: the clock s
 def _time_calls(fn, steps, warmup, torch, mla):
     """Warm up (`warmup` calls, and at least WARM_SECONDS of calls so that the
     engine clock has settled), then time exactly `steps` calls between two
-    synchronisations.  Returns (ms per call from stream events, per-kernel ms per call)."""
+    synchronisations, without any other instrumentation; then run `steps` more
+    calls with the library's per-kernel events for the breakdown.  Returns (ms per
+    call from the stream events around the first run, per-kernel ms per call)."""
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
@@ -79,13 +81,18 @@ def _time_calls(fn, steps, warmup, torch, mla):
         torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    # the step time: nothing but the calls between the two events
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # the per-kernel split: the same calls again with the library's per-kernel events
     with mla.KernelTimer() as kt:
-        e0.record()
         for i in range(steps):
             fn(i)
-        e1.record()
         torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
     per = {k: v / max(kt.calls, 1) for k, v in kt.ms.items()}
     return ms, per
 
