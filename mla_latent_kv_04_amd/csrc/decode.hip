@@ -11,8 +11,9 @@
 // contiguous range [g*chunk, (g+1)*chunk) of that list (chunk = ceil(total/W)),
 // so every compute unit streams the same number of pages whatever the length
 // mix.  A unit that lies inside one range is finished in place; a unit cut by
-// range borders leaves one normalised partial per piece (slot 2g for the first
-// segment of workgroup g, 2g+1 for its last), merged by log-sum-exp afterwards.
+// range borders leaves one normalised partial per piece (bf16, with an fp32 lse;
+// slot 2g for the first segment of workgroup g, 2g+1 for its last), merged by
+// log-sum-exp afterwards.
 //
 // Workgroup: 256 threads = 4 waves, one per SIMD.  Pages are processed as
 // 32-token tiles (36 KiB) copied HBM -> LDS with direct 16-byte loads
@@ -25,6 +26,11 @@
 // and a RoPE region (8 chunks per token), each with an XOR swizzle of the chunk
 // index that keeps both the row reads of QK (16 tokens, one chunk) and the
 // 4-row transposing reads of PV free of bank conflicts.
+//
+// The same kernel decodes the MXFP8 cache of mxfp8.h (decode_kernel<true>): the
+// tiles' codes and scales are staged per wave and dequantised to the bf16 tile
+// layout above in a ring of 3 slots (see the constants kF8*); everything from the
+// tile slot on is the bf16 kernel's.
 #include "common.h"
 #include "mxfp8.h"
 
