@@ -522,13 +522,18 @@ def main():
 
 
 def kernel_source_hash(kind="decode"):
-    """sha256 over the sources a kernel family is compiled from: counter readings taken
-    with other sources do not describe the kernels being timed."""
+    """sha256 over the code of the sources a kernel family is compiled from (comments
+    and blank space left out): counter readings taken with other code do not describe
+    the kernels being timed."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in TRAFFIC[kind]["sources"]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
