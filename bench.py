@@ -572,16 +572,14 @@ def pmc_run(steps, warmup, kind="decode"):
         qa = torch.randn((inp.batch, 1, 128, 512), device="cuda").to(torch.bfloat16)
         qr = torch.randn((inp.batch, 1, 128, 64), device="cuda").to(torch.bfloat16)
         bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
-        for _ in range(warmup + steps):
-            mla.decode_paged(qa, qr, pool, bt, sl, scale=inp.scale)
+        call = lambda: mla.decode_paged(qa, qr, pool, bt, sl, scale=inp.scale)
     elif kind == "mxfp8":
         inp = _workload_from_synth("c3", torch, with_host_pool=False)
         pool8 = mla.quantize_kv_mxfp8(_device_pool(inp.num_pages, inp.seed, torch))
         qa = torch.randn((inp.batch, 1, 128, 512), device="cuda").to(torch.bfloat16)
         qr = torch.randn((inp.batch, 1, 128, 64), device="cuda").to(torch.bfloat16)
         bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
-        for _ in range(warmup + steps):
-            mla.decode_paged_mxfp8(qa, qr, pool8, bt, sl, scale=inp.scale)
+        call = lambda: mla.decode_paged_mxfp8(qa, qr, pool8, bt, sl, scale=inp.scale)
     elif kind == "append":
         from synth import make_append_inputs
         inp = _workload_from_synth("c3", torch, with_host_pool=False)
@@ -590,8 +588,7 @@ def pmc_run(steps, warmup, kind="decode"):
         x, w_a = _dev_bf16(x_bits, torch), _dev_bf16(w_bits, torch)
         table = mla.rope_table(131072)
         bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
-        for _ in range(warmup + steps):
-            mla.append_kv(x, w_a, table, pool, bt, sl)
+        call = lambda: mla.append_kv(x, w_a, table, pool, bt, sl)
     elif kind == "prefill":
         from synth import make_custom
         B, L = 8, 4096
@@ -600,10 +597,16 @@ def pmc_run(steps, warmup, kind="decode"):
         q_r = torch.randn((B, L, 128, 64), device="cuda").to(torch.bfloat16)
         args = (q_c, q_r, _dev_bf16(base.w_uk, torch), _dev_bf16(base.w_uv, torch), _dev_bf16(base.pool, torch),
                 _dev_i32(base.block_table, torch), _dev_i32(base.seqlens, torch))
-        for _ in range(warmup + steps):
-            mla.prefill(*args, scale=base.scale)
+        call = lambda: mla.prefill(*args, scale=base.scale)
     else:
         raise SystemExit(f"unknown --pmc-run kind {kind!r}")
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    # marks the start of the steady launches (a power or clock sampler waits for it)
+    log(f"[bench] pmc run ({kind}): warm-up done, {steps} calls follow")
+    for _ in range(steps):
+        call()
     torch.cuda.synchronize()
     _copy_for_calibration(torch)
     log(f"[bench] pmc run ({kind}): {warmup + steps} calls, copy of {COPY_BYTES} B")
