@@ -243,7 +243,7 @@ typedef struct mla_prefill_params {
 } mla_prefill_params;
 
 /* Workspace bytes of mla_prefill: on the decompress branch the expanded K and V,
- * each [batch, max_blocks_per_seq * 64, 128, 128] bf16 (32 KiB per token slot),
+ * each [batch, 128 heads, max_blocks_per_seq * 64, 128] bf16 (32 KiB per token slot),
  * K at offset 0 and V at the size of one rounded up to 256 bytes; rows at or past
  * seqlens[b] are left as they were.  On the absorbed branch what mla_decode
  * needs.  0 when p is invalid. */

@@ -5,8 +5,8 @@
 
 namespace mla {
 
-// K, V [batch, max_len, H, 128] bf16 for every cached token t < seqlens[b] (rows past a
-// sequence's length are left as they were); max_len >= max_blocks * 64.
+// K, V [batch, H, max_len, 128] bf16 (each head's keys contiguous) for every cached token
+// t < seqlens[b] (rows past a sequence's length are left as they were); max_len >= max_blocks * 64.
 hipError_t launch_decompress(const uint16_t* kv, const int32_t* bt, const int32_t* seqlens, const uint16_t* w_uk,
                              const uint16_t* w_uv, uint16_t* k_out, uint16_t* v_out, int batch, int max_blocks,
                              int max_len, int64_t num_pages, hipStream_t s);

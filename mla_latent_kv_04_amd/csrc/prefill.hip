@@ -6,7 +6,7 @@
 // absorb below it and decompress above; section 6: the measured gain).  Two
 // kernels:
 //
-//   decompress_kernel  K[b, t, h, :] = c_t . W_UK[h]^T,  V[b, t, h, :] = c_t . W_UV[h]
+//   decompress_kernel  K[b, h, t, :] = c_t . W_UK[h]^T,  V[b, h, t, :] = c_t . W_UV[h]
 //                      for every cached token t < seqlens[b] ("DeepSeek的推理为什么
 //                      比别人便宜一个数量级", leslieaibin.github.io, section "MLA":
 //                      K = c . W_UK, V = c . W_UV), bf16 out, fp32 accumulation.
@@ -23,22 +23,29 @@ namespace {
 
 // ------------------------------------------------------------------ decompress
 
-constexpr int kDTok = 256;        // tokens per decompress workgroup
-constexpr int kDK = 64;           // latent values per K-loop chunk
-constexpr int kDPitchRow = kDK * 2 + 16;      // [row][k] tiles: rows 4 banks apart mod 64 for 16-byte reads
-constexpr int kCCPR = kDK * 2 / 16;           // 16-byte chunks per [row][k] tile row
-constexpr int kCRows = 512 / kCCPR;           // rows one pass of 512 threads covers
-constexpr int kCP = kDTok / kCRows;           // passes per chunk (equal to kDK / 16, the V tile's)
-constexpr int kDPitchV = 2 * kDimC * 2 + 32;  // [64 k][256 n] tile: 544 B = 8 banks mod 32 for transposing reads
+constexpr int kXWaves = 4;                     // waves per workgroup (one per SIMD)
+constexpr int kXHalves = 2;                    // workgroups per head
+constexpr int kXStreams = kXWaves * kXHalves;  // page streams per head
+constexpr int kXSteps = kLatent / 16;          // MFMA k-steps over the latent
+constexpr int kXAhead = 8;                     // k-steps of latent loads in flight ahead of their MFMAs
+constexpr int kWPitchK = kLatent * 2 + 16;     // W_UK[h] in LDS as [n][k]: 1040 B rows, 4 banks apart
+constexpr int kWPitchV = kDimC * 2;            // W_UV[h] in LDS as [k][n]: 256 B rows, 32-byte units swizzled
+constexpr int kWBytes = kDimC * kWPitchK;      // 133 120 B, the larger layout
+constexpr int kXStageRows = 16;                // output rows per staging round
+constexpr int kXStage = kXStageRows * kDimC * 2;   // 4 KiB of output staging per wave
+constexpr int kXBufFlags = 0x00020000;
+static_assert(kLatent * kWPitchV <= kWBytes, "both weight layouts fit the LDS array");
+static_assert(kWBytes + kXWaves * kXStage <= 160 * 1024, "weights and staging fit the LDS");
+static_assert(kXSteps % kXAhead == 0, "the load ring restarts with every page");
 
 struct DecompArgs {
   const uint16_t* kv;       // [num_pages, 64, 576]
   const int32_t* bt;        // [B, max_blocks]
   const int32_t* seqlens;   // [B]
   const uint16_t* w;        // W_UK [H, 128, 512] or W_UV [H, 512, 128]
-  uint16_t* out;            // [B, max_len, H, 128]
+  uint16_t* out;            // [B, H, max_len, 128]
   int64_t num_pages;
-  int max_blocks, max_len;
+  int batch, max_blocks, max_len;
 };
 
 __device__ __forceinline__ int clamp_len(int L, int max_blocks) {
@@ -46,136 +53,173 @@ __device__ __forceinline__ int clamp_len(int L, int max_blocks) {
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
-// Computes the transposed product out^T[n, t] = sum_k W[n, k] c[t, k] for 256 tokens
-// and the 256 output columns of two heads, so that each lane's accumulators hold
-// consecutive output columns of one token (8-byte stores).  Eight waves: wave w
-// owns head 2 hp + w / 4 (128 columns = 4 MFMA row blocks) and tokens
-// 64 (w % 4) .. +63 (2 column blocks) of v_mfma_f32_32x32x16_bf16.  The A
-// operand (weights) comes from LDS: for K row-major [n][k] (16-byte reads), for
-// V [k][n] through transposing reads; the B operand (latent rows) from a
-// [token][k] LDS tile.  Each kDK-wide chunk of the latent is loaded into
-// registers while the previous one is multiplied.
+// One head's expansion out^T[n, t] = sum_k W[n, k] c[t, k] over every cached page of
+// every sequence.  Two workgroups per head (256 in all: one per compute unit), each
+// with the head's whole weight matrix resident in LDS (W_UK[h] as [n][k], read with
+// 16-byte loads; W_UV[h] as [k][n], read transposed), loaded once.  The pages of all
+// sequences, in order, are dealt out to the 8 waves of the head's two workgroups in
+// turn; a wave multiplies a page (64 tokens = 2 column blocks) by all 128 output
+// columns (4 row blocks) of v_mfma_f32_32x32x16_bf16 over 32 k-steps.  The latent rows
+// are the B operand and come straight from the cache into registers (16 bytes of one
+// token per lane), kXAhead k-steps ahead of their MFMAs and across page boundaries, so
+// the waves run without barriers once the weights are in.  A finished page goes out
+// through a small per-wave LDS stage, 16 tokens at a time, so that every store
+// instruction writes 1 KiB of the head's contiguous [token][128] output.
 template <bool kIsV>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kXWaves, 64 * kXWaves), amdgpu_waves_per_eu(kXWaves / 4, kXWaves / 4)))
 void decompress_kernel(DecompArgs a) {
-  const int hp = blockIdx.x, tb = blockIdx.y, b = blockIdx.z;
-  const int L = clamp_len(a.seqlens[b], a.max_blocks);
-  const int t0 = tb * kDTok;
-  if (t0 >= L) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  constexpr int kWBytes = kIsV ? kDK * kDPitchV : 2 * kDimC * kDPitchRow;
+  const int h = blockIdx.x / kXHalves;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int stream = (blockIdx.x % kXHalves) * kXWaves + wave;
   __shared__ __attribute__((aligned(16))) unsigned char wt[kWBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char ct[kDTok * kDPitchRow];
+  __shared__ __attribute__((aligned(16))) unsigned char stages[kXWaves][kXStage];
+  unsigned char* stage = stages[wave];
 
-  static_assert(kCP == kDK / 16, "latent and weight chunks take the same number of passes");
-  // Latent chunk loads: thread -> token row tid / kCCPR + kCRows i, 16 bytes at k 8 (tid % kCCPR).
-  const uint16_t* crow[kCP];
+  // The head's weights: 8192 chunks of 16 bytes, all loads issued before the stores.
+  {
+    constexpr int kPer = kDimC * kLatent / 8 / (64 * kXWaves);
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.w + (size_t)h * kDimC * kLatent);
+    u32x4 v[kPer];
 #pragma unroll
-  for (int i = 0; i < kCP; ++i) {
-    const int t = t0 + tid / kCCPR + kCRows * i;
-    const int tt = t < L ? t : 0;             // rows past the sequence read its token 0, never stored
-    int64_t page = a.bt[(size_t)b * a.max_blocks + tt / kPage];
-    page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
-    crow[i] = a.kv + ((size_t)page * kPage + (tt & (kPage - 1))) * kRow + 8 * (tid % kCCPR);
-  }
-  unsigned char* cdst = ct + (tid / kCCPR) * kDPitchRow + (tid % kCCPR) * 16;
-
-  // Weight chunk loads.
-  const uint16_t* wsrc[kCP];
-  unsigned char* wdst[kCP];
+    for (int i = 0; i < kPer; ++i) v[i] = src[tid + 64 * kXWaves * i];
 #pragma unroll
-  for (int i = 0; i < kCP; ++i) {
-    if (!kIsV) {
-      // W_UK rows n = tid / kCCPR + kCRows i of the head pair ([n][k], 16 bytes at k 8 (tid % kCCPR))
-      const int n = tid / kCCPR + kCRows * i;
-      wsrc[i] = a.w + ((size_t)(2 * hp + n / kDimC) * kDimC + (n % kDimC)) * kLatent + 8 * (tid % kCCPR);
-      wdst[i] = wt + n * kDPitchRow + (tid % kCCPR) * 16;
-    } else {
-      // W_UV rows k = tid / 32 + 16 i of the chunk, 16 bytes of head 2 hp + (tid % 32) / 16 at e 8 (tid % 16)
-      const int k = tid / 32 + 16 * i, nc = tid % 32;
-      wsrc[i] = a.w + ((size_t)(2 * hp + nc / 16) * kLatent + k) * kDimC + 8 * (nc % 16);
-      wdst[i] = wt + k * kDPitchV + nc * 16;
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + 64 * kXWaves * i;
+      // W_UV row k: 32-byte unit u of the row stored at unit u ^ 2 (k % 4), so that the
+      // transposing reads of 4 consecutive rows by two lane groups hit distinct banks.
+      const int k = c / 16, x = c % 16;
+      const int off = kIsV ? k * kWPitchV + (((x >> 1) ^ (2 * (k & 3))) << 5) + (x & 1) * 16
+                           : (c / 64) * kWPitchK + (c % 64) * 16;
+      *(u32x4*)(wt + off) = v[i];
     }
   }
+  __syncthreads();
 
-  u32x4 cv[kCP], wv[kCP];
-  auto load_chunk = [&](int kc) {
-    const int k0 = kc * kDK;
-#pragma unroll
-    for (int i = 0; i < kCP; ++i) cv[i] = *(const u32x4*)(crow[i] + k0);
-#pragma unroll
-    for (int i = 0; i < kCP; ++i) wv[i] = *(const u32x4*)(wsrc[i] + (kIsV ? (size_t)k0 * kDimC : (size_t)k0));
+  // Page walk (wave-uniform): page j of sequence b; the stream's pages are every 16th
+  // page of the concatenation of all sequences' pages.
+  struct Walk {
+    int b, j, np;
+  };
+  auto pages_of = [&](int bb) { return (clamp_len(a.seqlens[bb], a.max_blocks) + kPage - 1) / kPage; };
+  auto settle = [&](Walk& w) {
+    while (w.b < a.batch && w.j >= w.np) {
+      w.j -= w.np;
+      ++w.b;
+      w.np = w.b < a.batch ? pages_of(w.b) : 0;
+    }
+  };
+  Walk cur{0, stream, pages_of(0)};
+  settle(cur);
+  if (cur.b >= a.batch) return;
+  Walk nxt{cur.b, cur.j + kXStreams, cur.np};
+  settle(nxt);
+  // A page's rows as a buffer (a finished walk gives an empty one: its loads read zeros).
+  auto page_rsrc = [&](const Walk& w) {
+    int64_t page = w.b < a.batch ? a.bt[(size_t)w.b * a.max_blocks + w.j] : 0;
+    page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(a.kv + (size_t)page * kPage * kRow), (short)0,
+                                             w.b < a.batch ? kPageBytes : 0, kXBufFlags);
+  };
+  __amdgpu_buffer_rsrc_t rc = page_rsrc(cur), rn = page_rsrc(nxt);
+
+  // B operand of column block nb at k-step ks: token 32 nb + lane % 32 of the page,
+  // latent values 16 ks + 8 (lane / 32) .. +7.
+  const uint32_t voff = (lane & 31) * kRowBytes + (lane >> 5) * 16;
+  auto bload = [&](__amdgpu_buffer_rsrc_t r, int ks, int nb) {
+    return __builtin_bit_cast(s16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                         r, voff + nb * 32 * kRowBytes + ks * 32, 0, 0));
+  };
+  // A operand of row block m at k-step ks (output columns 32 m + lane % 32).
+  // W_UV: rows 16 ks + 8 (lane / 32) + (lane % 16) / 4 (+4 for the second read), columns
+  // 32 m + 16 g + 4 (lane % 4): 32-byte unit 2 m + g of the row, stored at unit
+  // (2 m + g) ^ 2 (row % 4) = 2 (m ^ (row % 4)) + g (rows of one read share row % 4).
+  const int g = (lane >> 4) & 1, s = lane & 15, r4 = (s >> 2) & 3;
+  const unsigned char* abase = kIsV ? wt + (8 * (lane >> 5) + (s >> 2)) * kWPitchV + 32 * g + 8 * (s & 3)
+                                    : wt + (lane & 31) * kWPitchK + 16 * (lane >> 5);
+  auto aread = [&](int ks, int m) {
+    if constexpr (kIsV) {
+      const unsigned char* p = abase + 16 * ks * kWPitchV + 64 * (m ^ r4);
+      const s16x4 lo = lds_read_tr4(p);
+      const s16x4 hi = lds_read_tr4(p + 4 * kWPitchV);
+      return s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      return *(const s16x8*)(abase + 32 * m * kWPitchK + 32 * ks);
+    }
   };
 
-  const int nh = wave / 4;            // head of the pair this wave computes
-  const int tq = wave % 4;            // token quarter
-  f32x16 acc[4][2];
+  s16x8 bq[kXAhead][2];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int ks = 0; ks < kXAhead; ++ks)
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[m][n][j] = 0.f;
+    for (int nb = 0; nb < 2; ++nb) bq[ks][nb] = bload(rc, ks, nb);
 
-  load_chunk(0);
-  for (int kc = 0; kc < kLatent / kDK; ++kc) {
-    if (kc > 0) __syncthreads();
+  const f32x16 zero = {};
+  while (true) {
+    f32x16 acc[4][2];
+    // weight operands two k-steps ahead (LDS latency exceeds one MFMA)
+    s16x8 aop[3][4];
 #pragma unroll
-    for (int i = 0; i < kCP; ++i) *(u32x4*)(cdst + kCRows * i * kDPitchRow) = cv[i];
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int i = 0; i < kCP; ++i) *(u32x4*)wdst[i] = wv[i];
-    __syncthreads();
-    if (kc + 1 < kLatent / kDK) load_chunk(kc + 1);
-    // keep the next chunk's loads ahead of this chunk's MFMAs (the scheduler would sink
-    // them to their use, exposing the whole memory latency once per chunk)
-    __builtin_amdgcn_sched_barrier(0);
+      for (int m = 0; m < 4; ++m) aop[ks][m] = aread(ks, m);
 #pragma unroll
-    for (int ks = 0; ks < kDK / 16; ++ks) {
-      s16x8 bop[2];
+    for (int ks = 0; ks < kXSteps; ++ks) {
+      if (ks + 2 < kXSteps) {
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
-        bop[n] = *(const s16x8*)(ct + (64 * tq + 32 * n + (lane & 31)) * kDPitchRow + (16 * ks + 8 * (lane >> 5)) * 2);
+        for (int m = 0; m < 4; ++m) aop[(ks + 2) % 3][m] = aread(ks + 2, m);
+      }
+      const int slot = ks % kXAhead;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        s16x8 aop;
-        const int nrow = kDimC * nh + 32 * m;   // first output column of this row block
-        if (!kIsV) {
-          aop = *(const s16x8*)(wt + (nrow + (lane & 31)) * kDPitchRow + (16 * ks + 8 * (lane >> 5)) * 2);
-        } else {
-          // A[n][k] = W_UV[k][n]: rows k 16 ks + 8 (lane / 32) + 0..7 of column n, as two
-          // transposing reads of 4 rows.  Within a 16-lane group, lane s reads row 4 e + s / 4
-          // ... at columns 4 (s % 4): the group covers columns nrow + 16 (lane % 32 / 16) .. +15.
-          const int g = (lane >> 4) & 1, s = lane & 15;
-          const unsigned char* p = wt + (16 * ks + 8 * (lane >> 5) + (s >> 2)) * kDPitchV +
-                                   (nrow + 16 * g + 4 * (s & 3)) * 2;
-          const s16x4 lo = lds_read_tr4(p);
-          const s16x4 hi = lds_read_tr4(p + 4 * kDPitchV);
-          aop = s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int n = 0; n < 2; ++n) acc[m][n] = mfma32(aop, bop[n], acc[m][n]);
+        for (int nb = 0; nb < 2; ++nb) acc[m][nb] = mfma32(aop[ks % 3][m], bq[slot][nb], ks == 0 ? zero : acc[m][nb]);
+      // refill the slot with the operand kXAhead k-steps on (the next page's first ones at the end)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        bq[slot][nb] = ks + kXAhead < kXSteps ? bload(rc, ks + kXAhead, nb) : bload(rn, ks + kXAhead - kXSteps, nb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // D layout (32x32): lane l, register r -> row 8 (r / 4) + 4 (l / 32) + r % 4 (output column
+    // within the row block), column l % 32 (token within the column block).  Four rounds of
+    // 16 tokens through the wave's stage ([16 rows][256 B], 16-byte chunk c of row t stored
+    // at chunk c ^ t): the 32 lanes holding the round's tokens write 8 bytes per register
+    // quad, then all 64 lanes read 16 bytes each and store four consecutive tokens' rows
+    // (1 KiB of the head's contiguous [token][128] block) per instruction.
+    const int valid = clamp_len(a.seqlens[cur.b], a.max_blocks) - cur.j * kPage;
+    uint16_t* dst_page = a.out + (((size_t)cur.b * kHeads + h) * a.max_len + cur.j * kPage) * kDimC;
+#pragma unroll
+    for (int rd = 0; rd < kPage / kXStageRows; ++rd) {
+      constexpr int kRounds = 32 / kXStageRows;             // rounds per column block
+      const int nb = rd / kRounds, sub = rd % kRounds;
+      const int t = (lane & 31) - kXStageRows * sub;        // this lane's row in the round
+      if (t >= 0 && t < kXStageRows) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            u32x2 o;
+            o[0] = pack_bf16x2(acc[m][nb][4 * q], acc[m][nb][4 * q + 1]);
+            o[1] = pack_bf16x2(acc[m][nb][4 * q + 2], acc[m][nb][4 * q + 3]);
+            const int chunk = 4 * m + q;                    // columns 8 chunk .. +7; this lane's 4 at +4 (l / 32)
+            *(u32x2*)(stage + t * (kDimC * 2) + ((chunk ^ t) << 4) + 8 * (lane >> 5)) = o;
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < kXStageRows / 4; ++i) {
+        const int tr = 4 * i + (lane >> 4), c = lane & 15;
+        const u32x4 v = *(const u32x4*)(stage + tr * (kDimC * 2) + ((c ^ tr) << 4));
+        const int row = 32 * nb + kXStageRows * sub + tr;
+        if (row < valid) *(u32x4*)(dst_page + (size_t)row * kDimC + 8 * c) = v;
       }
     }
-  }
-
-  // D layout (32x32): lane l, register j -> row 8 (j / 4) + 4 (l / 32) + j % 4 (output column
-  // within the row block), column l % 32 (token within the column block).
-  const int h = 2 * hp + nh;
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int t = t0 + 64 * tq + 32 * n + (lane & 31);
-    if (t >= L) continue;
-    uint16_t* dst = a.out + (((size_t)b * a.max_len + t) * kHeads + h) * kDimC;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x2 o;
-        o[0] = pack_bf16x2(acc[m][n][4 * q], acc[m][n][4 * q + 1]);
-        o[1] = pack_bf16x2(acc[m][n][4 * q + 2], acc[m][n][4 * q + 3]);
-        *(u32x2*)(dst + 32 * m + 8 * q + 4 * (lane >> 5)) = o;
-      }
+    if (nxt.b >= a.batch) break;
+    cur = nxt;
+    rc = rn;
+    nxt.j += kXStreams;
+    settle(nxt);
+    rn = page_rsrc(nxt);
   }
 }
 
@@ -190,20 +234,20 @@ hipError_t launch_decompress(const uint16_t* kv, const int32_t* bt, const int32_
   a.bt = bt;
   a.seqlens = seqlens;
   a.num_pages = num_pages;
+  a.batch = batch;
   a.max_blocks = max_blocks;
   a.max_len = max_len;
-  const dim3 grid(kHeads / 2, (max_len + kDTok - 1) / kDTok, batch);
+  const dim3 grid(kHeads * kXHalves);
   a.w = w_uk;
   a.out = k_out;
-  hipLaunchKernelGGL(decompress_kernel<false>, grid, dim3(512), 0, s, a);
+  hipLaunchKernelGGL(decompress_kernel<false>, grid, dim3(64 * kXWaves), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.w = w_uv;
   a.out = v_out;
-  hipLaunchKernelGGL(decompress_kernel<true>, grid, dim3(512), 0, s, a);
+  hipLaunchKernelGGL(decompress_kernel<true>, grid, dim3(64 * kXWaves), 0, s, a);
   return hipGetLastError();
 }
-
 }  // namespace mla
 
 namespace mla {
@@ -231,8 +275,8 @@ constexpr int kValueAhead = 3;
 struct AttnArgs {
   const uint16_t* q_c;      // [B, M, H, 128]
   const uint16_t* q_r;      // [B, M, H, 64]
-  const uint16_t* k;        // [B, max_len, H, 128]
-  const uint16_t* v;        // [B, max_len, H, 128]
+  const uint16_t* k;        // [B, H, max_len, 128]
+  const uint16_t* v;        // [B, H, max_len, 128]
   const uint16_t* kv;       // [num_pages, 64, 576] (k_R = columns 512..575)
   const int32_t* bt;        // [B, max_blocks]
   const int32_t* seqlens;   // [B]
@@ -342,11 +386,11 @@ void prefill_attention_kernel(AttnArgs a) {
   // the tile's rows inside the sequence, so rows past it read as zeros.
   //   K_h: 64 rows x 16 chunks, 4 per thread; k_R: 64 rows x 8 chunks, 2 per thread;
   //   V_h: 64 rows x 16 chunks, 4 per thread.
-  constexpr uint32_t kRowBytesKV = kHeads * kDimC * 2;   // 32 KiB between consecutive keys in K and V
+  constexpr uint32_t kRowBytesKV = kDimC * 2;            // a head's keys (and values) are contiguous rows
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k) +
-                               ((size_t)b * a.max_len * kHeads + h) * kDimC * 2;
+                               ((size_t)b * kHeads + h) * a.max_len * kDimC * 2;
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v) +
-                               ((size_t)b * a.max_len * kHeads + h) * kDimC * 2;
+                               ((size_t)b * kHeads + h) * a.max_len * kDimC * 2;
   uint32_t khoff[kKH], kroff[kKR], vvoff[kVC], khdst[kKH], krdst[kKR], vdst[kVC];
   static_assert(kKH == kVC, "K and V chunks share the loop below");
 #pragma unroll

@@ -81,9 +81,9 @@ def test_expanded_keys_and_values_match_the_oracle():
     _, _, ws = _run(inp, mode=2, with_ws=True)
     max_len = inp.max_blocks * 64
     n = inp.batch * max_len * 128 * 128
-    kb = host_bits(ws[:2 * n].view(torch.int16)).reshape(inp.batch, max_len, 128, 128)
+    kb = host_bits(ws[:2 * n].view(torch.int16)).reshape(inp.batch, 128, max_len, 128).transpose(0, 2, 1, 3)
     off = (2 * n + 255) // 256 * 256
-    vb = host_bits(ws[off:off + 2 * n].view(torch.int16)).reshape(inp.batch, max_len, 128, 128)
+    vb = host_bits(ws[off:off + 2 * n].view(torch.int16)).reshape(inp.batch, 128, max_len, 128).transpose(0, 2, 1, 3)
     K, V = oracle.decompress_kv(inp.pool, inp.block_table, inp.seqlens, inp.w_uk, inp.w_uv, max_len=max_len)
     wk = np.abs(oracle.bf16_bits_to_f64(inp.w_uk))
     wv = np.abs(oracle.bf16_bits_to_f64(inp.w_uv))
