@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import make_custom
+from synth import make_custom, poison_unused
 
 from ._gpu import U, assert_bf16_match, assert_close, dev_bf16, dev_i32, host_bits, require_gpu
 
@@ -95,6 +95,38 @@ def test_expanded_keys_and_values_match_the_oracle():
         assert_bf16_match(kb[b, :L], K[b, :, :L].transpose(1, 0, 2), ek, f"K of sequence {b}")
         assert_bf16_match(vb[b, :L], V[b, :, :L].transpose(1, 0, 2), ev, f"V of sequence {b}")
 
+
+
+def test_expansion_over_many_ragged_sequences_leaves_other_rows_alone():
+    """Seven sequences from 1 to 200 tokens (partial, exact and single-row pages; the
+    pages of all sequences are dealt out to the expansion's waves in turn), NaN in every
+    pool row no sequence may read, and a workspace pre-filled with a marker: every row
+    t < L_b of K and V matches the oracle, every other row keeps the marker."""
+    lens = [1, 63, 64, 65, 129, 200, 7]
+    inp = poison_unused(make_custom(97, len(lens), 1, lens, extra_blocks=1))
+    print(f"decompress: B={inp.batch} L={lens}", flush=True)
+    params = mla.make_prefill_params(inp.batch, inp.s_q, inp.max_blocks, inp.num_pages, inp.scale, 2, 0)
+    ws = torch.full((mla.prefill_workspace_size(params),), 0x5A, dtype=torch.uint8, device="cuda")
+    mla.prefill(dev_bf16(inp.q_c), dev_bf16(inp.q_r), dev_bf16(inp.w_uk), dev_bf16(inp.w_uv), dev_bf16(inp.pool),
+                dev_i32(inp.block_table), dev_i32(inp.seqlens), scale=inp.scale, mode=2, workspace=ws)
+    torch.cuda.synchronize()
+    max_len = inp.max_blocks * 64
+    n = inp.batch * 128 * max_len * 128
+    off = (2 * n + 255) // 256 * 256
+    kb = host_bits(ws[:2 * n].view(torch.int16)).reshape(inp.batch, 128, max_len, 128)
+    vb = host_bits(ws[off:off + 2 * n].view(torch.int16)).reshape(inp.batch, 128, max_len, 128)
+    wk = np.abs(oracle.bf16_bits_to_f64(inp.w_uk))
+    wv = np.abs(oracle.bf16_bits_to_f64(inp.w_uv))
+    K, V = oracle.decompress_kv(inp.pool, inp.block_table, inp.seqlens, inp.w_uk, inp.w_uv, max_len=max_len)
+    for b, L in enumerate(lens):
+        c = np.abs(oracle.bf16_bits_to_f64(oracle.gather_rows(inp.pool, inp.block_table, b, L))[:, :512])
+        ek = (512 / 16 + 64) * U * np.einsum("tc,hdc->htd", c, wk)
+        ev = (512 / 16 + 64) * U * np.einsum("tc,hce->hte", c, wv)
+        assert_bf16_match(kb[b, :, :L], K[b, :, :L], ek, f"K of sequence {b} (L={L})")
+        assert_bf16_match(vb[b, :, :L], V[b, :, :L], ev, f"V of sequence {b} (L={L})")
+        marker = np.uint16(0x5A5A)
+        assert np.all(kb[b, :, L:] == marker), f"K rows past L={L} of sequence {b} were written"
+        assert np.all(vb[b, :, L:] == marker), f"V rows past L={L} of sequence {b} were written"
 
 CASES = [
     # (name, seed, batch, s_q, seqlens, mode)
