@@ -423,7 +423,7 @@ def main():
     fws = torch.empty(mla.workspace_size(fparams, fused=True), dtype=torch.uint8, device="cuda")
     fms, fper = _time_calls(lambda i: mla.decode(d_qc, d_qr, d_wuk, d_wuv, pool, d_bt, d_sl, scale=inp.scale,
                                                  out=fout, workspace=fws, want_lse=False),
-                            max(args.steps // 2, 5), 3, torch, mla)
+                            args.steps, args.warmup, torch, mla)
     log(f"[bench] c3 fused: {fms * 1e3:.1f} us/step; kernels us: "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in fper.items()))
 

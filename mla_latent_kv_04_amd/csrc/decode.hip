@@ -10,7 +10,8 @@
 // Work split: the pages of all units are laid end to end; workgroup g takes the
 // contiguous range [g*chunk, (g+1)*chunk) of that list (chunk = ceil(total/W)),
 // so every compute unit streams the same number of pages whatever the length
-// mix.  A unit that lies inside one range is finished in place; a unit cut by
+// mix (the prefix sums of pages per unit come from a wave scan inside each
+// workgroup for up to 64 units, else from plan_kernel).  A unit that lies inside one range is finished in place; a unit cut by
 // range borders leaves one normalised partial per piece (bf16, with an fp32 lse;
 // slot 2g for the first segment of workgroup g, 2g+1 for its last), merged by
 // log-sum-exp afterwards.
@@ -50,7 +51,7 @@ struct DecodeArgs {
   const int32_t* seqlens;
   uint16_t* out_latent;
   float* lse;
-  const int32_t* cum;
+  int32_t* cum;
   uint16_t* part_o;    // [2W, 128, 512] bf16 normalised partial outputs
   float* part_lse;
   int64_t num_pages;
@@ -78,6 +79,10 @@ __device__ __forceinline__ int unit_visible(const DecodeArgs& a, int u) {
 }
 
 // ---------------------------------------------------------------------------- plan
+
+// Up to this many work units (batch x queries), each decode workgroup computes the
+// page prefix sums itself and the plan kernel is not launched.
+constexpr int kSelfPlanUnits = 64;
 
 // Prefix sums of pages per work unit: cum[0] = 0, cum[u+1] = cum[u] + ceil(visible_u / 64).
 __global__ __attribute__((amdgpu_flat_work_group_size(1024, 1024)))
@@ -229,7 +234,7 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 constexpr float kHeadroom = 64.0f;
 
 // Scalar read of a value that no kernel of the launch writes (block table,
-// sequence lengths, the plan's prefix sums): through the constant address space
+// sequence lengths, plan_kernel's prefix sums): through the constant address space
 // the load is a scalar one, counted by lgkmcnt, so waiting for it never waits
 // for the tile loads in flight (a vector load would, as those share vmcnt).
 __device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int64_t i) {
@@ -260,7 +265,33 @@ void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char pbuf[2 * kPBytes];
 
   const int U = a.batch * a.s_q;
-  const int total = ld_uniform(a.cum, U);
+  const int tid = threadIdx.x, lane = tid & 63;
+  // Pages per work unit and their prefix sums.  Up to kSelfPlanUnits units, every wave
+  // scans them itself (lane u holds unit u) and workgroup 0 publishes the sums for the
+  // combine; more units come from the plan kernel's array.
+  int total, pex = 0;             // pex: exclusive prefix of this lane's unit
+  const bool self_plan = U <= kSelfPlanUnits;
+  if (self_plan) {
+    int pages = 0;
+    if (lane < U) {
+      const int n = unit_visible(a, lane);
+      pages = n > 0 ? (n + kPage - 1) / kPage : 0;
+    }
+    int x = pages;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    total = __builtin_amdgcn_readlane(x, 63);
+    pex = x - pages;
+    if (blockIdx.x == 0 && tid < 64) {
+      if (lane < U) a.cum[lane + 1] = x;
+      if (lane == 0) a.cum[0] = 0;
+    }
+  } else {
+    total = ld_uniform(a.cum, U);
+  }
   if (total <= 0) return;
   const int W = gridDim.x;
   const int chunk = (total + W - 1) / W;
@@ -269,7 +300,6 @@ void decode_kernel(DecodeArgs a) {
   if (start >= total) return;
   const int end = min(total, start + chunk);
 
-  const int tid = threadIdx.x, lane = tid & 63;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;       // which half of the wave
   const int l32 = lane & 31;
@@ -316,25 +346,45 @@ void decode_kernel(DecodeArgs a) {
     offV0 = (8 * hi + eb) * 1024 + 64 * eb + 16 * (cb ^ (2 * hi)) + 8 * (lane & 1) + 256 * wave_u;
   }
 
-  // Largest u with cum[u] <= start (then cum[u+1] > start).
-  int lo_u = 0, hi_u = U - 1;
-  while (lo_u < hi_u) {
-    const int mid = (lo_u + hi_u + 1) >> 1;
-    if (ld_uniform(a.cum, mid) <= start) lo_u = mid; else hi_u = mid - 1;
+  // Largest u with cum[u] <= start (then cum[u+1] > start), and ubeg = cum[u].
+  int u, ubeg;
+  if (self_plan) {
+    // the prefix sums do not decrease, so u + 1 lanes have theirs at or below start
+    u = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < U && pex <= start)) - 1;
+    ubeg = __builtin_amdgcn_readlane(pex, u);
+  } else {
+    int lo_u = 0, hi_u = U - 1;
+    while (lo_u < hi_u) {
+      const int mid = (lo_u + hi_u + 1) >> 1;
+      if (ld_uniform(a.cum, mid) <= start) lo_u = mid; else hi_u = mid - 1;
+    }
+    u = lo_u;
+    ubeg = ld_uniform(a.cum, u);
   }
-  int u = lo_u;
+  // pages of unit u (as the plan counts them)
+  auto unit_pages = [&](int uu) {
+    const int bb = uu / a.s_q;
+    const int n = clamp_len(ld_uniform(a.seqlens, bb), a.max_blocks) - a.s_q + (uu - bb * a.s_q) + 1;
+    return n > 0 ? (n + kPage - 1) / kPage : 0;
+  };
 
-  bool first_seg = true;
+  // Page offset of the first segment in its unit; -1 once that segment is done (every
+  // later segment starts its unit, so the walker keeps no unit start across segments).
+  int seg0_off = start - ubeg;
   int pos = start;
   bool redo = false;              // re-run the current segment with m_redo as the reference
   float m_redo = -INFINITY;
   while (pos < end) {
-    while (ld_uniform(a.cum, u + 1) <= pos) ++u;
-    const int ubeg = ld_uniform(a.cum, u), uend = ld_uniform(a.cum, u + 1);
+    const int ubeg = pos - (seg0_off >= 0 ? seg0_off : 0);
+    int uend = ubeg + unit_pages(u);
+    while (uend <= pos) {          // units without visible tokens (never the first)
+      ++u;
+      uend = ubeg + unit_pages(u);
+    }
     const int seg_end = min(end, uend);
     const int p0 = pos - ubeg, p1 = seg_end - ubeg;
     const bool complete = (pos == ubeg) && (seg_end == uend);
-    const int slot = complete ? -1 : 2 * g + (first_seg ? 0 : 1);
+    const int slot = complete ? -1 : 2 * g + (seg0_off >= 0 ? 0 : 1);
 
     const int b = u / a.s_q;
     const int n_vis = clamp_len(ld_uniform(a.seqlens, b), a.max_blocks) - a.s_q + (u - b * a.s_q) + 1;
@@ -972,7 +1022,8 @@ void decode_kernel(DecodeArgs a) {
     }
     if (!redo) {
       pos = seg_end;
-      first_seg = false;
+      ++u;                         // pos is now the next unit's start (or the range's end)
+      seg0_off = -1;
     }
   }
 }
@@ -1090,9 +1141,12 @@ hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint1
   a.out_latent = out_latent; a.lse = lse; a.cum = plan.cum; a.part_o = plan.part_o; a.part_lse = plan.part_lse;
   a.num_pages = num_pages; a.batch = batch; a.s_q = s_q; a.max_blocks = max_blocks;
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a, plan.cum);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (batch * s_q > kSelfPlanUnits) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a, plan.cum);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (ev_plan_done != nullptr && (e = hipEventRecord(ev_plan_done, s)) != hipSuccess) return e;
   if (kv8 != nullptr)
     hipLaunchKernelGGL(decode_kernel<true>, dim3(wgs), dim3(kThreads), 0, s, a);
