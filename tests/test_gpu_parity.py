@@ -107,6 +107,24 @@ def test_decode_paged_small(seed, s_q, seqlens, num_splits):
     assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= LSE_ATOL
 
 
+
+@pytest.mark.parametrize("batch,s_q", [(64, 1), (65, 1), (33, 2)])
+@pytest.mark.parametrize("num_splits", [0, 40])
+def test_decode_paged_around_the_in_kernel_plan_limit(batch, s_q, num_splits):
+    """Up to 64 work units (batch x queries) the decode workgroups compute the page prefix
+    sums themselves; above that a separate kernel does.  64, 65 and 66 units of short
+    ragged sequences (1 to 300 tokens), against the oracle, on both sides of that limit."""
+    rng = np.random.default_rng(36 + batch + s_q)
+    seqlens = [int(x) for x in rng.integers(s_q, 301, size=batch)]
+    inp = make_custom(37 + batch, batch, s_q, seqlens, extra_blocks=1)
+    _print_case(f"paged units={batch * s_q} splits={num_splits}", inp)
+    d = upload(inp)
+    qa = absorbed_inputs(inp)
+    ol, lse = _paged(inp, d, qa, num_splits)
+    ref_ol, ref_lse = oracle.decode_absorbed(qa, inp.q_r, inp.pool, inp.block_table, inp.seqlens, s_q, inp.scale)
+    assert_close(host_f64(ol), ref_ol, "out_latent")
+    assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= LSE_ATOL
+
 # ------------------------------------------------------------------ the five workloads
 
 def _sampled_check(inp, d, qa, ol, lse, batches):
