@@ -96,8 +96,8 @@ void decompress_kernel(DecompArgs a) {
   }
   __syncthreads();
 
-  // Page walk (wave-uniform): page j of sequence b; the stream's pages are every 16th
-  // page of the concatenation of all sequences' pages.
+  // Page walk (wave-uniform): page j of sequence b; the stream's pages are every
+  // kXStreams-th (8th) page of the concatenation of all sequences' pages.
   struct Walk {
     int b, j, np;
   };
