@@ -100,15 +100,18 @@ def test_expanded_keys_and_values_match_the_oracle():
 def test_expansion_over_many_ragged_sequences_leaves_other_rows_alone():
     """Seven sequences from 1 to 200 tokens (partial, exact and single-row pages; the
     pages of all sequences are dealt out to the expansion's waves in turn), NaN in every
-    pool row no sequence may read, and a workspace pre-filled with a marker: every row
-    t < L_b of K and V matches the oracle, every other row keeps the marker."""
+    pool row no sequence may read, unused table entries out of the pool's range, and a
+    workspace pre-filled with a marker: every row t < L_b of K and V matches the oracle,
+    every other row keeps the marker."""
     lens = [1, 63, 64, 65, 129, 200, 7]
     inp = poison_unused(make_custom(97, len(lens), 1, lens, extra_blocks=1))
     print(f"decompress: B={inp.batch} L={lens}", flush=True)
     params = mla.make_prefill_params(inp.batch, inp.s_q, inp.max_blocks, inp.num_pages, inp.scale, 2, 0)
     ws = torch.full((mla.prefill_workspace_size(params),), 0x5A, dtype=torch.uint8, device="cuda")
+    bt = inp.block_table.copy()
+    bt[bt < 0] = 10 ** 6              # unused table entries point outside the pool: never read
     mla.prefill(dev_bf16(inp.q_c), dev_bf16(inp.q_r), dev_bf16(inp.w_uk), dev_bf16(inp.w_uv), dev_bf16(inp.pool),
-                dev_i32(inp.block_table), dev_i32(inp.seqlens), scale=inp.scale, mode=2, workspace=ws)
+                dev_i32(bt), dev_i32(inp.seqlens), scale=inp.scale, mode=2, workspace=ws)
     torch.cuda.synchronize()
     max_len = inp.max_blocks * 64
     n = inp.batch * 128 * max_len * 128
