@@ -74,10 +74,10 @@ __device__ __forceinline__ s16x4 lds_read_tr4(const void* lds_byte_ptr) {
 
 // The same reads at a 32-bit LDS byte address.
 __device__ __forceinline__ s16x4 lds_read_tr4_at(uint32_t addr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)addr);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)addr);
 }
 __device__ __forceinline__ s16x8 lds_read_b128_at(uint32_t addr) {
-  return *(MLA_LDS const s16x8*)addr;
+  return *(MLA_LDS const s16x8*)(uintptr_t)addr;
 }
 
 // Host-side launch helpers (defined in the kernel translation units).

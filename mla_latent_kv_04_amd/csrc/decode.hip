@@ -438,7 +438,7 @@ void decode_kernel(DecodeArgs a) {
     };
     auto f8_read = [&](int j) {
       f8v[j] = __builtin_bit_cast(u32x4, lds_read_b128_at(f8cb + 1024 * j));
-      f8sc[j] = *(MLA_LDS const unsigned char*)(f8sb + 32 * j);
+      f8sc[j] = *(MLA_LDS const unsigned char*)(uintptr_t)(f8sb + 32 * j);
     };
     // Half h of part j: codes 8h .. 8h+7 of the lane's chunk -> bf16 chunk 2q + h.
     auto f8_write = [&](uint32_t slot_base, int j, int h) {
@@ -446,7 +446,7 @@ void decode_kernel(DecodeArgs a) {
       const uint32_t addr = (slot_base + 1024 * (8 * wave_u + 2 * j) + (f8l ^ u)) ^ (16u * h);
       const float sc = mx_scale_f32(f8sc[j]);
       const u32x2 d0 = e4m3x4_to_bf16(f8v[j][2 * h], sc), d1 = e4m3x4_to_bf16(f8v[j][2 * h + 1], sc);
-      *(MLA_LDS u32x4*)addr = u32x4{d0[0], d0[1], d1[0], d1[1]};
+      *(MLA_LDS u32x4*)(uintptr_t)addr = u32x4{d0[0], d0[1], d1[0], d1[1]};
     };
     // Rows at or past `valid` (only in a segment's last tile) are overwritten with zeros.
     auto f8_zero_tail = [&](uint32_t slot_base, int valid) {
@@ -457,8 +457,8 @@ void decode_kernel(DecodeArgs a) {
         const uint32_t u = 128u * (j & 1) + 16u * ((2 * wave_u + (j >> 1)) & 3);
         const uint32_t lo_addr = slot_base + 1024 * (8 * wave_u + 2 * j) + (f8l ^ u);
         if (t >= valid) {
-          *(MLA_LDS u32x4*)lo_addr = u32x4{0u, 0u, 0u, 0u};
-          *(MLA_LDS u32x4*)(lo_addr ^ 16u) = u32x4{0u, 0u, 0u, 0u};
+          *(MLA_LDS u32x4*)(uintptr_t)lo_addr = u32x4{0u, 0u, 0u, 0u};
+          *(MLA_LDS u32x4*)(uintptr_t)(lo_addr ^ 16u) = u32x4{0u, 0u, 0u, 0u};
         }
       }
     };
