@@ -84,53 +84,21 @@ __device__ __forceinline__ int unit_visible(const DecodeArgs& a, int u) {
 // page prefix sums itself and the plan kernel is not launched.
 constexpr int kSelfPlanUnits = 64;
 
-// Pages of work charged for starting a unit (its queries, the refill of the tile
-// pipeline, its output or partial) when the pages are split over W workgroups: a
-// sixteenth of the uncharged share of one workgroup, at most kMaxSetupPages.  A
-// workgroup whose range starts a unit then gets that many fewer real pages, which
-// keeps the ones that start units from finishing last.
-constexpr int kMaxSetupPages = 8;
-__device__ __forceinline__ int setup_pages(int total_pages, int W) {
-  const int d = (total_pages + W - 1) / W / 16;
-  return d < kMaxSetupPages ? d : kMaxSetupPages;
-}
-
-// Prefix sums of the split's pages per work unit: cum[0] = 0, cum[u+1] = cum[u] +
-// ceil(visible_u / 64) + setup (nothing for a unit without visible tokens), and
-// cum[U+1] = setup.  The setup pages sit at the start of each unit's range and hold
-// no data.
+// Prefix sums of pages per work unit: cum[0] = 0, cum[u+1] = cum[u] + ceil(visible_u / 64).
 __global__ __attribute__((amdgpu_flat_work_group_size(1024, 1024)))
-void plan_kernel(DecodeArgs a, int32_t* cum, int W) {
+void plan_kernel(DecodeArgs a, int32_t* cum) {
   __shared__ int32_t warp_tot[16];
-  __shared__ int32_t carry_s, setup_s;
+  __shared__ int32_t carry_s;
   const int U = a.batch * a.s_q;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // real pages of all units, for the setup charge
-  int sum = 0;
-  for (int u = tid; u < U; u += 1024) {
-    const int n = unit_visible(a, u);
-    sum += n > 0 ? (n + kPage - 1) / kPage : 0;
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  if (lane == 0) warp_tot[wave] = sum;
+  if (tid == 0) { carry_s = 0; cum[0] = 0; }
   __syncthreads();
-  if (tid == 0) {
-    int t = 0;
-    for (int w = 0; w < 16; ++w) t += warp_tot[w];
-    setup_s = setup_pages(t, W);
-    carry_s = 0;
-    cum[0] = 0;
-    cum[U + 1] = setup_s;
-  }
-  __syncthreads();
-  const int setup = setup_s;
   for (int base = 0; base < U; base += 1024) {
     const int u = base + tid;
     int pages = 0;
     if (u < U) {
       const int n = unit_visible(a, u);
-      pages = n > 0 ? (n + kPage - 1) / kPage + setup : 0;
+      pages = n > 0 ? (n + kPage - 1) / kPage : 0;
     }
     // inclusive scan inside the wave
     int x = pages;
@@ -301,9 +269,7 @@ void decode_kernel(DecodeArgs a) {
   // Pages per work unit and their prefix sums.  Up to kSelfPlanUnits units, every wave
   // scans them itself (lane u holds unit u) and workgroup 0 publishes the sums for the
   // combine; more units come from the plan kernel's array.
-  // (plan_kernel's counts, setup pages included: see there).
-  const int W = gridDim.x;
-  int total, setup, pex = 0;      // pex: exclusive prefix of this lane's unit
+  int total, pex = 0;             // pex: exclusive prefix of this lane's unit
   const bool self_plan = U <= kSelfPlanUnits;
   if (self_plan) {
     int pages = 0;
@@ -317,24 +283,17 @@ void decode_kernel(DecodeArgs a) {
       const int y = __shfl_up(x, off, 64);
       if (lane >= off) x += y;
     }
-    const uint64_t nzm = __builtin_amdgcn_ballot_w64(pages > 0);
-    const int real_total = __builtin_amdgcn_readlane(x, 63);
-    setup = setup_pages(real_total, W);
-    const int nz_below = __builtin_amdgcn_mbcnt_hi((uint32_t)(nzm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)nzm, 0));
-    pex = x - pages + setup * nz_below;
-    total = real_total + setup * __builtin_popcountll(nzm);
+    total = __builtin_amdgcn_readlane(x, 63);
+    pex = x - pages;
     if (blockIdx.x == 0 && tid < 64) {
-      if (lane < U) a.cum[lane + 1] = pex + (pages > 0 ? pages + setup : 0);
-      if (lane == 0) {
-        a.cum[0] = 0;
-        a.cum[U + 1] = setup;
-      }
+      if (lane < U) a.cum[lane + 1] = x;
+      if (lane == 0) a.cum[0] = 0;
     }
   } else {
     total = ld_uniform(a.cum, U);
-    setup = ld_uniform(a.cum, U + 1);
   }
   if (total <= 0) return;
+  const int W = gridDim.x;
   const int chunk = (total + W - 1) / W;
   const int g = blockIdx.x;
   const int start = g * chunk;
@@ -402,11 +361,11 @@ void decode_kernel(DecodeArgs a) {
     u = lo_u;
     ubeg = ld_uniform(a.cum, u);
   }
-  // the split's pages of unit u (real pages plus the setup charge; as the plan counts them)
-  auto unit_vpages = [&](int uu) {
+  // pages of unit u (as the plan counts them)
+  auto unit_pages = [&](int uu) {
     const int bb = uu / a.s_q;
     const int n = clamp_len(ld_uniform(a.seqlens, bb), a.max_blocks) - a.s_q + (uu - bb * a.s_q) + 1;
-    return n > 0 ? (n + kPage - 1) / kPage + setup : 0;
+    return n > 0 ? (n + kPage - 1) / kPage : 0;
   };
 
   // Page offset of the first segment in its unit; -1 once that segment is done (every
@@ -417,16 +376,14 @@ void decode_kernel(DecodeArgs a) {
   float m_redo = -INFINITY;
   while (pos < end) {
     const int ubeg = pos - (seg0_off >= 0 ? seg0_off : 0);
-    int uend = ubeg + unit_vpages(u);
+    int uend = ubeg + unit_pages(u);
     while (uend <= pos) {          // units without visible tokens (never the first)
       ++u;
-      uend = ubeg + unit_vpages(u);
+      uend = ubeg + unit_pages(u);
     }
     const int seg_end = min(end, uend);
-    // real pages [p0, p1) of the unit: the first `setup` pages of its range hold no data
-    const int p0 = max(0, pos - ubeg - setup), p1 = max(0, seg_end - ubeg - setup);
-    if (p1 <= p0) break;           // the range ends inside the unit's setup share
-    const bool complete = (p0 == 0) && (seg_end == uend);
+    const int p0 = pos - ubeg, p1 = seg_end - ubeg;
+    const bool complete = (pos == ubeg) && (seg_end == uend);
     const int slot = complete ? -1 : 2 * g + (seg0_off >= 0 ? 0 : 1);
 
     const int b = u / a.s_q;
@@ -1104,9 +1061,7 @@ void combine_kernel(DecodeArgs a, int W) {
     return;
   }
   const int chunk = (total + W - 1) / W;
-  // workgroups holding the unit's real pages (the first `setup` pages of its range hold none)
-  const int setup = ld_uniform(a.cum, U + 1);
-  const int g0 = (ubeg + setup) / chunk, g1 = (uend - 1) / chunk;
+  const int g0 = ubeg / chunk, g1 = (uend - 1) / chunk;
   if (g0 == g1) return;
 
   auto load = [&](int gg, u32x2 (&x)[4], float& l) {
@@ -1188,7 +1143,7 @@ hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint1
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = hipSuccess;
   if (batch * s_q > kSelfPlanUnits) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a, plan.cum, wgs);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a, plan.cum);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -91,7 +91,7 @@ WsLayout layout(const mla_decode_params* p, int wgs, bool fused) {
   WsLayout L;
   size_t off = 0;
   L.cum = off;
-  off += round_up((units + 2) * sizeof(int32_t));   // prefix sums and the setup charge
+  off += round_up((units + 1) * sizeof(int32_t));
   L.part_lse = off;
   off += round_up((size_t)2 * wgs * mla::kHeads * sizeof(float));
   L.part_o = off;
