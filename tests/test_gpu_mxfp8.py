@@ -118,6 +118,29 @@ def test_decode_paged_small(seed, s_q, seqlens, num_splits):
     assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= LSE_ATOL
 
 
+
+@pytest.mark.parametrize("num_splits", [0, 40])
+def test_decode_paged_above_the_in_kernel_plan_limit(num_splits):
+    """65 work units (65 sequences of 1 to 300 tokens): the page prefix sums come from the
+    separate plan kernel instead of each workgroup's own scan.  Against the oracle on the
+    dequantised cache, and bit for bit against the bf16 kernel on that cache."""
+    rng = np.random.default_rng(79)
+    seqlens = [int(x) for x in rng.integers(1, 301, size=65)]
+    inp = make_custom(79, 65, 1, seqlens, extra_blocks=1)
+    _case(f"paged units=65 splits={num_splits}", inp)
+    d, pool8 = _upload8(inp)
+    qa = absorbed_inputs(inp)
+    ol, lse = mla.decode_paged_mxfp8(dev_bf16(qa), d["q_r"], d["pool8"], d["bt"], d["sl"], scale=inp.scale,
+                                     num_splits=num_splits)
+    deq = F.dequantize_pool(pool8)
+    o16, l16 = mla.decode_paged(dev_bf16(qa), d["q_r"], dev_bf16(oracle.f64_to_bf16_bits(deq)), d["bt"], d["sl"],
+                                scale=inp.scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    ref_ol, ref_lse = oracle.decode_absorbed(qa, inp.q_r, deq, inp.block_table, inp.seqlens, 1, inp.scale)
+    assert_close(host_f64(ol), ref_ol, "out_latent")
+    assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= LSE_ATOL
+    assert np.array_equal(host_bits(ol), host_bits(o16)) and torch.equal(lse, l16)
+
 def test_decode_matches_the_bf16_kernel_on_the_dequantised_cache():
     """Both kernels feed the same bf16 tiles to the same MFMA sequence, so over a bf16
     cache holding the dequantised values the MXFP8 decode reproduces the bf16 decode
