@@ -40,6 +40,9 @@ TRAFFIC = {
     "mxfp8": dict(file="decode_kernel_mxfp8_c3_b64_traffic.md", kernels=("decode_kernel",),
                   sources=(_CSRC + "decode.hip", _CSRC + "common.h", _CSRC + "mxfp8.h"),
                   title="decode_kernel over the MXFP8 cache: paged MLA decode, batch 64, seq_len U[1024,32768]"),
+    "c5": dict(file="decode_kernel_c5_b4_sq2_traffic.md", kernels=("decode_kernel",),
+               sources=(_CSRC + "decode.hip", _CSRC + "common.h", _CSRC + "mxfp8.h"),
+               title="decode_kernel: two-token verify, batch 4, seq_len 131072"),
     "append": dict(file="append_kernel_c3_b64_traffic.md", kernels=("append_kernel", "append_finalize_kernel"),
                    sources=(_CSRC + "append.hip", _CSRC + "append.h", _CSRC + "common.h"),
                    title="cache append: 64 new tokens of the batch-64 workload, d = 7168 (both kernels of a call)"),
@@ -63,14 +66,10 @@ def _dev_i32(a, torch):
 
 
 WARM_SECONDS = 1.5   # untimed decode work before each timed region: the clock settles under the power cap
+FLUSH_BYTES = 1 << 30   # written between cold calls: four times the 256 MiB last-level cache
 
 
-def _time_calls(fn, steps, warmup, torch, mla):
-    """Warm up (`warmup` calls, and at least WARM_SECONDS of calls so that the
-    engine clock has settled), then time exactly `steps` calls between two
-    synchronisations, without any other instrumentation; then run `steps` more
-    calls with the library's per-kernel events for the breakdown.  Returns (ms per
-    call from the stream events around the first run, per-kernel ms per call)."""
+def _warm(fn, warmup, torch):
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
@@ -79,6 +78,76 @@ def _time_calls(fn, steps, warmup, torch, mla):
         for _ in range(10):
             fn(0)
         torch.cuda.synchronize()
+
+
+def _per_call(fn, n, torch, flush=None):
+    """GPU milliseconds of n calls, each between two stream events of its own.  With
+    `flush`, a 1 GiB write runs before every call, outside its events, so the call
+    finds neither its cache pages nor its queries in L2 or the last-level cache."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (e0, e1) in enumerate(ev):
+        if flush is not None:
+            flush()
+        e0.record()
+        fn(i)
+        e1.record()
+    torch.cuda.synchronize()
+    return np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+
+
+def _dist_us(ms):
+    """median / p10 / p90 / mean of per-call times, in microseconds."""
+    us = np.asarray(ms) * 1e3
+    return {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
+            "p90": round(float(np.percentile(us, 90)), 2), "mean": round(float(us.mean()), 2), "calls": int(us.size)}
+
+
+def _flusher(torch):
+    """Evicts L2 and the last-level cache between cold calls: a 1 GiB write, then a 1 GiB
+    read of another buffer, so the caches end up holding clean lines of neither the call's
+    cache pages nor its queries, and no dirty lines are left to be written back during the
+    timed call."""
+    wbuf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    rbuf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    state = {"i": 0}
+
+    def flush():
+        state["i"] += 1
+        wbuf.fill_(state["i"] & 0xFF)
+        torch.amax(rbuf)
+    return flush
+
+
+def run_stream(inp, pool_dev, torch, mla, steps, warmup):
+    """Time mla_stream_pages over a workload: the decode's page stream alone (same split,
+    loads and LDS ring, no arithmetic), the stream-read ceiling the decode kernel is
+    measured against."""
+    bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
+    params = mla.make_params(inp.batch, inp.s_q, inp.max_blocks, int(pool_dev.shape[0]), inp.scale)
+    ws = torch.empty(mla.workspace_size(params), dtype=torch.uint8, device="cuda")
+    sums = torch.empty(mla.decode_num_workgroups(params) * 256, dtype=torch.int32, device="cuda")
+
+    def step(i):
+        mla.stream_pages(pool_dev, bt, sl, s_q=inp.s_q, sums=sums, workspace=ws)
+    _warm(step, warmup, torch)
+    ms = _per_call(step, steps, torch)
+    cache_bytes = int(inp.seqlens.astype(np.int64).sum()) * ROW_BYTES
+    med = float(np.median(ms))
+    return {"kernel": "stream_kernel (mla_stream_pages)", "timing_us": _dist_us(ms),
+            "GBps_median": round(cache_bytes / (med * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(cache_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def _time_calls(fn, steps, warmup, torch, mla, flush=None):
+    """Warm up (`warmup` calls, and at least WARM_SECONDS of calls so that the
+    engine clock has settled), then time exactly `steps` calls between two
+    synchronisations, without any other instrumentation; then the same number of
+    calls each between its own events, back to back (warm) and, given `flush`,
+    after a 1 GiB write each (cold); then `steps` more calls with the library's
+    per-kernel events for the breakdown.  Returns (ms per call from the stream
+    events around the first run, per-kernel ms per launch of the kernels that ran,
+    {"warm": distribution, "cold": distribution or absent})."""
+    _warm(fn, warmup, torch)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     # the step time: nothing but the calls between the two events
@@ -88,13 +157,16 @@ def _time_calls(fn, steps, warmup, torch, mla):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    dist = {"warm": _dist_us(_per_call(fn, steps, torch))}
+    if flush is not None:
+        dist["cold"] = _dist_us(_per_call(fn, steps, torch, flush))
+        _warm(fn, 0, torch)
     # the per-kernel split: the same calls again with the library's per-kernel events
     with mla.KernelTimer() as kt:
         for i in range(steps):
             fn(i)
         torch.cuda.synchronize()
-    per = {k: v / max(kt.calls, 1) for k, v in kt.ms.items()}
-    return ms, per
+    return ms, kt.per_launch_ms(), dist
 
 
 def _workload_from_synth(name, torch, with_host_pool=True):
@@ -131,13 +203,50 @@ def run_mxfp8(inp, pool_dev, torch, mla, steps, warmup):
     def step(i):
         mla.decode_paged_mxfp8(q_abs, q_r, pool8, bt, sl, scale=inp.scale, out_latent=out, lse=lse, workspace=ws)
 
-    ms, per = _time_calls(step, steps, warmup, torch, mla)
+    ms, per, dist = _time_calls(step, steps, warmup, torch, mla)
     del pool8
     cache_bytes = int(inp.seqlens.astype(np.int64).sum()) * MXFP8_ROW_BYTES
-    return dict(ms=ms, per=per, cache_bytes=cache_bytes, tokens=int(inp.seqlens.sum()), queries=B * s_q)
+    return dict(ms=ms, per=per, dist=dist, cache_bytes=cache_bytes, tokens=int(inp.seqlens.sum()), queries=B * s_q)
 
 
-def run_paged(inp, pool_dev, torch, mla, steps, warmup, layers=1, pages_per_layer=None):
+def decode_flops(seqlens, s_q):
+    """Algorithmic flops of one decode step: 2 x 128 heads x (576 + 512) per visible
+    (key, query) pair -- the scores over the 576-wide row and P . c_KV over 512."""
+    L = np.asarray(seqlens, dtype=np.int64)
+    visible = int(sum(int(l) - s_q + i + 1 for l in L for i in range(s_q)))
+    return 2 * 128 * (576 + 512) * visible
+
+
+def other_row(oi, orr, layers):
+    """Report row of a workload other than the graded one: step time (back-to-back calls),
+    per-call distributions warm and cold, the decode kernel's time and its roofline -- HBM
+    for one query per sequence, MFMA when several queries share each cache byte."""
+    dec_ms = orr["per"]["decode"]
+    row = {"us_per_step": round(orr["ms"] * 1e3, 2),
+           "cache_GBps": round(orr["cache_bytes"] / (orr["ms"] * 1e-3) / 1e9, 1),
+           "timing_us": orr["dist"],
+           "kernels_us": {k: round(v * 1e3, 2) for k, v in orr["per"].items()},
+           "batch": oi.batch, "s_q": oi.s_q, "cached_tokens": orr["tokens"],
+           "pool": "device-generated bf16 N(0,1)" + (", 60 layers, layer i%60 per call" if layers > 1 else "")}
+    cold = orr["dist"].get("cold")
+    if cold is not None:
+        row["cold_cache_GBps_median"] = round(orr["cache_bytes"] / (cold["median"] * 1e-6) / 1e9, 1)
+    flops = decode_flops(oi.seqlens, oi.s_q)
+    if oi.s_q > 1:
+        tf = flops / (dec_ms * 1e-3) / 1e12
+        row["roofline"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                           "kernel": "decode_kernel", "algorithmic_flops_per_launch": flops,
+                           "hbm_GBps_of_cache": round(orr["cache_bytes"] / (dec_ms * 1e-3) / 1e9, 1)}
+    else:
+        gb = orr["cache_bytes"] / (dec_ms * 1e-3) / 1e9
+        row["roofline"] = {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(gb / HBM_PEAK_GBS, 4), "kernel": "decode_kernel",
+                           "algorithmic_bytes_per_launch": orr["cache_bytes"]}
+    return row
+
+
+def run_paged(inp, pool_dev, torch, mla, steps, warmup, layers=1, pages_per_layer=None, flush=None):
     """Time the paged decode of one workload; returns a result dict."""
     q_abs = mla.absorb_q(_dev_bf16(inp.q_c, torch), _dev_bf16(inp.w_uk, torch))
     q_r = _dev_bf16(inp.q_r, torch)
@@ -153,9 +262,9 @@ def run_paged(inp, pool_dev, torch, mla, steps, warmup, layers=1, pages_per_laye
         mla.decode_paged(q_abs, q_r, pool_dev, bts[i % layers], sl, scale=inp.scale, out_latent=out, lse=lse,
                          workspace=ws)
 
-    ms, per = _time_calls(step, steps, warmup, torch, mla)
+    ms, per, dist = _time_calls(step, steps, warmup, torch, mla, flush)
     cache_bytes = int(inp.seqlens.astype(np.int64).sum()) * ROW_BYTES
-    return dict(ms=ms, per=per, cache_bytes=cache_bytes, tokens=int(inp.seqlens.sum()), queries=B * s_q)
+    return dict(ms=ms, per=per, dist=dist, cache_bytes=cache_bytes, tokens=int(inp.seqlens.sum()), queries=B * s_q)
 
 
 D_MODEL = 7168                 # hidden size d of the appended tokens' states
@@ -341,9 +450,23 @@ def run_prefill(torch, mla, steps, warmup):
     }
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(inp, seconds):
-    """The fp64 oracle (absorbed form), timed on host cores on a bounded sample
-    of the same workload's sequences."""
+    """The fp64 oracle timed on host cores over the same workload's inputs: the absorbed
+    form (what the kernels compute) on whole sequences until `seconds` have passed, and
+    the decompressed form (the definition parity is checked against) on the shortest
+    sequence, heads added until about `seconds` more have passed; both extrapolated to
+    the whole step."""
     import oracle
     qa = oracle.absorb_q(inp.q_c, inp.w_uk)
     order = np.random.default_rng(0).permutation(inp.batch)
@@ -356,11 +479,32 @@ def cpu_baseline(inp, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-    return {"value": toks * ROW_BYTES / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+    total = int(inp.seqlens.sum())
+    # decompressed: the shortest sequence, heads in blocks of 8 until the time is spent
+    b = int(np.argmin(inp.seqlens))
+    heads_done = 0
+    t1 = time.perf_counter()
+    while heads_done < 128:
+        hs = list(range(heads_done, min(heads_done + 8, 128)))
+        oracle.decode_decompressed(inp.q_c, inp.q_r, inp.w_uk, inp.w_uv, inp.pool, inp.block_table, inp.seqlens,
+                                   inp.s_q, inp.scale, batches=[b], heads=hs)
+        heads_done += len(hs)
+        if time.perf_counter() - t1 >= seconds:
+            break
+    dd = time.perf_counter() - t1
+    dd_step = dd * (128 / heads_done) * (total / int(inp.seqlens[b]))
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {"value": toks * ROW_BYTES / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"oracle.decode_absorbed (fp64) on {len(done)} of {inp.batch} sequences "
                       f"({toks} cached tokens) in {dt:.1f}s; seconds_per_step_extrapolated="
-                      f"{dt * int(inp.seqlens.sum()) / max(toks, 1):.1f}"}
+                      f"{dt * total / max(toks, 1):.1f}",
+            "host_cores_available": len(os.sched_getaffinity(0)), "blas_threads": threads,
+            "cpu_model": _cpu_model(),
+            "decompressed": {"value": total * ROW_BYTES / dd_step / 1e9, "unit": "GB/s",
+                             "seconds_per_step_extrapolated": round(dd_step, 1),
+                             "sample": f"oracle.decode_decompressed (fp64, K and V expanded per head) on sequence "
+                                       f"{b} ({int(inp.seqlens[b])} tokens), {heads_done} of 128 heads, "
+                                       f"in {dd:.1f}s"}}
 
 
 def main():
@@ -368,7 +512,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--extra", default="c1,c2,c3max,c5",
+    ap.add_argument("--extra", default="c1,c2,c3max,c4,c5",
                     help="comma list of other workloads timed for the report (c1,c2,c3max,c4,c5 or none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -378,6 +522,8 @@ def main():
                          "(target of rocprofv3 --pmc passes)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from the FETCH_SIZE and WRITE_SIZE pass output folders")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="write the decode kernel's cycle and instruction attribution from counter pass folders")
     ap.add_argument("--pmc-kind", default="decode", choices=sorted(TRAFFIC),
                     help="kernel family of --summarize-pmc")
     ap.add_argument("--pmc-command", action="append", default=[],
@@ -385,6 +531,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.pmc_command, args.pmc_kind)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.pmc_command)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -406,11 +555,14 @@ def main():
     # ---- graded workload: batch 64, lengths U[1024, 32768]
     inp = _workload_from_synth("c3", torch)
     pool = _dev_bf16(inp.pool, torch)
-    r = run_paged(inp, pool, torch, mla, args.steps, args.warmup)
+    flush = _flusher(torch)
+    r = run_paged(inp, pool, torch, mla, args.steps, args.warmup, flush=flush)
     ms = r["ms"]
     gbs = r["cache_bytes"] / (ms * 1e-3) / 1e9
     dec_ms = r["per"]["decode"]
     achieved = r["cache_bytes"] / (dec_ms * 1e-3) / 1e9
+    stream = run_stream(inp, pool, torch, mla, args.steps, args.warmup)
+    log(f"[bench] c3 stream ceiling: {stream}")
     log(f"[bench] c3 paged: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s; kernels us: "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in r["per"].items() if v > 0))
 
@@ -421,9 +573,9 @@ def main():
     fout = torch.empty(inp.batch, 1, 128, 128, dtype=torch.bfloat16, device="cuda")
     fparams = mla.make_params(inp.batch, 1, inp.max_blocks, inp.num_pages, inp.scale)
     fws = torch.empty(mla.workspace_size(fparams, fused=True), dtype=torch.uint8, device="cuda")
-    fms, fper = _time_calls(lambda i: mla.decode(d_qc, d_qr, d_wuk, d_wuv, pool, d_bt, d_sl, scale=inp.scale,
-                                                 out=fout, workspace=fws, want_lse=False),
-                            args.steps, args.warmup, torch, mla)
+    fms, fper, fdist = _time_calls(lambda i: mla.decode(d_qc, d_qr, d_wuk, d_wuv, pool, d_bt, d_sl,
+                                                        scale=inp.scale, out=fout, workspace=fws, want_lse=False),
+                                   args.steps, args.warmup, torch, mla)
     log(f"[bench] c3 fused: {fms * 1e3:.1f} us/step; kernels us: "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in fper.items()))
 
@@ -436,7 +588,8 @@ def main():
         "workload": "the batch-64 workload above, cache in MXFP8 (E4M3 codes, one E8M0 scale per 32 latent "
                     "values, bf16 k_R: 656 B per token)",
         "us_per_step": round(f8["ms"] * 1e3, 2),
-        "kernels_us": {k: round(v * 1e3, 2) for k, v in f8["per"].items() if v > 0},
+        "timing_us": f8["dist"],
+        "kernels_us": {k: round(v * 1e3, 2) for k, v in f8["per"].items()},
         "cache_bytes_per_step": f8["cache_bytes"],
         "cache_GBps": round(f8["cache_bytes"] / (f8["ms"] * 1e-3) / 1e9, 1),
         "kv_tokens_per_s": round(f8["tokens"] / (f8["ms"] * 1e-3), 1),
@@ -455,13 +608,10 @@ def main():
         oi = make_inputs(name, with_pool=False)
         layers = 60 if name == "c4" else 1
         opool = _device_pool(oi.num_pages * layers, oi.seed, torch)
-        orr = run_paged(oi, opool, torch, mla, max(args.steps // 2, 5), 3, layers=layers,
-                        pages_per_layer=oi.num_pages)
-        others[name] = {"us_per_step": round(orr["ms"] * 1e3, 2),
-                        "cache_GBps": round(orr["cache_bytes"] / (orr["ms"] * 1e-3) / 1e9, 1),
-                        "decode_kernel_us": round(orr["per"]["decode"] * 1e3, 2),
-                        "batch": oi.batch, "s_q": oi.s_q, "cached_tokens": orr["tokens"],
-                        "pool": "device-generated bf16 N(0,1)" + (", 60 layers, layer i%60 per call" if layers > 1 else "")}
+        # the 60-layer cache cycles through 72 GB, its own rotation; the others are flushed
+        orr = run_paged(oi, opool, torch, mla, max(args.steps, 20), 3, layers=layers,
+                        pages_per_layer=oi.num_pages, flush=None if layers > 1 else flush)
+        others[name] = other_row(oi, orr, layers)
         log(f"[bench] {name}: {others[name]}")
         del opool
         torch.cuda.empty_cache()
@@ -500,18 +650,25 @@ def main():
         "config": {"workload": "paged MLA decode, batch 64, seq_len U[1024,32768] (seed 44, sum 1166687), "
                                "1 query token, 128 heads, latent 512 + rope 64 bf16, page 64, permuted pages",
                    "batch": inp.batch, "cached_tokens": r["tokens"], "pages": inp.num_pages,
-                   "num_splits": device_cus(mla), "cache_bytes_per_step": r["cache_bytes"]},
+                   "num_splits": mla.decode_num_workgroups(mla.make_params(inp.batch, 1, inp.max_blocks,
+                                                                           inp.num_pages, inp.scale)),
+                   "cache_bytes_per_step": r["cache_bytes"]},
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "kv_tokens_per_s": round(r["tokens"] / (ms * 1e-3), 1),
         "query_tokens_per_s": round(r["queries"] / (ms * 1e-3), 1),
-        "kernels_us": {k: round(v * 1e3, 2) for k, v in r["per"].items() if v > 0},
+        "timing_us": r["dist"],
+        "kernels_us": {k: round(v * 1e3, 2) for k, v in r["per"].items()},
         "fused_us_per_step": round(fms * 1e3, 2),
+        "fused_timing_us": fdist,
         "fused_kernels_us": {k: round(v * 1e3, 2) for k, v in fper.items()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic["fetch"] + traffic["write"]),
                      "traffic_split": traffic,
-                     "kernel": "decode_kernel", "algorithmic_bytes_per_launch": r["cache_bytes"]},
+                     "kernel": "decode_kernel", "algorithmic_bytes_per_launch": r["cache_bytes"],
+                     "measured_stream_ceiling_GBps": stream["GBps_median"],
+                     "frac_of_measured_stream_ceiling": round(achieved / stream["GBps_median"], 4)},
+        "stream_ceiling": stream,
         "cpu_baseline": cpu,
         "other_workloads": others,
         "cache_append": app,
@@ -571,6 +728,13 @@ def pmc_run(steps, warmup, kind="decode"):
         pool = _device_pool(inp.num_pages, inp.seed, torch)
         qa = torch.randn((inp.batch, 1, 128, 512), device="cuda").to(torch.bfloat16)
         qr = torch.randn((inp.batch, 1, 128, 64), device="cuda").to(torch.bfloat16)
+        bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
+        call = lambda: mla.decode_paged(qa, qr, pool, bt, sl, scale=inp.scale)
+    elif kind == "c5":
+        inp = _workload_from_synth("c5", torch, with_host_pool=False)
+        pool = _device_pool(inp.num_pages, inp.seed, torch)
+        qa = torch.randn((inp.batch, 2, 128, 512), device="cuda").to(torch.bfloat16)
+        qr = torch.randn((inp.batch, 2, 128, 64), device="cuda").to(torch.bfloat16)
         bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
         call = lambda: mla.decode_paged(qa, qr, pool, bt, sl, scale=inp.scale)
     elif kind == "mxfp8":
@@ -634,6 +798,69 @@ def _prefill_algorithmic_bytes():
             + B * L * 64 * 2)
 
 
+COUNTER_FILE = "decode_kernel_c3_b64_counters.md"
+def _c3_tiles():
+    from synth import make_inputs
+    inp = make_inputs("c3", with_pool=False)
+    return int(((inp.seqlens.astype(np.int64) + 31) // 32).sum())
+
+
+def summarize_counters(run_dirs, command, kernel="decode_kernel"):
+    """Writes the attribution summary of the decode kernel from rocprofv3 --pmc passes over
+    `bench.py --pmc-run decode`: every counter averaged over the kernel's launches (the first,
+    cold launch left out), then per tile per wave (instruction counts) and as shares of the
+    waves' cycles (SQ_WAVE_CYCLES; the SQ cycle counters share its quad-cycle unit)."""
+    vals = {}
+    for d in run_dirs:
+        import glob
+        import csv
+        names = set()
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    names.add(r["Counter_Name"])
+        for name in names:
+            per = _pmc_per_dispatch(d, name)
+            v = [x for k, xs in per.items() if kernel + "<" in k or kernel + "(" in k for x in xs]
+            if v:
+                vals.setdefault(name, []).append(sum(v[1:]) / max(len(v) - 1, 1) if len(v) > 1 else v[0])
+    avg = {k: float(np.mean(v)) for k, v in vals.items()}
+    tiles = _c3_tiles()
+    wave_tiles = 4 * tiles
+    lines = [
+        "# Cycle and instruction attribution of decode_kernel: paged MLA decode, batch 64, seq_len U[1024,32768]",
+        "",
+        f"rocprofv3 counter passes (one per line, at most 8 SQ counters each) over `python3 bench.py --pmc-run "
+        "decode`, run from /tmp:",
+        "",
+        "```",
+        *command,
+        "```",
+        "",
+        f"Values are per launch of decode_kernel (the first launch of each pass left out). The workload has "
+        f"{tiles} tiles of 32 tokens; each is processed by all four waves of its workgroup, so per-tile-per-wave "
+        f"figures divide by {wave_tiles}. Cycle counters are shares of SQ_WAVE_CYCLES (the SQ counts wave cycles "
+        "in quad-cycle units, the same unit for all of them); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+        "(GRBM_GUI_ACTIVE / 8 dies x 1024 SIMDs).",
+        "",
+        "| counter | per launch | per tile per wave | share of wave cycles |",
+        "|---|---|---|---|",
+    ]
+    wc = avg.get("SQ_WAVE_CYCLES")
+    for k in sorted(avg):
+        share = f"{avg[k] / wc:.3f}" if wc and (("CYCLES" in k or k.startswith(("SQ_WAIT", "SQ_ACTIVE", "SQ_BUSY")))
+                                                and k.startswith("SQ_")) else ""
+        lines.append(f"| {k} | {avg[k]:.4g} | {avg[k] / wave_tiles:.2f} | {share} |")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg:
+        busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] / 8 * 1024)
+        lines += ["", f"MFMA busy share of the launch's cycles: {busy:.3f}."]
+    lines += ["", f"source_sha256: {kernel_source_hash('decode')}", ""]
+    path = os.path.join(ROOT, "profiles", COUNTER_FILE)
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    log(f"[bench] wrote {path}")
+
+
 def summarize_pmc(fetch_dir, write_dir, command, kind="decode"):
     """Writes the traffic summary of a kernel family: FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch) of its kernels, each scaled by COPY_BYTES over what the same counter reads
@@ -663,6 +890,8 @@ def summarize_pmc(fetch_dir, write_dir, command, kind="decode"):
         alg, alg_note = 1166687 * ROW_BYTES, "cache rows read once"
     elif kind == "mxfp8":
         alg, alg_note = 1166687 * MXFP8_ROW_BYTES, "MXFP8 cache rows read once"
+    elif kind == "c5":
+        alg, alg_note = 4 * 131072 * ROW_BYTES, "cache rows read once (both queries of a sequence share them)"
     elif kind == "append":
         alg, alg_note = append_algorithmic_bytes(64), "W_A, x, rows written, table rows, table entries and lengths"
     else:
@@ -700,13 +929,6 @@ def summarize_pmc(fetch_dir, write_dir, command, kind="decode"):
     with open(path, "w") as f:
         f.write("\n".join(lines))
     log(f"[bench] wrote {path}: fetch {fetch:.0f} B, write {write:.0f} B per launch")
-
-
-def device_cus(mla):
-    try:
-        return mla.device_cu_count()
-    except Exception:  # noqa: BLE001
-        return None
 
 
 if __name__ == "__main__":

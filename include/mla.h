@@ -92,12 +92,22 @@ mla_status mla_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_a
                         int32_t tokens, int32_t num_heads, void* stream);
 
 /* Workspace bytes needed by mla_decode_paged (fused = 0) or mla_decode
- * (fused = 1) for these parameters.  With p->num_splits == 0 the current
- * device's compute-unit count is queried (a HIP call).  Returns 0 when p is
- * invalid or the query fails. */
+ * (fused = 1) for these parameters: the pages-per-unit prefix sums, the
+ * normalised partial outputs and lse of sequences split across workgroups,
+ * and, when fused, q_abs and out_latent.  The pages size the cache by its
+ * 64-token pages of 1152-byte rows (sheratonhq.com sections 1 and 3) and say
+ * nothing of a split over the sequence; the split-KV workspace is this
+ * library's.  With p->num_splits == 0 the current device's compute-unit count
+ * is queried (a HIP call).  Returns 0 when p is invalid (including
+ * 2 * batch * s_q * max_blocks_per_seq > 2^31 - 1: the sums of 32-token tiles
+ * over sequences are 32-bit) or the query fails. */
 size_t mla_decode_workspace_size(const mla_decode_params* p, int32_t fused);
 
-/* Paged decode in latent space (split-KV over pages, log-sum-exp merge).
+/* Paged decode in latent space (split-KV over pages, log-sum-exp merge):
+ * scores (q_abs . c_KV + q_R . k_R) * scale over the rows the block table
+ * names (sheratonhq.com section 4, path B; section 3, page_size 64; section 5,
+ * the page table feeding 16-byte loads), softmax, and P . c_KV kept in latent
+ * space for the later W_UV projection (leslieaibin.github.io section "MLA").
  *   q_abs       [B, s_q, H, 512] bf16   absorbed content query
  *   q_r         [B, s_q, H, 64]  bf16   RoPE query (already rotated)
  *   kv_blocks   [num_pages, 64, 576] bf16, row = c_KV[512] || k_R[64]
@@ -122,7 +132,10 @@ mla_status mla_decode_paged(const uint16_t* q_abs, const uint16_t* q_r, const ui
 mla_status mla_up_proj(const uint16_t* out_latent, const uint16_t* w_uv, uint16_t* out,
                        int32_t tokens, int32_t num_heads, void* stream);
 
-/* Fused decode step: absorb -> paged decode -> merge -> up-projection.
+/* Fused decode step: absorb -> paged decode -> merge -> up-projection; the
+ * same function as expanding K = c . W_UK[h] and V = c . W_UV[h] per head and
+ * running plain attention (sheratonhq.com section 4, paths A and B;
+ * leslieaibin.github.io section "MLA").
  *   q_c [B, s_q, H, 128], q_r [B, s_q, H, 64], w_uk [H, 128, 512],
  *   w_uv [H, 512, 128], out [B, s_q, H, 128] bf16, lse as above (may be NULL).
  * workspace >= mla_decode_workspace_size(p, 1) bytes (holds q_abs and
@@ -133,8 +146,9 @@ mla_status mla_decode(const uint16_t* q_c, const uint16_t* q_r, const uint16_t* 
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Test export of the page gather: dense[b, t, :] = kv_blocks[block_table[b][t / 64], t % 64, :]
- * for t < seqlens[b]; rows t in [seqlens[b], max_blocks_per_seq * 64) are zero.
- * dense [B, max_blocks_per_seq * 64, 576] bf16. */
+ * for t < seqlens[b]; rows t in [seqlens[b], max_blocks_per_seq * 64) are zero
+ * (the paging of sheratonhq.com section 3, page_size 64, and the page-table
+ * lookup of section 5).  dense [B, max_blocks_per_seq * 64, 576] bf16. */
 mla_status mla_gather_kv(const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens,
                          uint16_t* dense, const mla_decode_params* p, void* stream);
 
@@ -316,13 +330,16 @@ mla_status mla_append_kv_mxfp8(const uint16_t* x, const uint16_t* w_a, const flo
 /* Benchmark timing hook.  After mla_profile_enable(1), every mla_decode_paged
  * and mla_decode call (either cache format) on any stream records HIP events around each of its
  * kernels (up to 65536 calls; the library creates those events once and keeps
- * them).  mla_profile_collect waits for the recorded calls, writes the summed
- * milliseconds of [absorb, plan, decode, combine, up-projection] to ms[0..4]
- * (host array of 5) and the number of calls to *calls, and clears the record.
+ * them).  mla_profile_collect waits for the recorded calls and, for kernel k of
+ * [absorb, plan, decode, combine, up-projection], writes to launches[k] the
+ * number of calls that launched it and to ms[k] the summed milliseconds of
+ * those launches (host arrays of 5; a paged call launches no absorb or
+ * up-projection, and with at most 64 sequence-query units no plan kernel, so
+ * those stay 0), the number of calls to *calls, and clears the record.
  * mla_profile_enable(0) stops recording.  Off by default; not for code under
  * graph capture. */
 mla_status mla_profile_enable(int32_t enable);
-mla_status mla_profile_collect(double* ms, int32_t* calls);
+mla_status mla_profile_collect(double* ms, int32_t* launches, int32_t* calls);
 
 /* The same hook for mla_append_kv and mla_append_kv_mxfp8 calls (recorded while mla_profile_enable(1) is
  * in force, up to 65536 calls): writes the summed milliseconds of [projection
@@ -334,6 +351,29 @@ mla_status mla_profile_collect_append(double* ms, int32_t* calls);
 /* The same for decompress-branch mla_prefill calls: ms[0] = decompress kernels,
  * ms[1] = attention kernel. */
 mla_status mla_profile_collect_prefill(double* ms, int32_t* calls);
+
+/* Decode workgroups (split-KV ranges) that mla_decode_paged, mla_decode and
+ * mla_stream_pages launch for these parameters: p->num_splits when > 0, else the
+ * current device's compute-unit count (a HIP call).  0 when p is invalid. */
+int32_t mla_decode_num_workgroups(const mla_decode_params* p);
+
+/* Measurement of the page stream alone.  The pages call decode memory-bound: its
+ * arithmetic intensity sits far below the roofline ridge, so HBM bandwidth sets its
+ * speed (sheratonhq.com section 1).  This call reads exactly the cache rows
+ * mla_decode_paged reads for the same arguments, with the same work split, the same
+ * 16-byte direct loads into the same LDS ring and the same per-tile workgroup
+ * barrier, and does no arithmetic on them: its time is the stream-read ceiling of the
+ * decode on the device.  So that every load is observable, thread t of workgroup g
+ * writes to sums[g * 256 + t] the 32-bit sum (mod 2^32) of dword t of the first row
+ * of every 32-token tile the workgroup streams (the tile's first token's latent,
+ * 256 dwords); the sum of all of sums[] is therefore the sum, over every tile of
+ * every (sequence, query) unit, of that row's latent dwords.
+ *   kv_blocks, block_table, seqlens, p: as for mla_decode_paged (p->scale unused)
+ *   sums       [mla_decode_num_workgroups(p) * 256] uint32, 4-byte aligned
+ *   workspace  >= mla_decode_workspace_size(p, 0) bytes (the tile prefix sums) */
+mla_status mla_stream_pages(const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens,
+                            uint32_t* sums, const mla_decode_params* p, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Number of compute units of the current device (a HIP call). */
 mla_status mla_device_cu_count(int32_t* num_cus);

@@ -28,6 +28,7 @@ __all__ = [
     "append_workspace", "append_workspace_size", "make_append_params", "rope_q", "rope_table",
     "PrefillParams", "make_prefill_params", "prefill", "prefill_workspace_size", "PREFILL_THRESHOLD",
     "MXFP8_ROW_BYTES", "quantize_kv_mxfp8", "decode_paged_mxfp8", "decode_mxfp8", "append_kv_mxfp8",
+    "decode_num_workgroups", "stream_pages",
 ]
 
 MXFP8_ROW_BYTES = 656    # MXFP8 cache row: 512 E4M3 codes, 16 E8M0 scale bytes, 64 bf16 of k_R
@@ -241,8 +242,10 @@ class KernelTimer:
     """Per-kernel HIP-event timing of decode and cache-append calls (library hook; see
     mla_profile_enable).
 
-    with KernelTimer() as kt: ...calls...;  kt.ms -> dict of summed milliseconds of decode
-    calls, kt.calls; kt.append_ms, kt.append_calls likewise for append calls."""
+    with KernelTimer() as kt: ...calls...;  kt.ms -> dict of summed milliseconds per kernel of
+    decode calls, holding only kernels that were launched, kt.launches -> how many calls
+    launched each of them, kt.calls; kt.per_launch_ms() -> average milliseconds per launch;
+    kt.append_ms, kt.append_calls likewise for append calls."""
 
     NAMES = ("absorb", "plan", "decode", "combine", "up_proj")
 
@@ -257,8 +260,9 @@ class KernelTimer:
     def __exit__(self, *exc):
         lib = _lib.load()
         ms = (ctypes.c_double * 5)()
+        launches = (ctypes.c_int32 * 5)()
         calls = ctypes.c_int32(0)
-        st = lib.mla_profile_collect(ms, ctypes.byref(calls))
+        st = lib.mla_profile_collect(ms, launches, ctypes.byref(calls))
         ams = (ctypes.c_double * 2)()
         acalls = ctypes.c_int32(0)
         st2 = lib.mla_profile_collect_append(ams, ctypes.byref(acalls))
@@ -271,11 +275,48 @@ class KernelTimer:
         self.prefill_calls = int(pcalls.value)
         _lib.check(st, "mla_profile_collect")
         _lib.check(st2, "mla_profile_collect_append")
-        self.ms = dict(zip(self.NAMES, list(ms)))
+        self.launches = {k: int(n) for k, n in zip(self.NAMES, list(launches)) if n > 0}
+        self.ms = {k: v for k, v in zip(self.NAMES, list(ms)) if k in self.launches}
         self.calls = int(calls.value)
         self.append_ms = dict(zip(self.APPEND_NAMES, list(ams)))
         self.append_calls = int(acalls.value)
         return False
+
+    def per_launch_ms(self):
+        """Average milliseconds per launch of each decode-call kernel that ran."""
+        return {k: v / self.launches[k] for k, v in self.ms.items()}
+
+
+def decode_num_workgroups(params: DecodeParams) -> int:
+    """Split-KV workgroups a decode with these parameters launches."""
+    lib = _lib.load()
+    n = lib.mla_decode_num_workgroups(ctypes.byref(params))
+    if n <= 0:
+        raise MlaError(_lib.MLA_ERR_INVALID_ARG, "mla_decode_num_workgroups", lib.mla_last_error().decode())
+    return int(n)
+
+
+def stream_pages(kv_blocks, block_table, seqlens, *, s_q=1, num_splits=0, sums=None, workspace=None):
+    """The decode's page stream alone (mla_stream_pages): reads every cache row a decode
+    over these sequences reads, with the decode's split, loads and LDS ring, and no
+    arithmetic.  Returns sums [workgroups * 256] uint32 (see include/mla.h)."""
+    torch = _torch()
+    B = int(block_table.shape[0])
+    mb = int(block_table.shape[1])
+    P = int(kv_blocks.shape[0])
+    params = make_params(B, s_q, mb, P, DEFAULT_SCALE, num_splits)
+    n = decode_num_workgroups(params) * 256
+    if sums is None:
+        sums = torch.empty(n, dtype=torch.int32, device=kv_blocks.device)
+    workspace, need = _workspace(params, False, workspace)
+    lib = _lib.load()
+    st = lib.mla_stream_pages(_ptr(kv_blocks, "kv_blocks", _bf16_types(), (P, PAGE, D_C + D_R)),
+                              _ptr(block_table, "block_table", _i32(), (B, mb)),
+                              _ptr(seqlens, "seqlens", _i32(), (B,)),
+                              _ptr(sums, "sums", (torch.int32,), (n,)), ctypes.byref(params),
+                              _ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream())
+    _lib.check(st, "mla_stream_pages")
+    return sums
 
 
 def gather_kv(kv_blocks, block_table, seqlens, out=None):

@@ -42,6 +42,8 @@ EXPORTS = (
     "mla_decode_paged_mxfp8",
     "mla_decode_mxfp8",
     "mla_append_kv_mxfp8",
+    "mla_decode_num_workgroups",
+    "mla_stream_pages",
     "mla_status_string",
     "mla_last_error",
 )
@@ -137,7 +139,8 @@ def load() -> ctypes.CDLL:
         "mla_rope_table": ([vp, i32, ctypes.c_double, vp], ctypes.c_int),
         "mla_device_cu_count": ([ctypes.POINTER(i32)], ctypes.c_int),
         "mla_profile_enable": ([i32], ctypes.c_int),
-        "mla_profile_collect": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)], ctypes.c_int),
+        "mla_profile_collect": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32), ctypes.POINTER(i32)],
+                                ctypes.c_int),
         "mla_profile_collect_append": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)], ctypes.c_int),
         "mla_profile_collect_prefill": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)], ctypes.c_int),
         "mla_prefill_workspace_size": ([fp], sz),
@@ -146,6 +149,8 @@ def load() -> ctypes.CDLL:
         "mla_decode_paged_mxfp8": ([vp, vp, vp, vp, vp, vp, vp, pp, vp, sz, vp], ctypes.c_int),
         "mla_decode_mxfp8": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, sz, vp], ctypes.c_int),
         "mla_append_kv_mxfp8": ([vp, vp, vp, vp, vp, vp, vp, ap, vp, sz, vp], ctypes.c_int),
+        "mla_decode_num_workgroups": ([pp], i32),
+        "mla_stream_pages": ([vp, vp, vp, vp, pp, vp, sz, vp], ctypes.c_int),
         "mla_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "mla_last_error": ([], ctypes.c_char_p),
     }

@@ -80,6 +80,10 @@ __device__ __forceinline__ s16x8 lds_read_b128_at(uint32_t addr) {
   return *(MLA_LDS const s16x8*)(uintptr_t)addr;
 }
 
+// Fewest 32-token tiles a decode workgroup takes when the caller lets the library size
+// the split (num_splits = 0); an explicit num_splits splits the tiles evenly.
+constexpr int kAutoMinChunk = 1;
+
 // Host-side launch helpers (defined in the kernel translation units).
 struct DecodePlanView {
   int32_t* cum;       // [units + 1] prefix sums of pages per work unit
@@ -93,8 +97,17 @@ hipError_t launch_up_proj(const uint16_t* ol, const uint16_t* w_uv, uint16_t* ou
 // Exactly one of kv (bf16 cache) and kv8 (MXFP8 cache) is non-null.
 hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv, const unsigned char* kv8,
                          const int32_t* bt, const int32_t* seqlens, uint16_t* out_latent, float* lse, int batch,
-                         int s_q, int max_blocks, int64_t num_pages, float scale, int wgs, const DecodePlanView& plan,
-                         hipStream_t s, hipEvent_t ev_plan_done = nullptr, hipEvent_t ev_decode_done = nullptr);
+                         int s_q, int max_blocks, int64_t num_pages, float scale, int wgs, int min_chunk,
+                         const DecodePlanView& plan, hipStream_t s, hipEvent_t ev_plan_done = nullptr,
+                         hipEvent_t ev_decode_done = nullptr);
+// Whether a decode of this many (sequence, query) units launches the separate
+// prefix-sum kernel (smaller ones compute the sums inside every decode workgroup).
+bool decode_launches_plan(int units);
+// The decode's page stream alone (same split, loads and LDS ring, no arithmetic); sums
+// [wgs * 256] receive per-thread sums of the tiles' first-row dwords.  cum: [units + 1].
+hipError_t launch_stream(const uint16_t* kv, const int32_t* bt, const int32_t* seqlens, uint32_t* sums, int batch,
+                         int s_q, int max_blocks, int64_t num_pages, int wgs, int min_chunk, int32_t* cum,
+                         hipStream_t s);
 hipError_t launch_gather(const uint16_t* kv, const int32_t* bt, const int32_t* seqlens, uint16_t* dense, int batch,
                          int max_blocks, int64_t num_pages, hipStream_t s);
 

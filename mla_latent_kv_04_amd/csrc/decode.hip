@@ -7,14 +7,14 @@
 // ("撕开 DeepSeek MLA 源码", sheratonhq.com, section 4, path B for the scores; the
 // output stays in latent space and is up-projected by W_UV afterwards.)
 //
-// Work split: the pages of all units are laid end to end; workgroup g takes the
-// contiguous range [g*chunk, (g+1)*chunk) of that list (chunk = ceil(total/W)),
-// so every compute unit streams the same number of pages whatever the length
-// mix (the prefix sums of pages per unit come from a wave scan inside each
-// workgroup for up to 64 units, else from plan_kernel).  A unit that lies inside one range is finished in place; a unit cut by
-// range borders leaves one normalised partial per piece (bf16, with an fp32 lse;
-// slot 2g for the first segment of workgroup g, 2g+1 for its last), merged by
-// log-sum-exp afterwards.
+// Work split: the 32-token tiles (half pages) of all units are laid end to end;
+// workgroup g takes the contiguous range [g*chunk, (g+1)*chunk) of that list
+// (chunk = ceil(total/W)), so every compute unit streams the same number of tiles
+// whatever the length mix (the prefix sums of tiles per unit come from a wave scan
+// inside each workgroup for up to 64 units, else from plan_kernel).  A unit that
+// lies inside one range is finished in place; a unit cut by range borders leaves
+// one normalised partial per piece (bf16, with an fp32 lse; slot 2g for the first
+// segment of workgroup g, 2g+1 for its last), merged by log-sum-exp afterwards.
 //
 // Workgroup: 256 threads = 4 waves, one per SIMD.  Pages are processed as
 // 32-token tiles (36 KiB) copied HBM -> LDS with direct 16-byte loads
@@ -40,6 +40,9 @@ namespace mla {
 namespace {
 
 constexpr int kThreads = 256;
+// Tokens per tile: the cache streams in half pages, and the pages of all work units are
+// split across workgroups in whole tiles.
+constexpr int kTile = 32;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct DecodeArgs {
@@ -56,8 +59,17 @@ struct DecodeArgs {
   float* part_lse;
   int64_t num_pages;
   int batch, s_q, max_blocks;
+  int min_chunk;     // fewest tiles a workgroup takes (see split_chunk)
   float scale_log2;  // scale * log2(e)
 };
+
+// Tiles per workgroup range: the tiles split evenly over the W workgroups, but never
+// fewer than min_chunk per workgroup (a workgroup's fixed costs -- its queries, its
+// partial output and the merge of that partial -- then pay for enough tiles).
+__device__ __forceinline__ int split_chunk(int total, int W, int min_chunk) {
+  const int even = (total + W - 1) / W;
+  return even > min_chunk ? even : min_chunk;
+}
 
 // LDS swizzles (the LDS has 64 banks of 4 bytes; a 16-byte read by 16 lanes, or
 // an 8-byte transposing read by 32 lanes, moves 256 bytes per cycle).
@@ -81,10 +93,15 @@ __device__ __forceinline__ int unit_visible(const DecodeArgs& a, int u) {
 // ---------------------------------------------------------------------------- plan
 
 // Up to this many work units (batch x queries), each decode workgroup computes the
-// page prefix sums itself and the plan kernel is not launched.
+// tile prefix sums itself and the plan kernel is not launched.
 constexpr int kSelfPlanUnits = 64;
 
-// Prefix sums of pages per work unit: cum[0] = 0, cum[u+1] = cum[u] + ceil(visible_u / 64).
+// Tiles of a work unit: its visible tokens in 32-token tiles (the work split's grain).
+__device__ __forceinline__ int unit_tiles(int n_visible) {
+  return n_visible > 0 ? (n_visible + kTile - 1) / kTile : 0;
+}
+
+// Prefix sums of tiles per work unit: cum[0] = 0, cum[u+1] = cum[u] + ceil(visible_u / 32).
 __global__ __attribute__((amdgpu_flat_work_group_size(1024, 1024)))
 void plan_kernel(DecodeArgs a, int32_t* cum) {
   __shared__ int32_t warp_tot[16];
@@ -95,13 +112,9 @@ void plan_kernel(DecodeArgs a, int32_t* cum) {
   __syncthreads();
   for (int base = 0; base < U; base += 1024) {
     const int u = base + tid;
-    int pages = 0;
-    if (u < U) {
-      const int n = unit_visible(a, u);
-      pages = n > 0 ? (n + kPage - 1) / kPage : 0;
-    }
+    const int tiles = u < U ? unit_tiles(unit_visible(a, u)) : 0;
     // inclusive scan inside the wave
-    int x = pages;
+    int x = tiles;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(x, off, 64);
@@ -125,7 +138,6 @@ void plan_kernel(DecodeArgs a, int32_t* cum) {
 // 160 KiB of LDS exactly.  Tile slot layout: latent region [32 tokens][1024 B]
 // at offset 0, RoPE region [32 tokens][128 B] at offset 32768, both swizzled as
 // above.
-constexpr int kTile = 32;
 constexpr int kTileBytes = kTile * kRowBytes;        // 36864
 constexpr int kRopeRegion = kTile * kLatent * 2;     // 32768
 constexpr int kSlots = 4;
@@ -241,6 +253,59 @@ __device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int64_t i) {
   return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
+// A workgroup's share of the work: tiles [start, end) of the tiles of all units laid
+// end to end (chunk = ceil(total / W) per workgroup), unit u holding tile `start`, and
+// ubeg, the first tile of unit u.
+struct WorkRange {
+  int start, end, u, ubeg;
+};
+
+// False when the workgroup has no tiles.  Up to kSelfPlanUnits units every wave scans
+// the lengths itself (lane u holds unit u) and workgroup 0 publishes the prefix sums for
+// the combine; more units read plan_kernel's array.
+__device__ __forceinline__ bool work_range(const DecodeArgs& a, int lane, WorkRange& r) {
+  const int U = a.batch * a.s_q;
+  int total, pex = 0;             // pex: exclusive prefix of this lane's unit
+  const bool self_plan = U <= kSelfPlanUnits;
+  if (self_plan) {
+    const int tiles = lane < U ? unit_tiles(unit_visible(a, lane)) : 0;
+    int x = tiles;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    total = __builtin_amdgcn_readlane(x, 63);
+    pex = x - tiles;
+    if (blockIdx.x == 0 && threadIdx.x < 64) {
+      if (lane < U) a.cum[lane + 1] = x;
+      if (lane == 0) a.cum[0] = 0;
+    }
+  } else {
+    total = ld_uniform(a.cum, U);
+  }
+  if (total <= 0) return false;
+  const int chunk = split_chunk(total, (int)gridDim.x, a.min_chunk);
+  r.start = blockIdx.x * chunk;
+  if (r.start >= total) return false;
+  r.end = min(total, r.start + chunk);
+  // largest u with cum[u] <= start (then cum[u+1] > start)
+  if (self_plan) {
+    // the prefix sums do not decrease, so u + 1 lanes have theirs at or below start
+    r.u = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < U && pex <= r.start)) - 1;
+    r.ubeg = __builtin_amdgcn_readlane(pex, r.u);
+  } else {
+    int lo_u = 0, hi_u = U - 1;
+    while (lo_u < hi_u) {
+      const int mid = (lo_u + hi_u + 1) >> 1;
+      if (ld_uniform(a.cum, mid) <= r.start) lo_u = mid; else hi_u = mid - 1;
+    }
+    r.u = lo_u;
+    r.ubeg = ld_uniform(a.cum, r.u);
+  }
+  return true;
+}
+
 template <bool B>
 struct Flag {
   static constexpr bool value = B;
@@ -264,41 +329,11 @@ void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kF8 ? kF8LdsBytes : kSlots * kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char pbuf[2 * kPBytes];
 
-  const int U = a.batch * a.s_q;
   const int tid = threadIdx.x, lane = tid & 63;
-  // Pages per work unit and their prefix sums.  Up to kSelfPlanUnits units, every wave
-  // scans them itself (lane u holds unit u) and workgroup 0 publishes the sums for the
-  // combine; more units come from the plan kernel's array.
-  int total, pex = 0;             // pex: exclusive prefix of this lane's unit
-  const bool self_plan = U <= kSelfPlanUnits;
-  if (self_plan) {
-    int pages = 0;
-    if (lane < U) {
-      const int n = unit_visible(a, lane);
-      pages = n > 0 ? (n + kPage - 1) / kPage : 0;
-    }
-    int x = pages;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
-    total = __builtin_amdgcn_readlane(x, 63);
-    pex = x - pages;
-    if (blockIdx.x == 0 && tid < 64) {
-      if (lane < U) a.cum[lane + 1] = x;
-      if (lane == 0) a.cum[0] = 0;
-    }
-  } else {
-    total = ld_uniform(a.cum, U);
-  }
-  if (total <= 0) return;
-  const int W = gridDim.x;
-  const int chunk = (total + W - 1) / W;
+  WorkRange wr;
+  if (!work_range(a, lane, wr)) return;
   const int g = blockIdx.x;
-  const int start = g * chunk;
-  if (start >= total) return;
-  const int end = min(total, start + chunk);
+  const int start = wr.start, end = wr.end;
 
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;       // which half of the wave
@@ -346,57 +381,47 @@ void decode_kernel(DecodeArgs a) {
     offV0 = (8 * hi + eb) * 1024 + 64 * eb + 16 * (cb ^ (2 * hi)) + 8 * (lane & 1) + 256 * wave_u;
   }
 
-  // Largest u with cum[u] <= start (then cum[u+1] > start), and ubeg = cum[u].
-  int u, ubeg;
-  if (self_plan) {
-    // the prefix sums do not decrease, so u + 1 lanes have theirs at or below start
-    u = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < U && pex <= start)) - 1;
-    ubeg = __builtin_amdgcn_readlane(pex, u);
-  } else {
-    int lo_u = 0, hi_u = U - 1;
-    while (lo_u < hi_u) {
-      const int mid = (lo_u + hi_u + 1) >> 1;
-      if (ld_uniform(a.cum, mid) <= start) lo_u = mid; else hi_u = mid - 1;
-    }
-    u = lo_u;
-    ubeg = ld_uniform(a.cum, u);
-  }
-  // pages of unit u (as the plan counts them)
-  auto unit_pages = [&](int uu) {
+  int u = wr.u;
+  // tiles of unit u (as the plan counts them)
+  auto unit_tiles_at = [&](int uu) {
     const int bb = uu / a.s_q;
-    const int n = clamp_len(ld_uniform(a.seqlens, bb), a.max_blocks) - a.s_q + (uu - bb * a.s_q) + 1;
-    return n > 0 ? (n + kPage - 1) / kPage : 0;
+    return unit_tiles(clamp_len(ld_uniform(a.seqlens, bb), a.max_blocks) - a.s_q + (uu - bb * a.s_q) + 1);
   };
 
-  // Page offset of the first segment in its unit; -1 once that segment is done (every
+  // Tile offset of the first segment in its unit; -1 once that segment is done (every
   // later segment starts its unit, so the walker keeps no unit start across segments).
-  int seg0_off = start - ubeg;
+  int seg0_off = start - wr.ubeg;
   int pos = start;
   bool redo = false;              // re-run the current segment with m_redo as the reference
   float m_redo = -INFINITY;
   while (pos < end) {
     const int ubeg = pos - (seg0_off >= 0 ? seg0_off : 0);
-    int uend = ubeg + unit_pages(u);
+    int uend = ubeg + unit_tiles_at(u);
     while (uend <= pos) {          // units without visible tokens (never the first)
       ++u;
-      uend = ubeg + unit_pages(u);
+      uend = ubeg + unit_tiles_at(u);
     }
     const int seg_end = min(end, uend);
-    const int p0 = pos - ubeg, p1 = seg_end - ubeg;
+    // tiles t0 .. t1-1 of the unit: tile t is rows 32 (t % 2) .. +31 of logical page t / 2
+    const int t0 = pos - ubeg, t1 = seg_end - ubeg;
     const bool complete = (pos == ubeg) && (seg_end == uend);
     const int slot = complete ? -1 : 2 * g + (seg0_off >= 0 ? 0 : 1);
 
     const int b = u / a.s_q;
     const int n_vis = clamp_len(ld_uniform(a.seqlens, b), a.max_blocks) - a.s_q + (u - b * a.s_q) + 1;
     const int64_t bt_row = (int64_t)b * a.max_blocks;
-    const int tok_begin = p0 * kPage;
-    const int n_tiles = (min(n_vis, p1 * kPage) - tok_begin + kTile - 1) / kTile;   // every tile has a visible token
-
+    const int tok_begin = t0 * kTile;
+    const int n_tiles = t1 - t0;   // every tile has a visible token
+    const int last_page = (t1 - 1) >> 1;
+    // Half of its page that the segment's tile k occupies.  Tiles past the segment's end
+    // (the dummy loads of the last steps) take the first half of the last page, whose
+    // row 0 is a visible token, so they never fetch a row past the sequence.
+    auto tile_half = [&](int k) -> int { return k < n_tiles ? ((t0 + k) & 1) : 0; };
     auto tile_src = [&](int k) -> const unsigned char* {
-      int64_t phys = ld_uniform(a.bt, bt_row + p0 + (k >> 1));
+      int64_t phys = ld_uniform(a.bt, bt_row + ((t0 + k) >> 1));
       phys = phys < 0 ? 0 : (phys >= a.num_pages ? a.num_pages - 1 : phys);
-      if constexpr (kF8) return a.kv8 + phys * (int64_t)kF8PageBytes + (k & 1) * kF8TileBytes;
-      else return (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + (k & 1) * kTileBytes;
+      if constexpr (kF8) return a.kv8 + phys * (int64_t)kF8PageBytes + tile_half(k) * kF8TileBytes;
+      else return (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + tile_half(k) * kTileBytes;
     };
     auto tile_valid = [&](int k) { return min(kTile, n_vis - tok_begin - k * kTile); };
     auto issue = [&](int k) {
@@ -554,7 +579,7 @@ void decode_kernel(DecodeArgs a) {
         if (part != 0) return;
         const int32_t r = __builtin_amdgcn_readfirstlane(raw);
         const int64_t phys = r < 0 ? 0 : (r >= a.num_pages ? a.num_pages - 1 : r);
-        dsrc = a.kv8 + phys * (int64_t)kF8PageBytes + (kn & 1) * kF8TileBytes;
+        dsrc = a.kv8 + phys * (int64_t)kF8PageBytes + tile_half(kn) * kF8TileBytes;
         m0n = lbase + slot_off(kn) + kRopeRegion + 1024 * wave_u;
         m0c = lbase + kF8StageOff + (kn & 1) * kF8Stage + 4096 * wave_u;
         m0s = lbase + kF8ScaleOff + (kn & 1) * kF8ScaleStage + 256 * wave_u;
@@ -565,7 +590,7 @@ void decode_kernel(DecodeArgs a) {
       if (part == 0) {
         const int32_t r = __builtin_amdgcn_readfirstlane(raw);   // uniform: keeps the base in SGPRs
         const int64_t phys = r < 0 ? 0 : (r >= a.num_pages ? a.num_pages - 1 : r);
-        dsrc = (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + (kn & 1) * kTileBytes;
+        dsrc = (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + tile_half(kn) * kTileBytes;
         m0n = lbase + (kn & 3) * kTileBytes + kRopeRegion + 1024 * wave_u;
         // rows at or past `valid` fetch the RoPE chunk of row 0 instead
         const uint32_t r_0 = (uint32_t)(kLatent * 2 + (lane & 7) * 16);
@@ -580,7 +605,7 @@ void decode_kernel(DecodeArgs a) {
       }
     };
     {
-      const int32_t raw2 = ld_uniform(a.bt, bt_row + min(p0 + 1, p1 - 1));
+      const int32_t raw2 = ld_uniform(a.bt, bt_row + min((t0 + 2) >> 1, last_page));
 #pragma unroll
       for (int part = 0; part < 3; ++part) {
         prep_qk(0, part);
@@ -631,7 +656,7 @@ void decode_kernel(DecodeArgs a) {
         if constexpr (!kMasked) {
           // the block-table entry of the page of tile k+3, for the next step's loads
           const int32_t* btp = a.bt + bt_row;
-          const int bto = 4 * min(p0 + ((k + 3) >> 1), p1 - 1);
+          const int bto = 4 * min((t0 + k + 3) >> 1, last_page);
           int32_t bt_next;
           uint32_t m0v = m0n;
           if constexpr (kF8) {
@@ -1028,6 +1053,64 @@ void decode_kernel(DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------- stream (measurement)
+
+// The memory side of decode_kernel<false> alone: the same work split, the same direct
+// 16-byte non-temporal loads of the same 32-token tiles into the same 4-slot LDS ring,
+// two tiles ahead, one workgroup barrier per tile -- and no arithmetic on the tiles.  Its
+// time is the ceiling the decode's page stream can reach on the device.  So that every
+// load is observable, thread t of each workgroup adds dword t of each tile's first row
+// (the latent of the tile's first token, 256 dwords) into a 32-bit sum, stored at
+// sums[block * 256 + t]: the sum over all threads and workgroups is the sum, over every
+// tile of every unit, of its first row's latent dwords (mod 2^32).
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void stream_kernel(DecodeArgs a, uint32_t* __restrict__ sums) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kSlots * kTileBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t acc = 0;
+  WorkRange wr;
+  if (work_range(a, lane, wr)) {
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t lbase = lds_addr(lds);
+    const TileLoadOffsets ldo = tile_load_offsets(lane, wave_u);
+    int u = wr.u, pos = wr.start, seg0_off = wr.start - wr.ubeg;
+    while (pos < wr.end) {
+      const int ubeg = pos - (seg0_off >= 0 ? seg0_off : 0);
+      int uend = ubeg;
+      while (uend <= pos) {          // skips units without visible tokens
+        const int bb = u / a.s_q;
+        uend = ubeg + unit_tiles(clamp_len(ld_uniform(a.seqlens, bb), a.max_blocks) - a.s_q + (u - bb * a.s_q) + 1);
+        if (uend <= pos) ++u;
+      }
+      const int seg_end = min(wr.end, uend);
+      const int t0 = pos - ubeg, n_tiles = seg_end - pos;
+      const int b = u / a.s_q;
+      const int n_vis = clamp_len(ld_uniform(a.seqlens, b), a.max_blocks) - a.s_q + (u - b * a.s_q) + 1;
+      const int64_t bt_row = (int64_t)b * a.max_blocks;
+      auto issue = [&](int k) {
+        int64_t phys = ld_uniform(a.bt, bt_row + ((t0 + k) >> 1));
+        phys = phys < 0 ? 0 : (phys >= a.num_pages ? a.num_pages - 1 : phys);
+        const unsigned char* src = (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + ((t0 + k) & 1) * kTileBytes;
+        issue_tile(src, lbase + (k & 3) * kTileBytes, ldo, wave_u, lane, min(kTile, n_vis - (t0 + k) * kTile));
+      };
+      issue(0);
+      if (n_tiles > 1) issue(1);
+      for (int k = 0; k < n_tiles; ++k) {
+        if (k + 1 < n_tiles) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerTile));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();   // tile k in LDS for all; the slot of tile k+2 was read two steps ago
+        if (k + 2 < n_tiles) issue(k + 2);
+        acc += *(MLA_LDS const uint32_t*)(uintptr_t)(lbase + (k & 3) * kTileBytes + 4 * tid);
+      }
+      __syncthreads();     // the next segment's first loads reuse the slots
+      pos = seg_end;
+      ++u;
+      seg0_off = -1;
+    }
+  }
+  sums[(size_t)blockIdx.x * kThreads + tid] = acc;
+}
+
 // ---------------------------------------------------------------------------- combine
 
 // One workgroup per (work unit, 8 heads); wave w merges heads 2w and 2w+1 of the
@@ -1060,7 +1143,7 @@ void combine_kernel(DecodeArgs a, int W) {
     if (a.lse != nullptr && (lane & 31) == 0) a.lse[(size_t)u * kHeads + head] = -INFINITY;
     return;
   }
-  const int chunk = (total + W - 1) / W;
+  const int chunk = split_chunk(total, W, a.min_chunk);
   const int g0 = ubeg / chunk, g1 = (uend - 1) / chunk;
   if (g0 == g1) return;
 
@@ -1133,16 +1216,18 @@ void gather_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ 
 
 hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv, const unsigned char* kv8,
                          const int32_t* bt, const int32_t* seqlens, uint16_t* out_latent, float* lse, int batch,
-                         int s_q, int max_blocks, int64_t num_pages, float scale, int wgs, const DecodePlanView& plan,
-                         hipStream_t s, hipEvent_t ev_plan_done, hipEvent_t ev_decode_done) {
+                         int s_q, int max_blocks, int64_t num_pages, float scale, int wgs, int min_chunk,
+                         const DecodePlanView& plan, hipStream_t s, hipEvent_t ev_plan_done,
+                         hipEvent_t ev_decode_done) {
   if (batch <= 0) return hipSuccess;
-  DecodeArgs a;
+  DecodeArgs a{};
+  a.min_chunk = min_chunk;
   a.q_abs = q_abs; a.q_r = q_r; a.kv = kv; a.kv8 = kv8; a.bt = bt; a.seqlens = seqlens;
   a.out_latent = out_latent; a.lse = lse; a.cum = plan.cum; a.part_o = plan.part_o; a.part_lse = plan.part_lse;
   a.num_pages = num_pages; a.batch = batch; a.s_q = s_q; a.max_blocks = max_blocks;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = hipSuccess;
-  if (batch * s_q > kSelfPlanUnits) {
+  if (decode_launches_plan(batch * s_q)) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a, plan.cum);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1156,6 +1241,25 @@ hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint1
   if (e != hipSuccess) return e;
   if (ev_decode_done != nullptr && (e = hipEventRecord(ev_decode_done, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(batch * s_q, kHeads / kCombineHeads), dim3(256), 0, s, a, wgs);
+  return hipGetLastError();
+}
+
+bool decode_launches_plan(int units) { return units > kSelfPlanUnits; }
+
+hipError_t launch_stream(const uint16_t* kv, const int32_t* bt, const int32_t* seqlens, uint32_t* sums, int batch,
+                         int s_q, int max_blocks, int64_t num_pages, int wgs, int min_chunk, int32_t* cum,
+                         hipStream_t s) {
+  if (batch <= 0) return hipSuccess;
+  DecodeArgs a{};
+  a.min_chunk = min_chunk;
+  a.kv = kv; a.bt = bt; a.seqlens = seqlens; a.cum = cum;
+  a.num_pages = num_pages; a.batch = batch; a.s_q = s_q; a.max_blocks = max_blocks;
+  if (decode_launches_plan(batch * s_q)) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a, cum);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(stream_kernel, dim3(wgs), dim3(kThreads), 0, s, a, sums);
   return hipGetLastError();
 }
 

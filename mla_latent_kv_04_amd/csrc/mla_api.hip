@@ -6,6 +6,7 @@
 
 #include <array>
 #include <cstdio>
+#include <deque>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -63,6 +64,11 @@ mla_status check_params(const mla_decode_params* p) {
   if (!(p->scale > 0.f) || p->scale > 1e30f) return fail(MLA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (p->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "reserved must be 0");
   if ((int64_t)p->batch * p->s_q > (1 << 24)) return fail(MLA_ERR_INVALID_ARG, "batch * s_q too large");
+  // The kernels sum 32-token tiles per (sequence, query) unit in 32-bit integers; a unit
+  // has at most 2 * max_blocks_per_seq tiles, so this bounds every prefix sum.
+  if ((int64_t)p->batch * p->s_q * p->max_blocks_per_seq * 2 > INT32_MAX)
+    return fail(MLA_ERR_INVALID_ARG, "batch * s_q * max_blocks_per_seq * 2 = %lld tiles exceeds 2^31 - 1",
+                (long long)p->batch * p->s_q * p->max_blocks_per_seq * 2);
   return MLA_OK;
 }
 
@@ -81,6 +87,10 @@ mla_status resolve_wgs(const mla_decode_params* p, int* wgs) {
   *wgs = cus;
   return MLA_OK;
 }
+
+// Fewest tiles per decode workgroup: the library's choice when it sizes the split, none
+// beyond an even split when the caller fixes num_splits.
+int min_chunk(const mla_decode_params* p) { return p->num_splits > 0 ? 1 : mla::kAutoMinChunk; }
 
 struct WsLayout {
   size_t cum, part_lse, part_o, q_abs, out_latent, total;
@@ -108,10 +118,18 @@ WsLayout layout(const mla_decode_params* p, int wgs, bool fused) {
 // Opt-in kernel timing for benchmarks: HIP events recorded on the caller's
 // stream around each kernel of a decode call.  Slot layout: 0 start,
 // 1 absorb done, 2 plan done, 3 decode done, 4 combine done, 5 up-proj done.
+// `ran` has bit k set when kernel k (absorb, plan, decode, combine, up-proj) was
+// launched by the call: an interval with no kernel in it is only event overhead
+// and is left out of the sums.
+constexpr int kProfKernels = 5;
+struct ProfCall {
+  std::array<hipEvent_t, kProfKernels + 1> ev{};
+  unsigned ran = 0;
+};
 struct Profiler {
   std::mutex mu;
   bool enabled = false;
-  std::vector<std::array<hipEvent_t, 6>> ev;
+  std::deque<ProfCall> ev;   // a deque: entries handed out stay where they are
   size_t used = 0;
   // cache-append calls: 0 start, 1 projection done, 2 partial sums done
   std::vector<std::array<hipEvent_t, 3>> aev;
@@ -122,17 +140,20 @@ struct Profiler {
 };
 Profiler g_prof;
 constexpr size_t kMaxProfiledCalls = 1 << 16;
+constexpr unsigned kRanAbsorb = 1u, kRanPlan = 2u, kRanDecode = 4u, kRanCombine = 8u, kRanUpProj = 16u;
 
-hipEvent_t* prof_slot() {
+ProfCall* prof_slot() {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   if (!g_prof.enabled || g_prof.used >= kMaxProfiledCalls) return nullptr;
   if (g_prof.used == g_prof.ev.size()) {
-    std::array<hipEvent_t, 6> e{};
-    for (auto& x : e)
+    ProfCall c;
+    for (auto& x : c.ev)
       if (hipEventCreate(&x) != hipSuccess) return nullptr;
-    g_prof.ev.push_back(e);
+    g_prof.ev.push_back(c);
   }
-  return g_prof.ev[g_prof.used++].data();
+  ProfCall* c = &g_prof.ev[g_prof.used++];
+  c->ran = 0;
+  return c;
 }
 
 hipEvent_t* prof_triple_slot(std::vector<std::array<hipEvent_t, 3>>& v, size_t& used) {
@@ -172,16 +193,19 @@ hipEvent_t* prof_append_slot() { return prof_triple_slot(g_prof.aev, g_prof.ause
 mla_status run_paged(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv, const unsigned char* kv8,
                      const int32_t* bt, const int32_t* seqlens, uint16_t* out_latent, float* lse,
                      const mla_decode_params* p, unsigned char* ws, const WsLayout& L, int wgs, hipStream_t s,
-                     hipEvent_t* ev) {
+                     ProfCall* pc) {
+  hipEvent_t* ev = pc ? pc->ev.data() : nullptr;
   mla::DecodePlanView plan;
   plan.cum = reinterpret_cast<int32_t*>(ws + L.cum);
   plan.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
   plan.part_o = reinterpret_cast<uint16_t*>(ws + L.part_o);
   hipError_t e = mla::launch_decode(q_abs, q_r, kv, kv8, bt, seqlens, out_latent, lse, p->batch, p->s_q,
-                                    p->max_blocks_per_seq, p->num_pages, p->scale, wgs, plan, s,
+                                    p->max_blocks_per_seq, p->num_pages, p->scale, wgs, min_chunk(p), plan, s,
                                     ev ? ev[2] : nullptr, ev ? ev[3] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (ev != nullptr && (e = hipEventRecord(ev[4], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (pc != nullptr && p->batch > 0)
+    pc->ran |= kRanDecode | kRanCombine | (mla::decode_launches_plan(p->batch * p->s_q) ? kRanPlan : 0u);
   return MLA_OK;
 }
 
@@ -430,16 +454,16 @@ mla_status decode_paged_impl(const uint16_t* q_abs, const uint16_t* q_r, const u
   if (workspace == nullptr || workspace_bytes < L.total)
     return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipEvent_t* ev = prof_slot();
-  if (ev != nullptr) {
-    hipError_t e = hipEventRecord(ev[0], s);
-    if (e == hipSuccess) e = hipEventRecord(ev[1], s);
+  ProfCall* pc = prof_slot();
+  if (pc != nullptr) {
+    hipError_t e = hipEventRecord(pc->ev[0], s);
+    if (e == hipSuccess) e = hipEventRecord(pc->ev[1], s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
   st = run_paged(q_abs, q_r, kv_blocks, kv8, block_table, seqlens, out_latent, lse, p,
-                 static_cast<unsigned char*>(workspace), L, wgs, s, ev);
-  if (st == MLA_OK && ev != nullptr) {
-    hipError_t e = hipEventRecord(ev[5], s);
+                 static_cast<unsigned char*>(workspace), L, wgs, s, pc);
+  if (st == MLA_OK && pc != nullptr) {
+    hipError_t e = hipEventRecord(pc->ev[5], s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
   return st == MLA_OK ? ok() : st;
@@ -470,17 +494,19 @@ mla_status decode_fused_impl(const uint16_t* q_c, const uint16_t* q_r, const uin
   const int tokens = p->batch * p->s_q;
   uint16_t* q_abs = reinterpret_cast<uint16_t*>(ws + L.q_abs);
   uint16_t* ol = reinterpret_cast<uint16_t*>(ws + L.out_latent);
-  hipEvent_t* ev = prof_slot();
+  ProfCall* pc = prof_slot();
+  hipEvent_t* ev = pc ? pc->ev.data() : nullptr;
   hipError_t e;
   if (ev != nullptr && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = mla::launch_absorb_q(q_c, w_uk, q_abs, tokens, s);
   if (e != hipSuccess) return hip_fail(e, "absorb_q launch");
   if (ev != nullptr && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  st = run_paged(q_abs, q_r, kv_blocks, kv8, block_table, seqlens, ol, lse, p, ws, L, wgs, s, ev);
+  st = run_paged(q_abs, q_r, kv_blocks, kv8, block_table, seqlens, ol, lse, p, ws, L, wgs, s, pc);
   if (st != MLA_OK) return st;
   e = mla::launch_up_proj(ol, w_uv, out, tokens, s);
   if (e != hipSuccess) return hip_fail(e, "up_proj launch");
   if (ev != nullptr && (e = hipEventRecord(ev[5], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (pc != nullptr) pc->ran |= kRanAbsorb | kRanUpProj;
   return ok();
 }
 
@@ -573,19 +599,24 @@ mla_status mla_profile_enable(int32_t enable) {
   return ok();
 }
 
-mla_status mla_profile_collect(double* ms, int32_t* calls) {
-  if (ms == nullptr || calls == nullptr) return fail(MLA_ERR_INVALID_ARG, "NULL output pointer");
+mla_status mla_profile_collect(double* ms, int32_t* launches, int32_t* calls) {
+  if (ms == nullptr || launches == nullptr || calls == nullptr) return fail(MLA_ERR_INVALID_ARG, "NULL output pointer");
   std::lock_guard<std::mutex> lk(g_prof.mu);
-  for (int k = 0; k < 5; ++k) ms[k] = 0.0;
+  for (int k = 0; k < kProfKernels; ++k) {
+    ms[k] = 0.0;
+    launches[k] = 0;
+  }
   for (size_t i = 0; i < g_prof.used; ++i) {
-    auto& e = g_prof.ev[i];
-    hipError_t r = hipEventSynchronize(e[5]);
+    auto& c = g_prof.ev[i];
+    hipError_t r = hipEventSynchronize(c.ev[kProfKernels]);
     if (r != hipSuccess) return hip_fail(r, "hipEventSynchronize");
-    for (int k = 0; k < 5; ++k) {
+    for (int k = 0; k < kProfKernels; ++k) {
+      if (!(c.ran & (1u << k))) continue;
       float t = 0.f;
-      r = hipEventElapsedTime(&t, e[k], e[k + 1]);
+      r = hipEventElapsedTime(&t, c.ev[k], c.ev[k + 1]);
       if (r != hipSuccess) return hip_fail(r, "hipEventElapsedTime");
       ms[k] += t;
+      ++launches[k];
     }
   }
   *calls = (int32_t)g_prof.used;
@@ -613,6 +644,37 @@ mla_status mla_gather_kv(const uint16_t* kv_blocks, const int32_t* block_table, 
   hipError_t e = mla::launch_gather(kv_blocks, block_table, seqlens, dense, p->batch, p->max_blocks_per_seq,
                                     p->num_pages, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+int32_t mla_decode_num_workgroups(const mla_decode_params* p) {
+  if (check_params(p) != MLA_OK) return 0;
+  int wgs = 0;
+  if (resolve_wgs(p, &wgs) != MLA_OK) return 0;
+  return wgs;
+}
+
+mla_status mla_stream_pages(const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens,
+                            uint32_t* sums, const mla_decode_params* p, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (p->batch == 0) return ok();
+  if (!kv_blocks || !block_table || !seqlens || !sums) return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(kv_blocks) || !aligned16(block_table) || !aligned16(workspace) || !aligned4(sums) ||
+      (reinterpret_cast<uintptr_t>(seqlens) & 3u))
+    return fail(MLA_ERR_MISALIGNED, "tensor or workspace not aligned (16 B; sums and seqlens 4 B)");
+  int wgs = 0;
+  st = resolve_wgs(p, &wgs);
+  if (st != MLA_OK) return st;
+  const WsLayout L = layout(p, wgs, false);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
+  hipError_t e = mla::launch_stream(kv_blocks, block_table, seqlens, sums, p->batch, p->s_q, p->max_blocks_per_seq,
+                                    p->num_pages, wgs, min_chunk(p),
+                                    reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + L.cum),
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream launch");
   return ok();
 }
 

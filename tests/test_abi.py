@@ -77,6 +77,22 @@ def test_bad_params_rejected(lib, field, value, status):
     assert lib.mla_last_error().decode() != ""
 
 
+def test_page_sum_overflow_rejected(lib):
+    """The decode sums 32-token tiles per (sequence, query) unit in 32-bit integers; a unit
+    has at most two tiles per block-table entry, so 2 * batch * s_q * max_blocks_per_seq
+    must stay below 2^31."""
+    over = _params(batch=4096, s_q=2, max_blocks_per_seq=1 << 17, num_splits=8)     # exactly 2^31 tiles
+    assert _paged(lib, over) == _lib.MLA_ERR_INVALID_ARG
+    assert "2^31" in lib.mla_last_error().decode()
+    assert lib.mla_decode_workspace_size(ctypes.byref(over), 0) == 0
+    st = lib.mla_decode(A, A, A, A, A, A, A, A, None, ctypes.byref(over), A, 1 << 40, None)
+    assert st == _lib.MLA_ERR_INVALID_ARG
+    st = lib.mla_decode_paged_mxfp8(A, A, A, A, A, A, None, ctypes.byref(over), A, 1 << 40, None)
+    assert st == _lib.MLA_ERR_INVALID_ARG
+    fits = _params(batch=4096, s_q=2, max_blocks_per_seq=(1 << 17) - 1, num_splits=8)
+    assert lib.mla_decode_workspace_size(ctypes.byref(fits), 0) > 0
+
+
 def test_null_params_and_pointers(lib):
     assert lib.mla_decode_paged(A, A, A, A, A, A, None, None, A, 1 << 30, None) == _lib.MLA_ERR_INVALID_ARG
     assert _paged(lib, _params(), (A, None, A, A, A, A, None)) == _lib.MLA_ERR_INVALID_ARG
@@ -126,6 +142,22 @@ def test_fused_and_gather_argument_checks(lib):
     assert st == _lib.MLA_ERR_MISALIGNED
     assert lib.mla_gather_kv(A, A, A, None, ctypes.byref(p), None) == _lib.MLA_ERR_INVALID_ARG
     assert lib.mla_gather_kv(MIS, A, A, A2, ctypes.byref(p), None) == _lib.MLA_ERR_MISALIGNED
+
+
+def test_stream_and_workgroup_count_argument_checks(lib):
+    p = _params()
+    assert lib.mla_decode_num_workgroups(ctypes.byref(p)) == p.num_splits
+    assert lib.mla_decode_num_workgroups(ctypes.byref(_params(page_size=16))) == 0
+    assert lib.mla_decode_num_workgroups(None) == 0
+    need = lib.mla_decode_workspace_size(ctypes.byref(p), 0)
+    assert lib.mla_stream_pages(A, A, A, A, ctypes.byref(p), A, need - 1, None) == _lib.MLA_ERR_WORKSPACE
+    assert lib.mla_stream_pages(A, A, A, None, ctypes.byref(p), A, need, None) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_stream_pages(MIS, A, A, A, ctypes.byref(p), A, need, None) == _lib.MLA_ERR_MISALIGNED
+    assert lib.mla_stream_pages(A, A, A, ctypes.c_void_p(0x10002), ctypes.byref(p), A, need, None) == \
+        _lib.MLA_ERR_MISALIGNED
+    assert lib.mla_stream_pages(A, A, A, A, ctypes.byref(_params(num_heads=64)), A, need, None) == \
+        _lib.MLA_ERR_UNSUPPORTED
+    assert lib.mla_stream_pages(None, None, None, None, ctypes.byref(_params(batch=0)), None, 0, None) == _lib.MLA_OK
 
 
 # ------------------------------------------------------------------ cache append

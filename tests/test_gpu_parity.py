@@ -126,74 +126,7 @@ def test_decode_paged_around_the_in_kernel_plan_limit(batch, s_q, num_splits):
     assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= LSE_ATOL
 
 # ------------------------------------------------------------------ the five workloads
-
-def _sampled_check(inp, d, qa, ol, lse, batches):
-    ref_ol, ref_lse = oracle.decode_absorbed(qa, inp.q_r, inp.pool, inp.block_table, inp.seqlens, inp.s_q,
-                                             inp.scale, batches=batches)
-    got = host_f64(ol)[batches]
-    assert_close(got, ref_ol, "out_latent")
-    assert np.max(np.abs(lse.double().cpu().numpy()[batches] - ref_lse)) <= LSE_ATOL
-
-
-@pytest.mark.parametrize("name", ["c1", "c2"])
-def test_workload_full_check(name):
-    inp = make_inputs(name)
-    _print_case(name, inp)
-    d = upload(inp)
-    qa = absorbed_inputs(inp)
-    ol, lse = _paged(inp, d, qa)
-    _sampled_check(inp, d, qa, ol, lse, list(range(inp.batch)))
-
-
-@pytest.mark.parametrize("name", ["c3", "c5"])
-def test_workload_sampled_check(name):
-    inp = make_inputs(name)
-    _print_case(name, inp)
-    d = upload(inp)
-    qa = absorbed_inputs(inp)
-    ol, lse = _paged(inp, d, qa)
-    L = inp.seqlens
-    batches = sorted({int(np.argmin(L)), int(np.argmax(L)), inp.batch // 2})
-    _sampled_check(inp, d, qa, ol, lse, batches)
-
-
-def test_workload_c4_sampled_layers():
-    """The 60-layer long-context workload at full size: 16 sequences x 65536 tokens per
-    layer, the 60 layers' caches in one 72 GB device pool (so later layers sit at byte
-    offsets beyond 2^36), one decode call per layer as a model would run it.  Sampled
-    (layer, sequence) pairs are checked against the oracle on host copies of exactly
-    the pages that sequence reads."""
-    import torch
-    inp = make_inputs("c4")
-    layers, P = 60, inp.num_pages
-    _print_case("c4 (60 layers)", inp)
-    g = torch.Generator(device="cuda")
-    g.manual_seed(inp.seed)
-    pool = torch.empty((layers * P, 64, 576), dtype=torch.bfloat16, device="cuda")
-    for i in range(layers):
-        pool[i * P:(i + 1) * P].normal_(generator=g)
-    qa = absorbed_inputs(inp)
-    d_qa, d_qr = dev_bf16(qa), dev_bf16(inp.q_r)
-    d_bt, d_sl = dev_i32(inp.block_table), dev_i32(inp.seqlens)
-    try:
-        for layer in (0, 37, layers - 1):
-            ol, lse = mla.decode_paged(d_qa, d_qr, pool[layer * P:(layer + 1) * P], d_bt, d_sl, scale=inp.scale)
-            torch.cuda.synchronize()
-            got_ol, got_lse = host_f64(ol), lse.double().cpu().numpy()
-            for b in (0, 7, inp.batch - 1):
-                L = int(inp.seqlens[b])
-                n = (L + 63) // 64
-                pages = inp.block_table[b, :n].astype(np.int64)
-                sub = host_bits(pool[layer * P + torch.from_numpy(pages).cuda()])
-                bt1 = np.arange(n, dtype=np.int32).reshape(1, n)
-                ref_ol, ref_lse = oracle.decode_absorbed(qa[b:b + 1], inp.q_r[b:b + 1], sub, bt1,
-                                                         inp.seqlens[b:b + 1], 1, inp.scale)
-                print(f"[c4] layer {layer} seq {b}: {L} tokens", flush=True)
-                assert_close(got_ol[b:b + 1], ref_ol, f"out_latent layer {layer} seq {b}")
-                assert np.max(np.abs(got_lse[b:b + 1] - ref_lse)) <= LSE_ATOL
-    finally:
-        del pool
-        torch.cuda.empty_cache()
+# Every sequence of every workload, paged and fused: tests/test_gpu_00_workloads.py.
 
 
 # ------------------------------------------------------------------ fused path vs the decompress definition
@@ -225,12 +158,47 @@ def test_fused_small_vs_decompressed(seed, s_q, seqlens):
     assert np.all(np.abs(lse.double().cpu().numpy()[:, :, heads] - ref_lse) <= bound)
 
 
-def test_fused_c2_sampled_heads():
-    inp = make_inputs("c2")
+# ------------------------------------------------------------------ the page stream alone (ceiling measurement)
+
+def _stream_expected(inp):
+    """Sum (mod 2^32) over every 32-token tile of every (sequence, query) unit of the 256
+    little-endian dwords of the tile's first row's latent: what mla_stream_pages must read."""
+    total = 0
+    for b in range(inp.batch):
+        L = int(inp.seqlens[b])
+        for i in range(inp.s_q):
+            n = L - inp.s_q + i + 1
+            if n <= 0:
+                continue
+            rows = oracle.gather_rows(inp.pool, inp.block_table, b, n)[::32, :512]      # first row of each tile
+            words = rows.astype(np.uint64).reshape(-1, 256, 2)
+            total += int((words[..., 0] | (words[..., 1] << np.uint64(16))).sum())
+    return total % (1 << 32)
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 3, 40])
+@pytest.mark.parametrize("seed,s_q,seqlens", [(61, 1, [1, 33, 64, 65, 300, 2500]), (62, 2, [2, 31, 32, 97, 1000])])
+def test_stream_pages_reads_every_tile_once(seed, s_q, seqlens, num_splits):
+    inp = make_custom(seed, len(seqlens), s_q, seqlens, extra_blocks=1)
+    _print_case(f"stream splits={num_splits}", inp)
     d = upload(inp)
-    out, _ = mla.decode(d["q_c"], d["q_r"], d["w_uk"], d["w_uv"], d["pool"], d["bt"], d["sl"], scale=inp.scale)
-    batches, heads = [0, 7, 15], [0, 45, 127]
-    ref, _ = oracle.decode_decompressed(inp.q_c, inp.q_r, inp.w_uk, inp.w_uv, inp.pool, inp.block_table,
-                                        inp.seqlens, 1, inp.scale, batches=batches, heads=heads)
-    got = host_f64(out)[batches][:, :, heads]
-    assert_close(got, ref, "out")
+    sums = mla.stream_pages(d["pool"], d["bt"], d["sl"], s_q=s_q, num_splits=num_splits)
+    import torch
+    torch.cuda.synchronize()
+    got = int(sums.cpu().numpy().view(np.uint32).astype(np.uint64).sum()) % (1 << 32)
+    assert got == _stream_expected(inp)
+
+
+def test_stream_pages_many_units_and_c3():
+    """Above 64 units the prefix sums come from the plan kernel; and the full batch-64 workload
+    in the benchmark's configuration."""
+    rng = np.random.default_rng(63)
+    for inp in (make_custom(64, 70, 1, [int(x) for x in rng.integers(1, 400, size=70)], extra_blocks=1),
+                make_inputs("c3")):
+        _print_case("stream", inp)
+        d = upload(inp)
+        sums = mla.stream_pages(d["pool"], d["bt"], d["sl"])
+        import torch
+        torch.cuda.synchronize()
+        got = int(sums.cpu().numpy().view(np.uint32).astype(np.uint64).sum()) % (1 << 32)
+        assert got == _stream_expected(inp)
