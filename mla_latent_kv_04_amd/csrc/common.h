@@ -81,8 +81,13 @@ __device__ __forceinline__ s16x8 lds_read_b128_at(uint32_t addr) {
 }
 
 // Fewest 32-token tiles a decode workgroup takes when the caller lets the library size
-// the split (num_splits = 0); an explicit num_splits splits the tiles evenly.
-constexpr int kAutoMinChunk = 1;
+// the split (num_splits = 0); an explicit num_splits splits the tiles evenly.  A
+// workgroup pays a fixed cost per range (its queries, its partial output and that
+// partial's merge) that only a few tiles amortise: measured on MI355X at batch 1 and
+// 2048 tokens (64 tiles), decode plus merge takes 30 us with 4 tiles per workgroup
+// (16 workgroups), 32 us with 2 and 39-40 us with 1; larger workloads, whose even split
+// already gives 8 or more tiles per compute unit, are unaffected.
+constexpr int kAutoMinChunk = 4;
 
 // Host-side launch helpers (defined in the kernel translation units).
 struct DecodePlanView {

@@ -58,6 +58,7 @@ struct DecodeArgs {
   uint16_t* part_o;    // [2W, 128, 512] bf16 normalised partial outputs
   float* part_lse;
   int64_t num_pages;
+  int last_page;     // min(num_pages, 2^31) - 1: page ids are int32, so clamps stay 32-bit
   int batch, s_q, max_blocks;
   int min_chunk;     // fewest tiles a workgroup takes (see split_chunk)
   float scale_log2;  // scale * log2(e)
@@ -418,8 +419,7 @@ void decode_kernel(DecodeArgs a) {
     // row 0 is a visible token, so they never fetch a row past the sequence.
     auto tile_half = [&](int k) -> int { return k < n_tiles ? ((t0 + k) & 1) : 0; };
     auto tile_src = [&](int k) -> const unsigned char* {
-      int64_t phys = ld_uniform(a.bt, bt_row + ((t0 + k) >> 1));
-      phys = phys < 0 ? 0 : (phys >= a.num_pages ? a.num_pages - 1 : phys);
+      const int64_t phys = min(max(ld_uniform(a.bt, bt_row + ((t0 + k) >> 1)), 0), a.last_page);
       if constexpr (kF8) return a.kv8 + phys * (int64_t)kF8PageBytes + tile_half(k) * kF8TileBytes;
       else return (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + tile_half(k) * kTileBytes;
     };
@@ -578,7 +578,7 @@ void decode_kernel(DecodeArgs a) {
         // per-lane source offsets are kernel constants: only bases change
         if (part != 0) return;
         const int32_t r = __builtin_amdgcn_readfirstlane(raw);
-        const int64_t phys = r < 0 ? 0 : (r >= a.num_pages ? a.num_pages - 1 : r);
+        const int64_t phys = min(max(r, 0), a.last_page);
         dsrc = a.kv8 + phys * (int64_t)kF8PageBytes + tile_half(kn) * kF8TileBytes;
         m0n = lbase + slot_off(kn) + kRopeRegion + 1024 * wave_u;
         m0c = lbase + kF8StageOff + (kn & 1) * kF8Stage + 4096 * wave_u;
@@ -589,7 +589,7 @@ void decode_kernel(DecodeArgs a) {
       const int valid = tile_valid(kn);
       if (part == 0) {
         const int32_t r = __builtin_amdgcn_readfirstlane(raw);   // uniform: keeps the base in SGPRs
-        const int64_t phys = r < 0 ? 0 : (r >= a.num_pages ? a.num_pages - 1 : r);
+        const int64_t phys = min(max(r, 0), a.last_page);
         dsrc = (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + tile_half(kn) * kTileBytes;
         m0n = lbase + (kn & 3) * kTileBytes + kRopeRegion + 1024 * wave_u;
         // rows at or past `valid` fetch the RoPE chunk of row 0 instead
@@ -642,6 +642,8 @@ void decode_kernel(DecodeArgs a) {
       // register is refilled only after the MFMA reading it has issued (its A read is
       // at issue, the LDS return much later); the trailing 14 wait states exceed the 12
       // an 8-pass XDL result needs before a VALU or memory read.
+      // The M0 steps of those loads are scalar adds, which write SCC: the blocks that
+      // issue loads name SCC as clobbered, so no compare result is kept in it across them.
       // Except in a segment's last step the block also issues the 9 direct loads of
       // tile k+2, one after every fourth MFMA (RoPE rows first, M0 stepping through
       // the LDS rows), so their issue overlaps the MFMAs, and the scalar load of the
@@ -715,7 +717,7 @@ void decode_kernel(DecodeArgs a) {
                     [a0] "v"(aq[0]), [a1] "v"(aq[1]), [a2] "v"(aq[2]), [a3] "v"(aq[3]), [a4] "v"(aq[4]), [a5] "v"(aq[5]), [a6] "v"(aq[6]), [a7] "v"(aq[7]),
                     [r0] "v"(ar[0]), [r1] "v"(ar[1]), [r2] "v"(ar[2]), [r3] "v"(ar[3]),
                     [src] "s"(dsrc), [btp] "s"(btp), [bto] "s"(bto), [vr] "v"(f8r), [vc] "v"(f8c), [vs] "v"(f8s), [mc] "s"(m0c), [ms] "s"(m0s)
-                  : "memory");
+                  : "memory", "scc");
           } else {
             asm volatile(
                   "s_nop 1\n\t"
@@ -771,7 +773,7 @@ void decode_kernel(DecodeArgs a) {
                     [a0] "v"(aq[0]), [a1] "v"(aq[1]), [a2] "v"(aq[2]), [a3] "v"(aq[3]), [a4] "v"(aq[4]), [a5] "v"(aq[5]), [a6] "v"(aq[6]), [a7] "v"(aq[7]),
                     [r0] "v"(ar[0]), [r1] "v"(ar[1]), [r2] "v"(ar[2]), [r3] "v"(ar[3]),
                     [src] "s"(dsrc), [btp] "s"(btp), [bto] "s"(bto), [d0] "v"(dv[0]), [d1] "v"(dv[1]), [d2] "v"(dv[2]), [d3] "v"(dv[3]), [d4] "v"(dv[4]), [d5] "v"(dv[5]), [d6] "v"(dv[6]), [d7] "v"(dv[7]), [d8] "v"(dv[8])
-                  : "memory");
+                  : "memory", "scc");
           }
           bt_pref = bt_next;
         } else {
@@ -981,12 +983,12 @@ void decode_kernel(DecodeArgs a) {
       // free once every wave is past this barrier; slot 0 holds the scratch.
       __syncthreads();
       int* flags = (int*)lds;
-      float* lsum = (float*)(lds + 256);
+      float* lsum = (float*)(lds + 256);   // 1 / (softmax denominator) of each head
       const bool any_over = __builtin_amdgcn_ballot_w64(m_seen > m_ref + kHeadroom) != 0;
       const float l_head = l_part + __shfl_xor(l_part, 32, 64);
       const float m_all = fmaxf(m_seen, __shfl_xor(m_seen, 32, 64));
       if (lane == 0) flags[wave_u] = any_over ? 1 : 0;
-      if (hi == 0) lsum[head] = l_head;
+      if (hi == 0) lsum[head] = 1.f / l_head;   // one division per head, shared by the four waves
       __syncthreads();
       const bool again = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
       m_redo = m_all;         // the segment's true maximum: no score exceeds it on a redo
@@ -1012,7 +1014,7 @@ void decode_kernel(DecodeArgs a) {
         for (int hb = 0; hb < 4; ++hb) {
           f32x16 il;
 #pragma unroll
-          for (int j = 0; j < 16; ++j) il[j] = 1.f / lrow[32 * hb + 8 * (j >> 2) + (j & 3)];
+          for (int j = 0; j < 16; ++j) il[j] = lrow[32 * hb + 8 * (j >> 2) + (j & 3)];
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const f32x16 v = o[hb][c] * il;
@@ -1088,8 +1090,7 @@ void stream_kernel(DecodeArgs a, uint32_t* __restrict__ sums) {
       const int n_vis = clamp_len(ld_uniform(a.seqlens, b), a.max_blocks) - a.s_q + (u - b * a.s_q) + 1;
       const int64_t bt_row = (int64_t)b * a.max_blocks;
       auto issue = [&](int k) {
-        int64_t phys = ld_uniform(a.bt, bt_row + ((t0 + k) >> 1));
-        phys = phys < 0 ? 0 : (phys >= a.num_pages ? a.num_pages - 1 : phys);
+        const int64_t phys = min(max(ld_uniform(a.bt, bt_row + ((t0 + k) >> 1)), 0), a.last_page);
         const unsigned char* src = (const unsigned char*)a.kv + phys * (int64_t)kPageBytes + ((t0 + k) & 1) * kTileBytes;
         issue_tile(src, lbase + (k & 3) * kTileBytes, ldo, wave_u, lane, min(kTile, n_vis - (t0 + k) * kTile));
       };
@@ -1117,9 +1118,14 @@ void stream_kernel(DecodeArgs a, uint32_t* __restrict__ sums) {
 // eight, lane l covering columns 4((l & 31) + 32v) .. +3 (v = 0..3) of head
 // 2w + l/32, so each load instruction reads two contiguous 512-byte runs.  Units
 // finished in place are skipped; units without visible tokens get zeros and
-// lse = -inf; split units merge their fragments in increasing workgroup order
-// with a running maximum, loading fragment f+1 while merging fragment f.
+// lse = -inf.  A split unit's fragments are merged in two passes: the lse of
+// every fragment first (one fragment per lane of the head's half-wave), giving
+// the largest lse m and each fragment's weight 2^(lse_f - m); then the partial
+// outputs in batches of kCombineBatch fragments whose loads are all in flight
+// together, accumulated in increasing fragment order (a fixed order: results do
+// not depend on timing), and divided by the sum of the weights at the end.
 constexpr int kCombineHeads = 8;
+constexpr int kCombineBatch = 8;
 
 __device__ __forceinline__ int fragment_slot(int gg, int g0, int chunk, int ubeg) {
   // The first fragment is its workgroup's second segment unless the unit starts
@@ -1133,64 +1139,75 @@ void combine_kernel(DecodeArgs a, int W) {
   const int U = a.batch * a.s_q;
   const int total = ld_uniform(a.cum, U);
   const int ubeg = ld_uniform(a.cum, u), uend = ld_uniform(a.cum, u + 1);
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31;
   const int head = blockIdx.y * kCombineHeads + 2 * (tid >> 6) + (lane >> 5);
-  const int col = 4 * (lane & 31);   // + 128 v
+  const int col = 4 * l32;   // + 128 v
   uint16_t* dst = a.out_latent + ((size_t)u * kHeads + head) * kLatent + col;
   if (uend <= ubeg) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) *(u32x2*)(dst + 128 * v) = u32x2{0u, 0u};
-    if (a.lse != nullptr && (lane & 31) == 0) a.lse[(size_t)u * kHeads + head] = -INFINITY;
+    if (a.lse != nullptr && l32 == 0) a.lse[(size_t)u * kHeads + head] = -INFINITY;
     return;
   }
   const int chunk = split_chunk(total, W, a.min_chunk);
   const int g0 = ubeg / chunk, g1 = (uend - 1) / chunk;
   if (g0 == g1) return;
+  const int F = g1 - g0 + 1;   // fragments of the unit, in workgroup order
 
-  auto load = [&](int gg, u32x2 (&x)[4], float& l) {
-    const int slot = fragment_slot(gg, g0, chunk, ubeg);
-    const uint16_t* src = a.part_o + ((size_t)slot * kHeads + head) * kLatent + col;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) x[v] = __builtin_nontemporal_load((const u32x2*)(src + 128 * v));
-    l = a.part_lse[(size_t)slot * kHeads + head];
+  // Pass 1: lse of fragment f is read by lane f % 32 of the head's half-wave.
+  auto frag_lse = [&](int f) {
+    return f < F ? a.part_lse[(size_t)fragment_slot(g0 + f, g0, chunk, ubeg) * kHeads + head] : -INFINITY;
   };
+  float m = -INFINITY;
+  for (int f0 = 0; f0 < F; f0 += 32) m = fmaxf(m, frag_lse(f0 + l32));
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 32));
+  float wsum = 0.f;
+  for (int f0 = 0; f0 < F; f0 += 32) {
+    const float l = frag_lse(f0 + l32);
+    wsum += f0 + l32 < F ? exp2f(l - m) : 0.f;
+  }
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off, 32);
+
+  // Pass 2: the partial outputs, kCombineBatch fragments in flight at a time.
   auto widen = [](const u32x2& x) {
     return f32x4{bf2f((uint16_t)(x[0] & 0xFFFFu)), bf2f((uint16_t)(x[0] >> 16)), bf2f((uint16_t)(x[1] & 0xFFFFu)),
                  bf2f((uint16_t)(x[1] >> 16))};
   };
   f32x4 acc[4];
-  u32x2 a0[4], fa[4], fb[4];
-  float m, la, lb;
-  load(g0, a0, m);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) acc[v] = widen(a0[v]);
-  float wsum = 1.f;
-  auto merge = [&](const u32x2 (&x)[4], float l) {
-    // rescale the running sum to the new maximum (base 2), add fragment x
-    const float mn = fmaxf(m, l);
-    const float s_old = exp2f(m - mn), s_new = exp2f(l - mn);
-    wsum = wsum * s_old + s_new;
+  for (int v = 0; v < 4; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float wl = 0.f;   // weight of fragment f0 + l32 (this lane's), shared through the half-wave
+  for (int f0 = 0; f0 < F; f0 += kCombineBatch) {
+    if ((f0 & 31) == 0) {
+      const float l = frag_lse(f0 + l32);
+      wl = f0 + l32 < F ? exp2f(l - m) : 0.f;
+    }
+    u32x2 x[kCombineBatch][4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = acc[v] * s_old + widen(x[v]) * s_new;
-    m = mn;
-  };
-  // two register buffers: the load of fragment gg+1 is in flight while gg merges
-  int gg = g0 + 1;
-  load(gg, fb, lb);
-  while (true) {
-    if (gg + 1 <= g1) load(gg + 1, fa, la);
-    merge(fb, lb);
-    if (++gg > g1) break;
-    if (gg + 1 <= g1) load(gg + 1, fb, lb);
-    merge(fa, la);
-    if (++gg > g1) break;
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const int f = f0 + j < F ? f0 + j : F - 1;   // past the end: a valid fragment, weight 0
+      const uint16_t* src =
+          a.part_o + ((size_t)fragment_slot(g0 + f, g0, chunk, ubeg) * kHeads + head) * kLatent + col;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) x[j][v] = __builtin_nontemporal_load((const u32x2*)(src + 128 * v));
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const float w = __shfl(wl, ((f0 + j) & 31) + (lane & 32), 64);
+      if (f0 + j < F) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] += widen(x[j][v]) * w;
+      }
+    }
   }
   const float inv = 1.f / wsum;
 #pragma unroll
   for (int v = 0; v < 4; ++v)
     *(u32x2*)(dst + 128 * v) = u32x2{pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv),
                                      pack_bf16x2(acc[v][2] * inv, acc[v][3] * inv)};
-  if (a.lse != nullptr && (lane & 31) == 0) a.lse[(size_t)u * kHeads + head] = (m + __log2f(wsum)) * kLn2;
+  if (a.lse != nullptr && l32 == 0) a.lse[(size_t)u * kHeads + head] = (m + __log2f(wsum)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------- gather (test export)
@@ -1225,6 +1242,7 @@ hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint1
   a.q_abs = q_abs; a.q_r = q_r; a.kv = kv; a.kv8 = kv8; a.bt = bt; a.seqlens = seqlens;
   a.out_latent = out_latent; a.lse = lse; a.cum = plan.cum; a.part_o = plan.part_o; a.part_lse = plan.part_lse;
   a.num_pages = num_pages; a.batch = batch; a.s_q = s_q; a.max_blocks = max_blocks;
+  a.last_page = (int)((num_pages < ((int64_t)1 << 31) ? num_pages : ((int64_t)1 << 31)) - 1);
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = hipSuccess;
   if (decode_launches_plan(batch * s_q)) {
@@ -1254,6 +1272,7 @@ hipError_t launch_stream(const uint16_t* kv, const int32_t* bt, const int32_t* s
   a.min_chunk = min_chunk;
   a.kv = kv; a.bt = bt; a.seqlens = seqlens; a.cum = cum;
   a.num_pages = num_pages; a.batch = batch; a.s_q = s_q; a.max_blocks = max_blocks;
+  a.last_page = (int)((num_pages < ((int64_t)1 << 31) ? num_pages : ((int64_t)1 << 31)) - 1);
   if (decode_launches_plan(batch * s_q)) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a, cum);
     const hipError_t e = hipGetLastError();

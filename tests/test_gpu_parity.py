@@ -125,6 +125,28 @@ def test_decode_paged_around_the_in_kernel_plan_limit(batch, s_q, num_splits):
     assert_close(host_f64(ol), ref_ol, "out_latent")
     assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= LSE_ATOL
 
+@pytest.mark.parametrize("tiles_per_split", [1, 2, 3])
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_decode_short_fragments_with_partial_tiles(tiles_per_split, s_q):
+    """Split plans whose ranges hold only 1, 2 or 3 tiles of 32 tokens, over lengths around tile
+    and page borders (a sequence's last tile often holds a single token): every fragment is
+    then a first step, a last step or both, so an error in either cannot be diluted by the
+    steady steps of a long range."""
+    seqlens = [2, 31, 32, 33, 63, 64, 65, 95, 96, 97, 129, 200]
+    inp = make_custom(70 + tiles_per_split + 3 * s_q, len(seqlens), s_q, seqlens, extra_blocks=1)
+    tiles = sum(-(-(L - s_q + i + 1) // 32) for L in seqlens for i in range(s_q))
+    num_splits = -(-tiles // tiles_per_split)
+    _print_case(f"short fragments splits={num_splits}", inp)
+    d = upload(inp)
+    qa = absorbed_inputs(inp)
+    ol, lse = _paged(inp, d, qa, num_splits)
+    ref_ol, ref_lse = oracle.decode_absorbed(qa, inp.q_r, inp.pool, inp.block_table, inp.seqlens, s_q, inp.scale)
+    got = host_f64(ol)
+    for b in range(inp.batch):
+        assert_close(got[b:b + 1], ref_ol[b:b + 1], f"out_latent seq {b} (L={seqlens[b]})")
+    assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= LSE_ATOL
+
+
 # ------------------------------------------------------------------ the five workloads
 # Every sequence of every workload, paged and fused: tests/test_gpu_00_workloads.py.
 
