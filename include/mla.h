@@ -352,6 +352,21 @@ mla_status mla_profile_collect_append(double* ms, int32_t* calls);
  * ms[1] = attention kernel. */
 mla_status mla_profile_collect_prefill(double* ms, int32_t* calls);
 
+/* mla_decode_paged without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments (less the workspace), kernels and results as
+ * mla_decode_paged on the same parameters; the workspace is a device array built
+ * into the library, one copy per device, looked up on the first call on each device
+ * and held until the process ends: 68 MiB, enough for at most 256 split-KV
+ * workgroups (num_splits, or the device's compute units when 0) and 65 536
+ * (sequence, query) units.  Larger parameters return MLA_ERR_UNSUPPORTED.  Allocates
+ * nothing.  All calls on one device share that device's array: calls that may overlap
+ * on one device (different streams, different threads) race and must be ordered by
+ * the caller.  bf16 cache only. */
+mla_status mla_decode_paged_noalloc(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv_blocks,
+                                    const int32_t* block_table, const int32_t* seqlens, uint16_t* out_latent,
+                                    float* lse, const mla_decode_params* p, void* stream);
+
 /* Decode workgroups (split-KV ranges) that mla_decode_paged, mla_decode and
  * mla_stream_pages launch for these parameters: p->num_splits when > 0, else the
  * current device's compute-unit count (a HIP call).  0 when p is invalid. */

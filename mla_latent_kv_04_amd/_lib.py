@@ -42,6 +42,7 @@ EXPORTS = (
     "mla_decode_paged_mxfp8",
     "mla_decode_mxfp8",
     "mla_append_kv_mxfp8",
+    "mla_decode_paged_noalloc",
     "mla_decode_num_workgroups",
     "mla_stream_pages",
     "mla_status_string",
@@ -149,6 +150,7 @@ def load() -> ctypes.CDLL:
         "mla_decode_paged_mxfp8": ([vp, vp, vp, vp, vp, vp, vp, pp, vp, sz, vp], ctypes.c_int),
         "mla_decode_mxfp8": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, sz, vp], ctypes.c_int),
         "mla_append_kv_mxfp8": ([vp, vp, vp, vp, vp, vp, vp, ap, vp, sz, vp], ctypes.c_int),
+        "mla_decode_paged_noalloc": ([vp, vp, vp, vp, vp, vp, vp, pp, vp], ctypes.c_int),
         "mla_decode_num_workgroups": ([pp], i32),
         "mla_stream_pages": ([vp, vp, vp, vp, pp, vp, sz, vp], ctypes.c_int),
         "mla_status_string": ([ctypes.c_int], ctypes.c_char_p),

@@ -113,6 +113,12 @@ bool decode_launches_plan(int units);
 hipError_t launch_stream(const uint16_t* kv, const int32_t* bt, const int32_t* seqlens, uint32_t* sums, int batch,
                          int s_q, int max_blocks, int64_t num_pages, int wgs, int min_chunk, int32_t* cum,
                          hipStream_t s);
+// Size of the device array that backs the allocation-free paged decode: a workspace for
+// up to 256 split-KV workgroups (2 x 256 partial outputs of 128 x 512 bf16 = 64 MiB, their
+// lse) and up to 65 536 (sequence, query) units of prefix sums.
+constexpr size_t kNoAllocScratchBytes = (size_t)68 << 20;
+// That array's address on the current device (looked up once per device).
+hipError_t noalloc_scratch(unsigned char** ptr);
 hipError_t launch_gather(const uint16_t* kv, const int32_t* bt, const int32_t* seqlens, uint16_t* dense, int batch,
                          int max_blocks, int64_t num_pages, hipStream_t s);
 

@@ -32,6 +32,8 @@
 // tiles' codes and scales are staged per wave and dequantised to the bf16 tile
 // layout above in a ring of 3 slots (see the constants kF8*); everything from the
 // tile slot on is the bf16 kernel's.
+#include <mutex>
+
 #include "common.h"
 #include "mxfp8.h"
 
@@ -1280,6 +1282,35 @@ hipError_t launch_stream(const uint16_t* kv, const int32_t* bt, const int32_t* s
   }
   hipLaunchKernelGGL(stream_kernel, dim3(wgs), dim3(kThreads), 0, s, a, sums);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- allocation-free workspace
+
+// The split-KV workspace of the allocation-free paged decode (prefix sums, partial lse
+// and partial outputs, laid out as for a caller's workspace): a file-scope device array,
+// one copy per device the library runs on, held until the process ends.  Every call on a
+// device shares that device's copy; nothing in it needs clearing between calls (the
+// decode writes every value it reads in the same call).
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(unsigned char** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static unsigned char* dev_ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (dev_ptr[dev] == nullptr) {
+    // the device's own address of its copy; the host-side name is only a stand-in
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    dev_ptr[dev] = static_cast<unsigned char*>(p);
+  }
+  *ptr = dev_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_gather(const uint16_t* kv, const int32_t* bt, const int32_t* seqlens, uint16_t* dense, int batch,

@@ -647,6 +647,28 @@ mla_status mla_gather_kv(const uint16_t* kv_blocks, const int32_t* block_table, 
   return ok();
 }
 
+mla_status mla_decode_paged_noalloc(const uint16_t* q_abs, const uint16_t* q_r, const uint16_t* kv_blocks,
+                                    const int32_t* block_table, const int32_t* seqlens, uint16_t* out_latent,
+                                    float* lse, const mla_decode_params* p, void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (p->batch == 0) return ok();
+  int wgs = 0;
+  st = resolve_wgs(p, &wgs);
+  if (st != MLA_OK) return st;
+  const WsLayout L = layout(p, wgs, false);
+  if (L.total > mla::kNoAllocScratchBytes)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "allocation-free decode: %d workgroups and %d units need %zu bytes of workspace, above the "
+                "built-in %zu (at most 256 workgroups and 65536 sequence-query units)",
+                wgs, p->batch * p->s_q, L.total, mla::kNoAllocScratchBytes);
+  unsigned char* ws = nullptr;
+  const hipError_t e = mla::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  return decode_paged_impl(q_abs, q_r, kv_blocks, nullptr, block_table, seqlens, out_latent, lse, p, ws, L.total,
+                           stream);
+}
+
 int32_t mla_decode_num_workgroups(const mla_decode_params* p) {
   if (check_params(p) != MLA_OK) return 0;
   int wgs = 0;

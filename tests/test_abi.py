@@ -144,6 +144,20 @@ def test_fused_and_gather_argument_checks(lib):
     assert lib.mla_gather_kv(MIS, A, A, A2, ctypes.byref(p), None) == _lib.MLA_ERR_MISALIGNED
 
 
+def test_noalloc_decode_rejects_sizes_beyond_its_array(lib):
+    """The allocation-free decode's workspace is a 68 MiB array in the library: more than
+    256 workgroups, or too many (sequence, query) units, is refused before any HIP call."""
+    def call(p):
+        return lib.mla_decode_paged_noalloc(A, A, A, A, A, A, None, ctypes.byref(p), None)
+    assert call(_params(num_splits=300)) == _lib.MLA_ERR_UNSUPPORTED
+    assert "256 workgroups" in lib.mla_last_error().decode()
+    assert call(_params(batch=1 << 16, s_q=256, max_blocks_per_seq=2, num_splits=256)) == _lib.MLA_ERR_UNSUPPORTED
+    assert call(_params(page_size=16)) == _lib.MLA_ERR_UNSUPPORTED
+    assert call(_params(batch=-1)) == _lib.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_paged_noalloc(A, A, A, A, A, A, None, None, None) == _lib.MLA_ERR_INVALID_ARG
+    assert call(_params(batch=0)) == _lib.MLA_OK
+
+
 def test_stream_and_workgroup_count_argument_checks(lib):
     p = _params()
     assert lib.mla_decode_num_workgroups(ctypes.byref(p)) == p.num_splits
