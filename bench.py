@@ -20,6 +20,7 @@ for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
 
 import argparse  # noqa: E402
 import json  # noqa: E402
+import math  # noqa: E402
 import sys  # noqa: E402
 import time  # noqa: E402
 
@@ -116,6 +117,48 @@ def _flusher(torch):
         wbuf.fill_(state["i"] & 0xFF)
         torch.amax(rbuf)
     return flush
+
+
+REDO_SLOPE = 0.25   # k_R[t][0] = REDO_SLOPE * t in the redo leg
+
+
+def run_redo(inp, pool_dev, torch, mla, steps, warmup, normal_ms):
+    """The batch-64 step with scores that rise along every sequence: q_abs = 0, q_R = e_0 for
+    every head, and the first RoPE component of token t's row set to REDO_SLOPE * t, so the score
+    of token t is scale * REDO_SLOPE * t.  A decode range re-runs once with its true maximum when a
+    later score leaves the first tile's maximum more than 64 log2 units behind; here that happens
+    in every range spanning more than 64 ln 2 / (scale * REDO_SLOPE) tokens.  Reports the step time
+    against the normal step's."""
+    n_seq = inp.batch
+    pages = np.full(int(pool_dev.shape[0]), -1, dtype=np.int64)
+    ramp = np.zeros((int(pool_dev.shape[0]), 64), dtype=np.float32)
+    for b in range(n_seq):
+        n = (int(inp.seqlens[b]) + 63) // 64
+        for j in range(n):
+            ramp[inp.block_table[b, j]] = REDO_SLOPE * (64 * j + np.arange(64))
+    pool2 = pool_dev.clone()
+    pool2[:, :, 512] = torch.from_numpy(ramp).cuda().to(torch.bfloat16)
+    del pages
+    q_abs = torch.zeros((n_seq, 1, 128, 512), dtype=torch.bfloat16, device="cuda")
+    q_r = torch.zeros((n_seq, 1, 128, 64), dtype=torch.bfloat16, device="cuda")
+    q_r[..., 0] = 1.0
+    sl, bt = _dev_i32(inp.seqlens, torch), _dev_i32(inp.block_table, torch)
+    out = torch.empty(n_seq, 1, 128, 512, dtype=torch.bfloat16, device="cuda")
+    params = mla.make_params(n_seq, 1, inp.max_blocks, int(pool2.shape[0]), inp.scale)
+    ws = torch.empty(mla.workspace_size(params), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        mla.decode_paged(q_abs, q_r, pool2, bt, sl, scale=inp.scale, out_latent=out, want_lse=False, workspace=ws)
+    ms, per, dist = _time_calls(step, steps, warmup, torch, mla)
+    del pool2
+    torch.cuda.empty_cache()
+    span = 64 * math.log(2) / (inp.scale * REDO_SLOPE)
+    return {"workload": "the batch-64 step with scores rising along every sequence (q_abs = 0, q_R = e_0, "
+                        f"k_R[t][0] = {REDO_SLOPE} t): every decode range longer than {span:.0f} tokens is redone "
+                        "once with its true maximum",
+            "us_per_step": round(ms * 1e3, 2), "timing_us": dist,
+            "kernels_us": {k: round(v * 1e3, 2) for k, v in per.items()},
+            "step_time_vs_normal": round(ms / normal_ms, 4)}
 
 
 def run_stream(inp, pool_dev, torch, mla, steps, warmup):
@@ -244,6 +287,31 @@ def other_row(oi, orr, layers):
                            "frac": round(gb / HBM_PEAK_GBS, 4), "kernel": "decode_kernel",
                            "algorithmic_bytes_per_launch": orr["cache_bytes"]}
     return row
+
+
+def mxfp8_row(inp, pool, torch, mla, steps, warmup, ms):
+    """The graded workload over its MXFP8 cache: step time, kernels, roofline on 656-byte rows."""
+    f8 = run_mxfp8(inp, pool, torch, mla, steps, warmup)
+    f8_dec = f8["per"]["decode"]
+    f8_ach = f8["cache_bytes"] / (f8_dec * 1e-3) / 1e9
+    traffic8 = load_traffic("mxfp8")
+    mx = {
+        "workload": "the batch-64 workload above, cache in MXFP8 (E4M3 codes, one E8M0 scale per 32 latent "
+                    "values, bf16 k_R: 656 B per token)",
+        "us_per_step": round(f8["ms"] * 1e3, 2),
+        "timing_us": f8["dist"],
+        "kernels_us": {k: round(v * 1e3, 2) for k, v in f8["per"].items()},
+        "cache_bytes_per_step": f8["cache_bytes"],
+        "cache_GBps": round(f8["cache_bytes"] / (f8["ms"] * 1e-3) / 1e9, 1),
+        "kv_tokens_per_s": round(f8["tokens"] / (f8["ms"] * 1e-3), 1),
+        "step_speedup_vs_bf16_cache": round(ms / f8["ms"], 4),
+        "roofline": {"bound": "hbm", "achieved": round(f8_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(f8_ach / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic8 is None else round(traffic8["fetch"] + traffic8["write"]),
+                     "traffic_split": traffic8, "kernel": "decode_kernel (MXFP8 variant)",
+                     "algorithmic_bytes_per_launch": f8["cache_bytes"]},
+    }
+    return mx
 
 
 def run_paged(inp, pool_dev, torch, mla, steps, warmup, layers=1, pages_per_layer=None, flush=None):
@@ -517,9 +585,17 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill chunk leg")
+    ap.add_argument("--no-redo", action="store_true", help="skip the softmax-redo leg")
+    ap.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8-cache leg")
+    ap.add_argument("--no-append", action="store_true", help="skip the cache-append leg")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_NAME"),
+                    help="write a kernel-trace summary (rocprofv3 --kernel-trace --stats csv folder) to profiles/")
+    ap.add_argument("--trace-title", default="", help="title line of --summarize-trace")
     ap.add_argument("--pmc-run", nargs="?", const="decode", default=None, choices=sorted(TRAFFIC),
                     help="only run launches of one kernel family (default decode) and the calibration copy "
                          "(target of rocprofv3 --pmc passes)")
+    ap.add_argument("--settle", type=float, default=0.0,
+                    help="with --pmc-run: seconds of untimed calls after the warm-up, before the counted ones")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from the FETCH_SIZE and WRITE_SIZE pass output folders")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
@@ -535,13 +611,16 @@ def main():
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.pmc_command)
         return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.pmc_command, args.trace_title)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(sequences shard across GPUs without exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
 
     if args.pmc_run:
-        pmc_run(args.steps, args.warmup, args.pmc_run)
+        pmc_run(args.steps, args.warmup, args.pmc_run, args.settle)
         return
 
     import torch
@@ -579,28 +658,17 @@ def main():
     log(f"[bench] c3 fused: {fms * 1e3:.1f} us/step; kernels us: "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in fper.items()))
 
+    # ---- the redo path of the fixed-reference softmax, made to fire in every long range
+    redo = None
+    if not args.no_redo:
+        redo = run_redo(inp, pool, torch, mla, args.steps, args.warmup, ms)
+        log(f"[bench] c3 redo: {redo}")
+
     # ---- the same workload over its MXFP8 cache
-    f8 = run_mxfp8(inp, pool, torch, mla, args.steps, args.warmup)
-    f8_dec = f8["per"]["decode"]
-    f8_ach = f8["cache_bytes"] / (f8_dec * 1e-3) / 1e9
-    traffic8 = load_traffic("mxfp8")
-    mx = {
-        "workload": "the batch-64 workload above, cache in MXFP8 (E4M3 codes, one E8M0 scale per 32 latent "
-                    "values, bf16 k_R: 656 B per token)",
-        "us_per_step": round(f8["ms"] * 1e3, 2),
-        "timing_us": f8["dist"],
-        "kernels_us": {k: round(v * 1e3, 2) for k, v in f8["per"].items()},
-        "cache_bytes_per_step": f8["cache_bytes"],
-        "cache_GBps": round(f8["cache_bytes"] / (f8["ms"] * 1e-3) / 1e9, 1),
-        "kv_tokens_per_s": round(f8["tokens"] / (f8["ms"] * 1e-3), 1),
-        "step_speedup_vs_bf16_cache": round(ms / f8["ms"], 4),
-        "roofline": {"bound": "hbm", "achieved": round(f8_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(f8_ach / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic8 is None else round(traffic8["fetch"] + traffic8["write"]),
-                     "traffic_split": traffic8, "kernel": "decode_kernel (MXFP8 variant)",
-                     "algorithmic_bytes_per_launch": f8["cache_bytes"]},
-    }
-    log(f"[bench] c3 mxfp8: {mx}")
+    mx = None
+    if not args.no_mxfp8:
+        mx = mxfp8_row(inp, pool, torch, mla, args.steps, args.warmup, ms)
+        log(f"[bench] c3 mxfp8: {mx}")
 
     # ---- other workloads (timing only; parity is in the tests)
     others = {}
@@ -618,8 +686,10 @@ def main():
 
     # ---- cache append of the same step's new tokens (timed after the decodes: it writes
     # one row per sequence into the pool)
-    app = run_append(inp, pool, torch, mla, args.steps, args.warmup)
-    log(f"[bench] c3 append: {app}")
+    app = None
+    if not args.no_append:
+        app = run_append(inp, pool, torch, mla, args.steps, args.warmup)
+        log(f"[bench] c3 append: {app}")
 
     pre = None
     if not args.no_prefill:
@@ -669,6 +739,7 @@ def main():
                      "measured_stream_ceiling_GBps": stream["GBps_median"],
                      "frac_of_measured_stream_ceiling": round(achieved / stream["GBps_median"], 4)},
         "stream_ceiling": stream,
+        "softmax_redo": redo,
         "cpu_baseline": cpu,
         "other_workloads": others,
         "cache_append": app,
@@ -716,7 +787,7 @@ def _copy_for_calibration(torch):
     torch.cuda.synchronize()
 
 
-def pmc_run(steps, warmup, kind="decode"):
+def pmc_run(steps, warmup, kind="decode", settle=0.0):
     """Workload for the rocprofv3 --pmc passes: `warmup + steps` launches of one kernel
     family (decode: the batch-64 paged decode; append: the 64-token cache append;
     prefill: the 8 x 4096-token prompt), then one device copy of COPY_BYTES bytes whose
@@ -766,6 +837,13 @@ def pmc_run(steps, warmup, kind="decode"):
         raise SystemExit(f"unknown --pmc-run kind {kind!r}")
     for _ in range(warmup):
         call()
+    # keep calling until the clock has settled under the power cap (the timed legs of the
+    # report do the same before they time anything)
+    t_end = time.perf_counter() + settle
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
     # marks the start of the steady launches (a power or clock sampler waits for it)
     log(f"[bench] pmc run ({kind}): warm-up done, {steps} calls follow")
@@ -856,6 +934,38 @@ def summarize_counters(run_dirs, command, kernel="decode_kernel"):
         lines += ["", f"MFMA busy share of the launch's cycles: {busy:.3f}."]
     lines += ["", f"source_sha256: {kernel_source_hash('decode')}", ""]
     path = os.path.join(ROOT, "profiles", COUNTER_FILE)
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    log(f"[bench] wrote {path}")
+
+
+def summarize_trace(trace_dir, out_name, command, title):
+    """Writes a kernel-trace summary to profiles/OUT_NAME: per kernel, the number of dispatches
+    and their duration (average, median, min, max) from a rocprofv3 --kernel-trace csv folder."""
+    import csv
+    import glob
+    import statistics
+    rows = []
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"summarize-trace: no kernel_trace.csv under {trace_dir}")
+    by = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        short = name.replace("(anonymous namespace)::", "").replace("void ", "").replace("mla::", "").split("(")[0]
+        by.setdefault(short, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    total = sum(sum(v) for v in by.values())
+    lines = [f"# Kernel trace: {title}", "", "Command (run from /tmp; `<repo>` is the repository root):", "", "```",
+             *command, "```", "",
+             "| kernel | dispatches | avg us | median us | min us | max us | share of traced kernel time |",
+             "|---|---|---|---|---|---|---|"]
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {k} | {len(v)} | {statistics.mean(v):.1f} | {statistics.median(v):.1f} | {min(v):.1f} | "
+                     f"{max(v):.1f} | {sum(v) / total:.1%} |")
+    lines += ["", f"source_sha256 (decode sources): {kernel_source_hash('decode')}", ""]
+    path = os.path.join(ROOT, "profiles", out_name)
     with open(path, "w") as f:
         f.write("\n".join(lines))
     log(f"[bench] wrote {path}")

@@ -72,6 +72,11 @@ __device__ __forceinline__ s16x4 lds_read_tr4(const void* lds_byte_ptr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(lds_byte_ptr));
 }
 
+// 32-bit LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(MLA_LDS const void*)p;
+}
+
 // The same reads at a 32-bit LDS byte address.
 __device__ __forceinline__ s16x4 lds_read_tr4_at(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS s16x4*)(uintptr_t)addr);

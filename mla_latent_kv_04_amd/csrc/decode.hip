@@ -202,10 +202,6 @@ __device__ __forceinline__ void dma_b32(const unsigned char* sbase, uint32_t vof
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds));
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(MLA_LDS const void*)p;
-}
-
 // The 9 direct loads of one tile.  Rows at or past `valid` (only in a
 // sequence's last tile) are fetched from row 0 of the tile instead: they are
 // masked out of the softmax, and loading finite data keeps 0 * V finite even

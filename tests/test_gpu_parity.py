@@ -60,7 +60,7 @@ def test_gather_bit_exact(seqlens):
 
 # ------------------------------------------------------------------ projections
 
-@pytest.mark.parametrize("tokens", [1, 17, 64, 130])
+@pytest.mark.parametrize("tokens", [1, 17, 64, 65, 130, 192])
 def test_absorb_q(tokens):
     inp = make_custom(22, tokens, 1, [1] * tokens)
     d = upload(inp)
@@ -71,7 +71,7 @@ def test_absorb_q(tokens):
     assert np.max(np.abs(got - ref) / (np.abs(ref) + 1e-3)) < 2 ** -7
 
 
-@pytest.mark.parametrize("tokens", [1, 17, 64, 130])
+@pytest.mark.parametrize("tokens", [1, 17, 64, 65, 130, 192])
 def test_up_proj(tokens):
     inp = make_custom(23, tokens, 1, [1] * tokens)
     rng = np.random.default_rng(5)
