@@ -181,6 +181,29 @@ def run_stream(inp, pool_dev, torch, mla, steps, warmup):
             "frac_of_peak": round(cache_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def run_cache_resident(inp, pool_dev, torch, mla, steps, warmup, decode_ms):
+    """The batch-64 step with every block-table entry mapped onto the first 32 pages of the
+    pool (2.25 MiB, which every die's 4 MiB L2 holds): the same sequences, lengths, split and
+    arithmetic as the real step, with the cache reads served from L2 instead of HBM.  The
+    decode kernel's time here is its time when HBM bandwidth is not the limit."""
+    bt = _dev_i32((inp.block_table.astype(np.int64) % 32).astype(np.int32), torch)
+    sl = _dev_i32(inp.seqlens, torch)
+    qa = torch.randn((inp.batch, 1, 128, 512), device="cuda").to(torch.bfloat16)
+    qr = torch.randn((inp.batch, 1, 128, 64), device="cuda").to(torch.bfloat16)
+    out = torch.empty(inp.batch, 1, 128, 512, dtype=torch.bfloat16, device="cuda")
+    params = mla.make_params(inp.batch, 1, inp.max_blocks, int(pool_dev.shape[0]), inp.scale)
+    ws = torch.empty(mla.workspace_size(params), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        mla.decode_paged(qa, qr, pool_dev, bt, sl, scale=inp.scale, out_latent=out, want_lse=False, workspace=ws)
+    ms, per, dist = _time_calls(step, steps, warmup, torch, mla)
+    return {"workload": "the batch-64 step (same lengths and split) with every page of every sequence mapped onto "
+                        "the first 32 pages of the pool (2.25 MiB, resident in each die's L2)",
+            "us_per_step": round(ms * 1e3, 2), "timing_us": dist,
+            "kernels_us": {k: round(v * 1e3, 2) for k, v in per.items()},
+            "decode_kernel_vs_hbm_resident": round(per["decode"] / decode_ms, 4)}
+
+
 def _time_calls(fn, steps, warmup, torch, mla, flush=None):
     """Warm up (`warmup` calls, and at least WARM_SECONDS of calls so that the
     engine clock has settled), then time exactly `steps` calls between two
@@ -260,6 +283,83 @@ def decode_flops(seqlens, s_q):
     return 2 * 128 * (576 + 512) * visible
 
 
+AUTO_MIN_CHUNK = 4    # fewest tiles per workgroup when the library sizes the split (num_splits = 0)
+
+
+def split_summary(seqlens, s_q, workgroups, auto):
+    """The decode's split of a workload, for the report: the 32-token tiles of all
+    (sequence, query) units laid end to end and cut into equal ranges of whole tiles, one
+    per workgroup; a unit cut by a range boundary leaves one bf16 partial output (128 heads
+    x 512) per range it meets, which the merge reads back."""
+    tiles = []
+    for L in np.asarray(seqlens, dtype=np.int64):
+        for i in range(s_q):
+            vis = max(int(L) - s_q + i + 1, 0)
+            tiles.append((vis + 31) // 32)
+    tiles = np.asarray(tiles, dtype=np.int64)
+    total = int(tiles.sum())
+    even = -(-total // workgroups)
+    chunk = max(even, AUTO_MIN_CHUNK) if auto else even
+    used = -(-total // chunk)
+    cum = np.concatenate([[0], np.cumsum(tiles)])
+    frags = 0
+    for u in range(len(tiles)):
+        if tiles[u] == 0:
+            continue
+        first, last = cum[u] // chunk, (cum[u + 1] - 1) // chunk
+        if last > first:
+            frags += int(last - first + 1)
+    part = frags * 128 * 512 * 2
+    return {"workgroups_launched": workgroups, "workgroups_with_tiles": used, "tiles": total,
+            "tiles_per_workgroup": chunk, "fragments": frags, "partial_bytes": part,
+            "partial_over_cache": round(part / (int(np.sum(seqlens)) * ROW_BYTES), 4)}
+
+
+def run_split_sweep(names, values, steps, torch, mla, command):
+    """Times the paged decode step of each named workload for each num_splits value (0 =
+    the library's own choice), warm and HBM-cold, and writes the table to profiles/."""
+    flush = _flusher(torch)
+    lines = ["# Split sizing of the paged decode: small and long-context workloads", "",
+             "Command (run from the repository root on one MI355X):", "", "```", *command, "```", "",
+             "Per workload and `num_splits` (0 = the library's choice: one workgroup per compute unit, at least "
+             f"{AUTO_MIN_CHUNK} tiles each): the split (tiles of 32 tokens per workgroup, units cut into "
+             "fragments, bytes of bf16 partial outputs written and read back by the merge, as a share of the "
+             "cache bytes), then the step time (decode + merge) median over back-to-back calls (warm) and over "
+             "calls each after a 1 GiB write and a 1 GiB read of other buffers (cold), and the two kernels' "
+             "durations from the library's per-kernel events (each includes about 2 us of event overhead).", "",
+             "| workload | num_splits | workgroups | tiles each | fragments | partials / cache | warm us | "
+             "cold us | decode us | merge us |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for name in names:
+        oi = make_inputs(name, with_pool=False)
+        pool = _device_pool(oi.num_pages, oi.seed, torch)
+        q_abs = torch.randn((oi.batch, oi.s_q, 128, 512), device="cuda").to(torch.bfloat16)
+        q_r = torch.randn((oi.batch, oi.s_q, 128, 64), device="cuda").to(torch.bfloat16)
+        sl, bt = _dev_i32(oi.seqlens, torch), _dev_i32(oi.block_table, torch)
+        out = torch.empty(oi.batch, oi.s_q, 128, 512, dtype=torch.bfloat16, device="cuda")
+        for ns in values:
+            params = mla.make_params(oi.batch, oi.s_q, oi.max_blocks, oi.num_pages, oi.scale, ns)
+            ws = torch.empty(mla.workspace_size(params), dtype=torch.uint8, device="cuda")
+            wgs = mla.decode_num_workgroups(params)
+
+            def step(i):
+                mla.decode_paged(q_abs, q_r, pool, bt, sl, scale=oi.scale, num_splits=ns, out_latent=out,
+                                 want_lse=False, workspace=ws)
+            ms, per, dist = _time_calls(step, steps, 5, torch, mla, flush)
+            sp = split_summary(oi.seqlens, oi.s_q, wgs, ns == 0)
+            lines.append(f"| {name} | {ns} | {wgs} | {sp['tiles_per_workgroup']} | {sp['fragments']} | "
+                         f"{sp['partial_over_cache']:.1%} | {dist['warm']['median']:.1f} | "
+                         f"{dist['cold']['median']:.1f} | {per.get('decode', 0) * 1e3:.1f} | "
+                         f"{per.get('combine', 0) * 1e3:.1f} |")
+            log(f"[bench] sweep {lines[-1]}")
+        del pool
+        torch.cuda.empty_cache()
+    lines += ["", f"source_sha256 (decode sources): {kernel_source_hash('decode')}", ""]
+    path = os.path.join(ROOT, "profiles", "decode_split_sweep_c1_c2_c5.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    log(f"[bench] wrote {path}")
+
+
 def other_row(oi, orr, layers):
     """Report row of a workload other than the graded one: step time (back-to-back calls),
     per-call distributions warm and cold, the decode kernel's time and its roofline -- HBM
@@ -270,7 +370,8 @@ def other_row(oi, orr, layers):
            "timing_us": orr["dist"],
            "kernels_us": {k: round(v * 1e3, 2) for k, v in orr["per"].items()},
            "batch": oi.batch, "s_q": oi.s_q, "cached_tokens": orr["tokens"],
-           "pool": "device-generated bf16 N(0,1)" + (", 60 layers, layer i%60 per call" if layers > 1 else "")}
+           "pool": "device-generated bf16 N(0,1)" + (", 60 layers, layer i%60 per call" if layers > 1 else ""),
+           "split": split_summary(oi.seqlens, oi.s_q, orr["workgroups"], True)}
     cold = orr["dist"].get("cold")
     if cold is not None:
         row["cold_cache_GBps_median"] = round(orr["cache_bytes"] / (cold["median"] * 1e-6) / 1e9, 1)
@@ -332,7 +433,8 @@ def run_paged(inp, pool_dev, torch, mla, steps, warmup, layers=1, pages_per_laye
 
     ms, per, dist = _time_calls(step, steps, warmup, torch, mla, flush)
     cache_bytes = int(inp.seqlens.astype(np.int64).sum()) * ROW_BYTES
-    return dict(ms=ms, per=per, dist=dist, cache_bytes=cache_bytes, tokens=int(inp.seqlens.sum()), queries=B * s_q)
+    return dict(ms=ms, per=per, dist=dist, cache_bytes=cache_bytes, tokens=int(inp.seqlens.sum()), queries=B * s_q,
+                workgroups=mla.decode_num_workgroups(params))
 
 
 D_MODEL = 7168                 # hidden size d of the appended tokens' states
@@ -591,15 +693,26 @@ def main():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_NAME"),
                     help="write a kernel-trace summary (rocprofv3 --kernel-trace --stats csv folder) to profiles/")
     ap.add_argument("--trace-title", default="", help="title line of --summarize-trace")
-    ap.add_argument("--pmc-run", nargs="?", const="decode", default=None, choices=sorted(TRAFFIC),
+    ap.add_argument("--pmc-run", nargs="?", const="decode", default=None, choices=sorted(set(TRAFFIC) | {"c1", "c2", "resident"}),
                     help="only run launches of one kernel family (default decode) and the calibration copy "
                          "(target of rocprofv3 --pmc passes)")
     ap.add_argument("--settle", type=float, default=0.0,
                     help="with --pmc-run: seconds of untimed calls after the warm-up, before the counted ones")
+    ap.add_argument("--flush", action="store_true",
+                    help="with --pmc-run: flush L2 and the last-level cache before every call")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from the FETCH_SIZE and WRITE_SIZE pass output folders")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                     help="write the decode kernel's cycle and instruction attribution from counter pass folders")
+    ap.add_argument("--summarize-clock", nargs="+", metavar="KIND=DIR",
+                    help="write the engine clock and MFMA occupancy summary from counter passes "
+                         "(SQ_VALU_MFMA_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY GRBM_GUI_ACTIVE) over "
+                         "--pmc-run KIND")
+    ap.add_argument("--sweep-splits", metavar="WORKLOADS",
+                    help="time the paged decode of these workloads (comma list) over --sweep-values num_splits "
+                         "and write the table to profiles/")
+    ap.add_argument("--sweep-values", default="0,16,32,64,128,256",
+                    help="num_splits values of --sweep-splits (0 = the library's choice)")
     ap.add_argument("--pmc-kind", default="decode", choices=sorted(TRAFFIC),
                     help="kernel family of --summarize-pmc")
     ap.add_argument("--pmc-command", action="append", default=[],
@@ -611,6 +724,9 @@ def main():
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.pmc_command)
         return
+    if args.summarize_clock:
+        summarize_clock([x.split("=", 1) for x in args.summarize_clock], args.pmc_command)
+        return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.pmc_command, args.trace_title)
         return
@@ -620,7 +736,15 @@ def main():
         sys.exit(2)
 
     if args.pmc_run:
-        pmc_run(args.steps, args.warmup, args.pmc_run, args.settle)
+        pmc_run(args.steps, args.warmup, args.pmc_run, args.settle, args.flush)
+        return
+    if args.sweep_splits:
+        import torch
+        import mla_latent_kv_04_amd as mla
+        cmd = [f"python3 bench.py --sweep-splits {args.sweep_splits} --sweep-values {args.sweep_values} "
+               f"--steps {args.steps}"]
+        run_split_sweep(args.sweep_splits.split(","), [int(x) for x in args.sweep_values.split(",")], args.steps,
+                        torch, mla, cmd)
         return
 
     import torch
@@ -644,6 +768,9 @@ def main():
     log(f"[bench] c3 stream ceiling: {stream}")
     log(f"[bench] c3 paged: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s; kernels us: "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in r["per"].items() if v > 0))
+
+    resident = run_cache_resident(inp, pool, torch, mla, args.steps, args.warmup, dec_ms)
+    log(f"[bench] c3 with the cache in L2: {resident}")
 
     # fused step (absorb + paged + merge + up-proj) on the same inputs
     d_qc, d_qr = _dev_bf16(inp.q_c, torch), _dev_bf16(inp.q_r, torch)
@@ -739,6 +866,7 @@ def main():
                      "measured_stream_ceiling_GBps": stream["GBps_median"],
                      "frac_of_measured_stream_ceiling": round(achieved / stream["GBps_median"], 4)},
         "stream_ceiling": stream,
+        "cache_resident": resident,
         "softmax_redo": redo,
         "cpu_baseline": cpu,
         "other_workloads": others,
@@ -787,11 +915,14 @@ def _copy_for_calibration(torch):
     torch.cuda.synchronize()
 
 
-def pmc_run(steps, warmup, kind="decode", settle=0.0):
-    """Workload for the rocprofv3 --pmc passes: `warmup + steps` launches of one kernel
-    family (decode: the batch-64 paged decode; append: the 64-token cache append;
-    prefill: the 8 x 4096-token prompt), then one device copy of COPY_BYTES bytes whose
-    counter readings calibrate the kernels'."""
+def pmc_run(steps, warmup, kind="decode", settle=0.0, flush=False):
+    """Workload for the rocprofv3 --pmc passes and kernel traces: `warmup + steps` launches
+    of one kernel family (decode: the batch-64 paged decode; c1, c2, c5: the paged decode
+    of those workloads; resident: the batch-64 decode with every page mapped onto the pool's
+    first 32 (held in L2); mxfp8: the batch-64 decode over the MXFP8 cache; append: the
+    64-token cache append; prefill: the 8 x 4096-token prompt), then one device copy of
+    COPY_BYTES bytes whose counter readings calibrate the kernels'.  settle: seconds of
+    further untimed calls after the warm-up; flush: evict the caches before every call."""
     import torch
     import mla_latent_kv_04_amd as mla
     if kind == "decode":
@@ -801,11 +932,19 @@ def pmc_run(steps, warmup, kind="decode", settle=0.0):
         qr = torch.randn((inp.batch, 1, 128, 64), device="cuda").to(torch.bfloat16)
         bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
         call = lambda: mla.decode_paged(qa, qr, pool, bt, sl, scale=inp.scale)
-    elif kind == "c5":
-        inp = _workload_from_synth("c5", torch, with_host_pool=False)
+    elif kind == "resident":
+        inp = _workload_from_synth("c3", torch, with_host_pool=False)
         pool = _device_pool(inp.num_pages, inp.seed, torch)
-        qa = torch.randn((inp.batch, 2, 128, 512), device="cuda").to(torch.bfloat16)
-        qr = torch.randn((inp.batch, 2, 128, 64), device="cuda").to(torch.bfloat16)
+        qa = torch.randn((inp.batch, 1, 128, 512), device="cuda").to(torch.bfloat16)
+        qr = torch.randn((inp.batch, 1, 128, 64), device="cuda").to(torch.bfloat16)
+        bt = _dev_i32((inp.block_table.astype(np.int64) % 32).astype(np.int32), torch)
+        sl = _dev_i32(inp.seqlens, torch)
+        call = lambda: mla.decode_paged(qa, qr, pool, bt, sl, scale=inp.scale)
+    elif kind in ("c1", "c2", "c5"):
+        inp = _workload_from_synth(kind, torch, with_host_pool=False)
+        pool = _device_pool(inp.num_pages, inp.seed, torch)
+        qa = torch.randn((inp.batch, inp.s_q, 128, 512), device="cuda").to(torch.bfloat16)
+        qr = torch.randn((inp.batch, inp.s_q, 128, 64), device="cuda").to(torch.bfloat16)
         bt, sl = _dev_i32(inp.block_table, torch), _dev_i32(inp.seqlens, torch)
         call = lambda: mla.decode_paged(qa, qr, pool, bt, sl, scale=inp.scale)
     elif kind == "mxfp8":
@@ -835,6 +974,13 @@ def pmc_run(steps, warmup, kind="decode", settle=0.0):
         call = lambda: mla.prefill(*args, scale=base.scale)
     else:
         raise SystemExit(f"unknown --pmc-run kind {kind!r}")
+    if flush:
+        # every call HBM-cold: the caches are flushed before it (the flush kernels show in a trace)
+        flusher, plain = _flusher(torch), call
+
+        def call():
+            flusher()
+            plain()
     for _ in range(warmup):
         call()
     # keep calling until the clock has settled under the power cap (the timed legs of the
@@ -854,14 +1000,25 @@ def pmc_run(steps, warmup, kind="decode", settle=0.0):
     log(f"[bench] pmc run ({kind}): {warmup + steps} calls, copy of {COPY_BYTES} B")
 
 
+def _csv_files(run_dir, kind):
+    """rocprofv3 csv outputs of one kind under a run folder, plain or gzip-compressed."""
+    import glob
+    return sorted(glob.glob(os.path.join(run_dir, "**", f"*{kind}.csv"), recursive=True)
+                  + glob.glob(os.path.join(run_dir, "**", f"*{kind}.csv.gz"), recursive=True))
+
+
+def _open_text(path):
+    import gzip
+    return gzip.open(path, "rt") if path.endswith(".gz") else open(path)
+
+
 def _pmc_per_dispatch(run_dir, counter):
     """{kernel name: [value per dispatch]} for one counter of a rocprofv3 csv run."""
     import csv
-    import glob
     import collections
     vals = collections.defaultdict(lambda: collections.defaultdict(float))
-    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
-        with open(path) as f:
+    for path in _csv_files(run_dir, "counter_collection"):
+        with _open_text(path) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] == counter:
                     vals[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
@@ -939,15 +1096,70 @@ def summarize_counters(run_dirs, command, kernel="decode_kernel"):
     log(f"[bench] wrote {path}")
 
 
+CLOCK_FILE = "mfma_busy_clock_decode_c3_prefill_b8_4096.md"
+CLOCK_KINDS = {
+    "decode": ("decode_kernel", "decode_kernel<false>: bf16 cache, batch 64 (c3)"),
+    "resident": ("decode_kernel", "decode_kernel<false>: the same step with its pages held in L2"),
+    "mxfp8": ("decode_kernel", "decode_kernel<true>: MXFP8 cache, batch 64 (c3)"),
+    "prefill": ("prefill_attention_kernel", "prefill_attention_kernel: 8 x 4096 prompt"),
+}
+
+
+def summarize_clock(kind_dirs, command):
+    """Writes the engine clock and matrix-pipe occupancy of the main kernel of each pass, per
+    launch (the first launch of a pass left out): clock = GRBM_GUI_ACTIVE / 8 dies / launch
+    duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8);
+    wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES."""
+    import csv
+    rows_out = []
+    for kind, d in kind_dirs:
+        kern, label = CLOCK_KINDS[kind]
+        per = {}
+        for path in _csv_files(d, "counter_collection"):
+            with _open_text(path) as f:
+                for r in csv.DictReader(f):
+                    if kern + "<" not in r["Kernel_Name"] and kern + "(" not in r["Kernel_Name"]:
+                        continue
+                    e = per.setdefault(int(r["Dispatch_Id"]), {"dur": (int(r["End_Timestamp"])
+                                                                      - int(r["Start_Timestamp"])) * 1e-9})
+                    e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        launches = [per[k] for k in sorted(per)][1:]
+        if not launches:
+            raise SystemExit(f"summarize-clock: no {kern} dispatches in {d}")
+        dur = [x["dur"] * 1e6 for x in launches]
+        clk = [x["GRBM_GUI_ACTIVE"] / 8 / x["dur"] / 1e9 for x in launches]
+        busy = [x["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (x["GRBM_GUI_ACTIVE"] / 8) for x in launches]
+        wait = [x["SQ_WAIT_INST_ANY"] / x["SQ_WAVE_CYCLES"] for x in launches]
+        rng = lambda v, f: f"{f.format(min(v))}–{f.format(max(v))}"
+        rows_out.append(f"| {label} | {len(launches)} | {rng(dur, '{:.0f}')} | {rng(clk, '{:.2f}')} | "
+                        f"{rng(busy, '{:.3f}')} | {rng(wait, '{:.3f}')} |")
+    lines = ["# Engine clock and MFMA occupancy per launch: decode (c3: bf16 cache, pages in L2, MXFP8 cache) "
+             "and prefill attention (8 x 4096)", "",
+             "rocprofv3 counter passes, one per kernel family, run from /tmp (`<repo>` is the repository root):", "",
+             "```", *command, "```", "",
+             "Per launch of the family's main kernel (the first launch of each pass left out): clock = "
+             "GRBM_GUI_ACTIVE / 8 dies / launch duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / "
+             "(GRBM_GUI_ACTIVE / 8) (a v_mfma_f32_32x32x16_bf16 keeps its SIMD's matrix pipe busy 32 cycles); "
+             "wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave cycles spent waiting on a dependency). Under --pmc "
+             "the launches are serialised one by one, so their durations spread more than the benchmark's.", "",
+             "| kernel | launches | duration us | clock GHz | MFMA busy | wait |", "|---|---|---|---|---|---|",
+             *rows_out, "",
+             f"source_sha256 (decode sources): {kernel_source_hash('decode')}",
+             f"source_sha256 (prefill sources): {kernel_source_hash('prefill')}", ""]
+    path = os.path.join(ROOT, "profiles", CLOCK_FILE)
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    log(f"[bench] wrote {path}")
+
+
 def summarize_trace(trace_dir, out_name, command, title):
     """Writes a kernel-trace summary to profiles/OUT_NAME: per kernel, the number of dispatches
     and their duration (average, median, min, max) from a rocprofv3 --kernel-trace csv folder."""
     import csv
-    import glob
     import statistics
     rows = []
-    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
-        with open(path) as f:
+    for path in _csv_files(trace_dir, "kernel_trace"):
+        with _open_text(path) as f:
             rows += list(csv.DictReader(f))
     if not rows:
         raise SystemExit(f"summarize-trace: no kernel_trace.csv under {trace_dir}")
