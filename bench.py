@@ -318,6 +318,7 @@ def split_summary(seqlens, s_q, workgroups, auto):
 def run_split_sweep(names, values, steps, torch, mla, command):
     """Times the paged decode step of each named workload for each num_splits value (0 =
     the library's own choice), warm and HBM-cold, and writes the table to profiles/."""
+    from synth import make_inputs
     flush = _flusher(torch)
     lines = ["# Split sizing of the paged decode: small and long-context workloads", "",
              "Command (run from the repository root on one MI355X):", "", "```", *command, "```", "",

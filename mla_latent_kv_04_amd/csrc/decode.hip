@@ -529,7 +529,11 @@ void decode_kernel(DecodeArgs a) {
       for (int ks = 0; ks < 4; ++ks) q[32 + ks] = *(const s16x8*)(qr + 16 * ks);
     }
 
-    f32x16 o[4][4];            // O[head block hb][column block c]
+    // O^T[column block c][head block hb], kept as o[hb][c]: the PV products take V^T as the A
+    // operand and P^T as B (the same registers either way), so that register j of tile (hb, c)
+    // is latent column 128w + 32c + 8(j/4) + 4hi + (j%4) of head 32hb + l32: each lane holds
+    // runs of four consecutive columns of one head.
+    f32x16 o[4][4];
     // Reference max (log2 units) of head 32w + l32: from the first tile, or the
     // segment's true maximum when the segment is being redone.
     float m_ref = redo ? m_redo : -INFINITY;
@@ -834,9 +838,10 @@ void decode_kernel(DecodeArgs a) {
 
       // ---- PV of tile k-1 (at k = 0: the zeroed P buffer 1 with the current, finite
       // tile as V, which adds exact zeros), interleaved with the softmax of tile k.
-      //   A (P), head block hb, k-step st: head 32hb + l32, tokens 16st + 8hi + 0..7
+      // O^T += V^T P^T, operands as loaded (lane l32 + 32hi):
+      //   P^T (B operand), head block hb, k-step st: head 32hb + l32, tokens 16st + 8hi + 0..7
       //     -> (pprev + offP0) XOR 32st, + 2048 hb
-      //   B (c_KV columns, transposing reads), half r, column block c: token 16st + 8hi + 4r + e,
+      //   V^T (A operand, transposing reads), half r, column block c: token 16st + 8hi + 4r + e,
       //     chunk 16w + 4c + cb, byte 8 (lane & 1) -> (vprev + offV0) XOR (64c + 16r), + 16384 st + 4096 r
       const unsigned char* vprev = lds + slot_off(k == 0 ? 0 : k - 1);
       const unsigned char* pprev = pbuf + ((k - 1) & 1) * kPBytes;
@@ -860,11 +865,15 @@ void decode_kernel(DecodeArgs a) {
       // (only in the segment's last tile) score -inf.
       float sc[16], xa[16], ex[16];
       float mx = -INFINITY;
+      // Token 8(j/4) + 4hi + (j%4) is past the end when 4hi >= valid - 8(j/4) - (j%4): the
+      // lane's 4hi (taken here, so it is not hoisted) against a uniform bound per register.
+      // Comparing per-register token indices instead made the compiler keep sixteen lane
+      // constants across the segment loop, spill them, and reload them one by one here.
+      const int h4 = kMasked ? 4 * (opaque_lane() >> 5) : 0;
       auto score = [&](int j) {
         sc[j] = sa[j];
         if constexpr (kMasked) {
-          const int t = 8 * (j >> 2) + 4 * hi + (j & 3);
-          if (t >= tile_valid(k)) sc[j] = -INFINITY;
+          if (h4 >= tile_valid(k) - (8 * (j >> 2) + (j & 3))) sc[j] = -INFINITY;
         }
         if (j & 1) mx = max3f(mx, sc[j - 1], sc[j]);
       };
@@ -893,13 +902,13 @@ void decode_kernel(DecodeArgs a) {
       for (int st = 0; st < 32; ++st) {
         if (st < 16) {
           const int hb = st >> 2, c = st & 3;
-          o[hb][c] = mfma32(pa[hb], bv[c], o[hb][c]);
+          o[hb][c] = mfma32(bv[c], pa[hb], o[hb][c]);
           if (c == 3) pa[hb] = ld_p(1, hb);
           if (st == 1) bvn = ld_v(1, 0);
           if (st >= 12 && st < 15) bv[st - 12] = ld_v(1, st - 11);
         } else {
           const int c = (st - 16) >> 2, hb = (st - 16) & 3;
-          o[hb][c] = mfma32(pa[hb], c == 0 ? bvn : bv[c - 1], o[hb][c]);
+          o[hb][c] = mfma32(c == 0 ? bvn : bv[c - 1], pa[hb], o[hb][c]);
         }
         if (!kFirst && st < 16) score(st);
         if (st >= oB && st < 16 + oB) xa[st - oB] = __builtin_fmaf(sc[st - oB], a.scale_log2, -m_ref);
@@ -972,7 +981,7 @@ void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) o[hb][c] = mfma32(pa[hb], bv[c], o[hb][c]);
+          for (int c = 0; c < 4; ++c) o[hb][c] = mfma32(bv[c], pa[hb], o[hb][c]);
       }
     }
 
@@ -990,50 +999,41 @@ void decode_kernel(DecodeArgs a) {
       __syncthreads();
       const bool again = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
       m_redo = m_all;         // the segment's true maximum: no score exceeds it on a redo
-      // normalise and write.  In registers, O tile (hb, c) register j is head
-      // 32hb + 8(j/4) + 4hi + (j%4), column 128w + 32c + l32: one column per lane.
-      // Each head block goes through a private LDS region of the wave (the ring is
-      // free now) so that the global stores are row-contiguous: lane (l32, hi) then
-      // holds head 32hb + 2i + hi, columns 128w + 4 l32 .. +3, and one store instruction
-      // writes two 512-byte row segments.  Row pitch 544 B keeps the two half-waves'
-      // LDS writes 32 banks apart.
+      // normalise and write.  Register j of tile (hb, c) is column 128w + 32c + 8(j/4) +
+      // 4hi + (j%4) of head 32hb + l32, so each group of four registers becomes one 8-byte
+      // bf16 write into a per-wave LDS stage of the wave's 128 columns of all 128 heads
+      // (the ring is free now; row pitch 272 B puts the 32 heads of one write on distinct
+      // bank pairs), read back as whole 16-byte row chunks: one store instruction then
+      // writes four 256-byte row segments.
       if (!again) {
         const float lse2 = m_ref + __log2f(l_head);
-        const float* lrow = lsum + 4 * hi;   // head 32hb + 8(j/4) + (j%4) from here
-        constexpr int kStagePitch = 544;
-        unsigned char* stage = lds + 1024 + wave_u * (32 * kStagePitch);
-        const int eln = opaque_lane();      // lane values recomputed here, not kept live
-        const size_t obase = (size_t)(eln >> 5) * kLatent + wave_u * 128 + 4 * (eln & 31);
-        // complete units go straight to out_latent, pieces of split units to their
-        // partial slot; both as bf16
-        uint16_t* ob16 = a.out_latent + (size_t)u * kHeads * kLatent + obase;
-        uint16_t* obp = a.part_o + (size_t)(slot < 0 ? 0 : slot) * kHeads * kLatent + obase;
+        constexpr int kStagePitch = 272;
+        static_assert(1024 + 4 * kHeads * kStagePitch <= (kF8 ? kF8LdsBytes : kSlots * kTileBytes),
+                      "the stage fits in the ring below the P buffers");
+        const int eln = opaque_lane(), el32 = eln & 31, ehi = eln >> 5;   // not kept live
+        unsigned char* stage = lds + 1024 + wave_u * (kHeads * kStagePitch);
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
-          f32x16 il;
+          const float il = lsum[32 * hb + el32];
+          unsigned char* srow = stage + (32 * hb + el32) * kStagePitch + 8 * ehi;
 #pragma unroll
-          for (int j = 0; j < 16; ++j) il[j] = lrow[32 * hb + 8 * (j >> 2) + (j & 3)];
+          for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const f32x16 v = o[hb][c] * il;
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-              *(float*)(stage + (8 * (j >> 2) + 4 * hi + (j & 3)) * kStagePitch + (32 * c + l32) * 4) = v[j];
-          }
-          // the wave reads back only what it wrote: LDS order within the wave suffices
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const f32x4 x = *(const f32x4*)(stage + (2 * i + hi) * kStagePitch + 16 * l32);
-            const size_t row = (size_t)(32 * hb + 2 * i) * kLatent;
-            const u32x2 w = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-            if (slot < 0) {
-              *(u32x2*)(ob16 + row) = w;
-            } else {
-              *(u32x2*)(obp + row) = w;
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
+            for (int q4 = 0; q4 < 4; ++q4)
+              *(u32x2*)(srow + 2 * (32 * c + 8 * q4)) =
+                  u32x2{pack_bf16x2(o[hb][c][4 * q4] * il, o[hb][c][4 * q4 + 1] * il),
+                        pack_bf16x2(o[hb][c][4 * q4 + 2] * il, o[hb][c][4 * q4 + 3] * il)};
         }
+        // the wave reads back only what it wrote: LDS order within the wave suffices.
+        // complete units go straight to out_latent, pieces of split units to their
+        // partial slot; both as bf16
+        const size_t obase = (size_t)(eln >> 4) * kLatent + wave_u * 128 + 8 * (eln & 15);
+        uint16_t* ob = (slot < 0 ? a.out_latent + (size_t)u * kHeads * kLatent
+                                 : a.part_o + (size_t)slot * kHeads * kLatent) + obase;
+        const unsigned char* rrow = stage + (eln >> 4) * kStagePitch + 16 * (eln & 15);
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          *(u32x4*)(ob + (size_t)(4 * i) * kLatent) = *(const u32x4*)(rrow + 4 * i * kStagePitch);
         if (hi == 0) {
           if (slot < 0) {
             if (a.lse != nullptr) a.lse[(size_t)u * kHeads + head] = lse2 * kLn2;
