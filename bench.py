@@ -688,6 +688,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill chunk leg")
+    ap.add_argument("--no-resident", action="store_true", help="skip the leg with the cache held in L2")
     ap.add_argument("--no-redo", action="store_true", help="skip the softmax-redo leg")
     ap.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8-cache leg")
     ap.add_argument("--no-append", action="store_true", help="skip the cache-append leg")
@@ -770,8 +771,10 @@ def main():
     log(f"[bench] c3 paged: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s; kernels us: "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in r["per"].items() if v > 0))
 
-    resident = run_cache_resident(inp, pool, torch, mla, args.steps, args.warmup, dec_ms)
-    log(f"[bench] c3 with the cache in L2: {resident}")
+    resident = None
+    if not args.no_resident:
+        resident = run_cache_resident(inp, pool, torch, mla, args.steps, args.warmup, dec_ms)
+        log(f"[bench] c3 with the cache in L2: {resident}")
 
     # fused step (absorb + paged + merge + up-proj) on the same inputs
     d_qc, d_qr = _dev_bf16(inp.q_c, torch), _dev_bf16(inp.q_r, torch)
@@ -1046,13 +1049,12 @@ def summarize_counters(run_dirs, command, kernel="decode_kernel"):
     `bench.py --pmc-run decode`: every counter averaged over the kernel's launches (the first,
     cold launch left out), then per tile per wave (instruction counts) and as shares of the
     waves' cycles (SQ_WAVE_CYCLES; the SQ cycle counters share its quad-cycle unit)."""
+    import csv
     vals = {}
     for d in run_dirs:
-        import glob
-        import csv
         names = set()
-        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            with open(path) as f:
+        for path in _csv_files(d, "counter_collection"):
+            with _open_text(path) as f:
                 for r in csv.DictReader(f):
                     names.add(r["Counter_Name"])
         for name in names:
