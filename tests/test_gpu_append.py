@@ -18,7 +18,7 @@ import pytest
 import oracle
 from synth import make_append_inputs, make_custom, make_inputs
 
-from ._gpu import (U, assert_bf16_match, assert_close, dev_bf16, dev_i32, host_bits, projection_err,
+from ._gpu import (assert_bf16_match, assert_close, dev_bf16, dev_i32, host_bits, projection_err,
                    require_gpu, rotation_err)
 
 pytestmark = pytest.mark.gpu

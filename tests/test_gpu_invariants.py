@@ -2,15 +2,13 @@
 from physical page placement, split-count invariance, NaN poison in unread
 rows, a dominant needle token, and the degenerate cases."""
 
-import math
-
 import numpy as np
 import pytest
 
 import oracle
-from synth import make_custom, make_inputs, poison_unused
+from synth import make_custom, poison_unused
 
-from ._gpu import LSE_ATOL, absorbed_inputs, assert_close, dev_bf16, dev_i32, host_bits, host_f64, require_gpu, upload
+from ._gpu import LSE_ATOL, absorbed_inputs, assert_close, dev_bf16, dev_i32, host_bits, require_gpu, upload
 
 pytestmark = pytest.mark.gpu
 

@@ -7,15 +7,13 @@ bound of scale * 2^-8 * sum|q_abs c| (+2e-3) against the unrounded definition.
 Paged-decode parity feeds both sides the same bf16 q_abs (RNE of the exact
 q_c . W_UK); the fused path is checked against the decompress oracle."""
 
-import math
-
 import numpy as np
 import pytest
 
 import oracle
-from synth import make_custom, make_inputs, poison_unused
+from synth import make_custom, make_inputs
 
-from ._gpu import (LSE_ATOL, absorbed_inputs, assert_close, dev_bf16, dev_i32, host_bits, host_f64,
+from ._gpu import (LSE_ATOL, absorbed_inputs, assert_close, dev_bf16, host_bits, host_f64,
                    lse_bound_for_rounded_q, require_gpu, upload)
 
 pytestmark = pytest.mark.gpu

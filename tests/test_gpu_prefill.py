@@ -11,8 +11,6 @@ max|err| <= 1e-2 max|ref| + 2e-3.  lse moves with the bf16 rounding of K (each
 score moves by at most scale 2^-8 sum_d |q_d K_d|) and of the queries' inputs,
 so it is held to that shift over the visible keys plus 2e-3."""
 
-import math
-
 import numpy as np
 import pytest
 
