@@ -228,6 +228,16 @@ __device__ __forceinline__ int opaque_lane() {
   return v;
 }
 
+// A per-step LDS address the compiler may not precompute: in the first step of a
+// segment the slot numbers are constants, and without this the compiler would fold
+// those addresses, hoist them out of the segment loop and, short of registers, spill
+// them; their reloads then sit in the memory counter in front of the steady loop,
+// whose counter waits it would have to tighten to zero on every step.  No instruction.
+__device__ __forceinline__ uint32_t step_local(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // max(a, b, c) in one instruction (the compiler would quiet each operand first).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
@@ -567,11 +577,11 @@ void decode_kernel(DecodeArgs a) {
       }
       // cur_addr is a multiple of 1024: the XOR after the add only touches bits 5..7
       if (part < 2) {
-        const uint32_t a0 = cur_addr + ql;
+        const uint32_t a0 = cur_addr + (kF8 ? ql : step_local(ql));
 #pragma unroll
         for (int q2 = 4 * part; q2 < 4 * part + 4; ++q2) aq[q2] = a0 ^ (32u * q2);
       } else {
-        const uint32_t r0 = cur_addr + rl;
+        const uint32_t r0 = cur_addr + (kF8 ? rl : step_local(rl));
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) ar[q2] = r0 ^ (32u * q2);
       }
@@ -846,7 +856,7 @@ void decode_kernel(DecodeArgs a) {
       //     chunk 16w + 4c + cb, byte 8 (lane & 1) -> (vprev + offV0) XOR (64c + 16r), + 16384 st + 4096 r
       const unsigned char* vprev = lds + slot_off(k == 0 ? 0 : k - 1);
       const unsigned char* pprev = pbuf + ((k - 1) & 1) * kPBytes;
-      const uint32_t vb = lds_addr(vprev) + offV0, pb = lds_addr(pprev) + offP0;
+      const uint32_t vb = lds_addr(vprev) + (kF8 ? offV0 : step_local(offV0)), pb = lds_addr(pprev) + (kF8 ? offP0 : step_local(offP0));
       auto ld_v = [&](int st, int c) -> s16x8 {
         const s16x4 v0 = lds_read_tr4_at((vb ^ (64u * c)) + 16384 * st);
         const s16x4 v1 = lds_read_tr4_at((vb ^ (64u * c + 16u)) + 16384 * st + 4096);
