@@ -161,6 +161,26 @@ def test_absorbed_branch(name, seed, batch, s_q, seqlens, mode):
     assert_close(oracle.bf16_bits_to_f64(host_bits(out))[:, :, HEADS], ref, name)
 
 
+def test_decompress_branch_with_rising_scores():
+    """Scores that rise along the keys (content queries 0, q_R = e_0, k_R[t][0] = t / 4).
+    In the 4000-token sequence every query sees past 3700 keys, so a later score exceeds
+    the largest score of the first 64 keys by more than 64 in log2 units and the
+    attention must redo those query tiles against their true maxima; in the
+    300-token sequence the scores stay within that headroom.  Both against the oracle."""
+    lens = [4000, 300]
+    inp = make_custom(103, 2, 300, lens, extra_blocks=1)
+    inp.q_c[:] = 0
+    inp.q_r[:] = 0
+    inp.q_r[..., 0] = np.uint16(0x3F80)                       # 1.0
+    inp.pool[:, :, 512:] = 0
+    for b, L in enumerate(lens):
+        t = np.arange(L)
+        inp.pool[inp.block_table[b, t // 64], t % 64, 512] = oracle.f64_to_bf16_bits(t / 4.0)
+    print("prefill decompress rising scores", flush=True)
+    out, lse = _run(inp, mode=2)
+    _check(inp, out, lse, "rising scores")
+
+
 def test_both_branches_agree():
     inp = make_custom(99, 2, 200, [200, 900], extra_blocks=1)
     a, la = _run(inp, mode=1)
