@@ -375,7 +375,12 @@ mla_status mla_rope_table(float* rope_table, int32_t max_pos, double base, void*
 }
 
 const char* mla_status_string(mla_status s) {
-  switch (s) {
+  // A C caller may pass any int; in C++ an enum object holding a value outside the
+  // enumerators' range may not be read as the enum, so its bytes are read as an int.
+  int32_t code;
+  static_assert(sizeof(s) == sizeof(code), "mla_status is int-sized");
+  memcpy(&code, &s, sizeof code);
+  switch (code) {
     case MLA_OK: return "MLA_OK";
     case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
     case MLA_ERR_MISALIGNED: return "MLA_ERR_MISALIGNED";
