@@ -136,6 +136,9 @@ CASES = [
     ("whole-prompt-64-forced", 93, 1, 64, [64], 2),
     ("longer-than-cache-forced", 94, 2, 40, [20, 200], 2),
     ("one-query-tile-edge", 95, 2, 129, [129, 4000], 2),
+    # a single query per sequence through the decompress branch, one sequence holding
+    # just that token (it sees only itself: the output is its own V row)
+    ("single-query-forced", 104, 2, 1, [1, 77], 2),
 ]
 
 
