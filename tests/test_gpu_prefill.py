@@ -154,7 +154,8 @@ def test_decompress_branch(name, seed, batch, s_q, seqlens, mode):
     ("chunk-100-auto", 96, 2, 100, [100, 500], 0),
     ("chunk-7-forced", 97, 3, 7, [7, 64, 1000], 1),
     ("chunk-255-auto", 98, 1, 255, [3000], 0),
-], ids=["chunk-100-auto", "chunk-7-forced", "chunk-255-auto"])
+    ("chunk-256-forced", 105, 2, 256, [256, 1500], 1),   # the largest s_q the absorbed decode takes
+], ids=["chunk-100-auto", "chunk-7-forced", "chunk-255-auto", "chunk-256-forced"])
 def test_absorbed_branch(name, seed, batch, s_q, seqlens, mode):
     inp = make_custom(seed, batch, s_q, seqlens, extra_blocks=1)
     print(f"prefill absorbed {name}", flush=True)
