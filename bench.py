@@ -320,7 +320,7 @@ def run_split_sweep(names, values, steps, torch, mla, command):
     the library's own choice), warm and HBM-cold, and writes the table to profiles/."""
     from synth import make_inputs
     flush = _flusher(torch)
-    lines = ["# Split sizing of the paged decode: small and long-context workloads", "",
+    lines = [f"# Split sizing of the paged decode: workloads {', '.join(names)}", "",
              "Command (run from the repository root on one MI355X):", "", "```", *command, "```", "",
              "Per workload and `num_splits` (0 = the library's choice: one workgroup per compute unit, at least "
              f"{AUTO_MIN_CHUNK} tiles each): the split (tiles of 32 tokens per workgroup, units cut into "
@@ -355,7 +355,7 @@ def run_split_sweep(names, values, steps, torch, mla, command):
         del pool
         torch.cuda.empty_cache()
     lines += ["", f"source_sha256 (decode sources): {kernel_source_hash('decode')}", ""]
-    path = os.path.join(ROOT, "profiles", "decode_split_sweep_c1_c2_c5.md")
+    path = os.path.join(ROOT, "profiles", f"decode_split_sweep_{'_'.join(names)}.md")
     with open(path, "w") as f:
         f.write("\n".join(lines))
     log(f"[bench] wrote {path}")
