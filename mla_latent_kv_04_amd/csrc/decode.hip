@@ -253,6 +253,8 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // with the segment's true maximum as the reference, so the fp32 accumulators
 // cannot overflow.
 constexpr float kHeadroom = 64.0f;
+// Ranges of at most this many tiles load a segment's queries before its first tiles.
+constexpr int kQFirstTiles = 32;
 
 // Scalar read of a value that no kernel of the launch writes (block table,
 // sequence lengths, plan_kernel's prefix sums): through the constant address space
@@ -343,6 +345,8 @@ void decode_kernel(DecodeArgs a) {
   if (!work_range(a, lane, wr)) return;
   const int g = blockIdx.x;
   const int start = wr.start, end = wr.end;
+  // queries before tiles at a segment start when the whole range is short (bf16 cache only)
+  const bool q_first = !kF8 && end - start <= kQFirstTiles;
 
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;       // which half of the wave
@@ -513,12 +517,18 @@ void decode_kernel(DecodeArgs a) {
     *(u32x4*)(pbuf + kPBytes + 32 * tid) = u32x4{0u, 0u, 0u, 0u};
     *(u32x4*)(pbuf + kPBytes + 32 * tid + 16) = u32x4{0u, 0u, 0u, 0u};
 
-    // Loads of the first two tiles go out before the queries.  The other order (the
-    // 144 KiB of queries streaming in while the block-table entries arrive) measured 4%
-    // faster steps at batch 1 and 16 but 1-3% slower ones at batch 64.
+    // Order of the segment's first loads.  A workgroup with a long range issues its first
+    // two tiles before the queries (its steady state is what counts; the other order
+    // measured 1-3% slower at batch 64); one with a short range issues the 144 KiB of
+    // queries first, which then stream in while the block-table entries of the first
+    // tiles arrive (the queries are as many bytes as four tiles, and issuing them takes a
+    // few thousand cycles): 1-4% less decode time at batch 16 (8-tile ranges), none at
+    // batch 1.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // earlier stores of this workgroup
-    issue(0);
-    if (n_tiles > 1) issue(1);
+    if (!q_first) {
+      issue(0);
+      if (n_tiles > 1) issue(1);
+    }
     if constexpr (kF8) {
       // tile 0 must be in bf16 before the first step; tile 1 may stay in flight
       if (n_tiles > 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
@@ -532,12 +542,20 @@ void decode_kernel(DecodeArgs a) {
     const int head = wave_u * 32 + l32;
     s16x8 q[36];
     {
-      const uint16_t* qa = a.q_abs + ((size_t)u * kHeads + head) * kLatent + 8 * hi;
-      const uint16_t* qr = a.q_r + ((size_t)u * kHeads + head) * kRope + 8 * hi;
+      // lane offsets taken here (an opaque lane id): hoisted out of the segment loop they
+      // would be spilled, and a reload between the loads waits for every load before it
+      const int ln = opaque_lane();
+      const int hq = wave_u * 32 + (ln & 31);
+      const uint16_t* qa = a.q_abs + ((size_t)u * kHeads + hq) * kLatent + 8 * (ln >> 5);
+      const uint16_t* qr = a.q_r + ((size_t)u * kHeads + hq) * kRope + 8 * (ln >> 5);
 #pragma unroll
       for (int ks = 0; ks < 32; ++ks) q[ks] = *(const s16x8*)(qa + 16 * ks);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) q[32 + ks] = *(const s16x8*)(qr + 16 * ks);
+    }
+    if (q_first) {
+      issue(0);
+      if (n_tiles > 1) issue(1);
     }
 
     // O^T[column block c][head block hb], kept as o[hb][c]: the PV products take V^T as the A
