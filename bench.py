@@ -706,6 +706,8 @@ def main():
                     help="write the traffic summary from the FETCH_SIZE and WRITE_SIZE pass output folders")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                     help="write the decode kernel's cycle and instruction attribution from counter pass folders")
+    ap.add_argument("--counters-kind", default="decode", choices=sorted(COUNTER_FILES),
+                    help="kernel family of --summarize-counters (the --pmc-run the passes ran)")
     ap.add_argument("--summarize-clock", nargs="+", metavar="KIND=DIR",
                     help="write the engine clock and MFMA occupancy summary from counter passes "
                          "(SQ_VALU_MFMA_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY GRBM_GUI_ACTIVE) over "
@@ -724,7 +726,7 @@ def main():
         summarize_pmc(*args.summarize_pmc, args.pmc_command, args.pmc_kind)
         return
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters, args.pmc_command)
+        summarize_counters(args.summarize_counters, args.pmc_command, args.counters_kind)
         return
     if args.summarize_clock:
         summarize_clock([x.split("=", 1) for x in args.summarize_clock], args.pmc_command)
@@ -1037,18 +1039,27 @@ def _prefill_algorithmic_bytes():
             + B * L * 64 * 2)
 
 
-COUNTER_FILE = "decode_kernel_c3_b64_counters.md"
+COUNTER_FILES = {
+    "decode": ("decode_kernel_c3_b64_counters.md", "decode_kernel",
+               "paged MLA decode, batch 64, seq_len U[1024,32768]"),
+    "mxfp8": ("decode_kernel_mxfp8_c3_b64_counters.md", "decode_kernel<true>",
+              "paged MLA decode over the MXFP8 cache, batch 64, seq_len U[1024,32768]"),
+}
+
+
 def _c3_tiles():
     from synth import make_inputs
     inp = make_inputs("c3", with_pool=False)
     return int(((inp.seqlens.astype(np.int64) + 31) // 32).sum())
 
 
-def summarize_counters(run_dirs, command, kernel="decode_kernel"):
+def summarize_counters(run_dirs, command, kind="decode"):
     """Writes the attribution summary of the decode kernel from rocprofv3 --pmc passes over
-    `bench.py --pmc-run decode`: every counter averaged over the kernel's launches (the first,
-    cold launch left out), then per tile per wave (instruction counts) and as shares of the
-    waves' cycles (SQ_WAVE_CYCLES; the SQ cycle counters share its quad-cycle unit)."""
+    `bench.py --pmc-run KIND` (decode: the bf16 cache, mxfp8: the MXFP8 cache): every counter
+    averaged over the kernel's launches (the first, cold launch left out), then per tile per
+    wave (instruction counts) and as shares of the waves' cycles (SQ_WAVE_CYCLES; the SQ cycle
+    counters share its quad-cycle unit)."""
+    out_name, kernel, what = COUNTER_FILES[kind]
     import csv
     vals = {}
     for d in run_dirs:
@@ -1066,16 +1077,16 @@ def summarize_counters(run_dirs, command, kernel="decode_kernel"):
     tiles = _c3_tiles()
     wave_tiles = 4 * tiles
     lines = [
-        "# Cycle and instruction attribution of decode_kernel: paged MLA decode, batch 64, seq_len U[1024,32768]",
+        f"# Cycle and instruction attribution of {kernel}: {what}",
         "",
         f"rocprofv3 counter passes (one per line, at most 8 SQ counters each) over `python3 bench.py --pmc-run "
-        "decode`, run from /tmp:",
+        f"{kind}`, run from /tmp:",
         "",
         "```",
         *command,
         "```",
         "",
-        f"Values are per launch of decode_kernel (the first launch of each pass left out). The workload has "
+        f"Values are per launch of {kernel} (the first launch of each pass left out). The workload has "
         f"{tiles} tiles of 32 tokens; each is processed by all four waves of its workgroup, so per-tile-per-wave "
         f"figures divide by {wave_tiles}. Cycle counters are shares of SQ_WAVE_CYCLES (the SQ counts wave cycles "
         "in quad-cycle units, the same unit for all of them); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
@@ -1093,7 +1104,7 @@ def summarize_counters(run_dirs, command, kernel="decode_kernel"):
         busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] / 8 * 1024)
         lines += ["", f"MFMA busy share of the launch's cycles: {busy:.3f}."]
     lines += ["", f"source_sha256: {kernel_source_hash('decode')}", ""]
-    path = os.path.join(ROOT, "profiles", COUNTER_FILE)
+    path = os.path.join(ROOT, "profiles", out_name)
     with open(path, "w") as f:
         f.write("\n".join(lines))
     log(f"[bench] wrote {path}")
