@@ -202,6 +202,13 @@ __device__ __forceinline__ void dma_b32(const unsigned char* sbase, uint32_t vof
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds));
 }
 
+// Query rows into a wave's LDS stage (the bf16-cache decode): the same 16-byte direct load
+// without `nt` (the workgroups that share a unit read its queries again) and with a
+// "memory" clobber, so that no LDS read of the stage moves across it.
+__device__ __forceinline__ void dma_q_b128(const unsigned char* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
 // The 9 direct loads of one tile.  Rows at or past `valid` (only in a
 // sequence's last tile) are fetched from row 0 of the tile instead: they are
 // masked out of the softmax, and loading finite data keeps 0 * V finite even
@@ -253,8 +260,21 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 // with the segment's true maximum as the reference, so the fp32 accumulators
 // cannot overflow.
 constexpr float kHeadroom = 64.0f;
-// Ranges of at most this many tiles load a segment's queries before its first tiles.
-constexpr int kQFirstTiles = 32;
+// The bf16-cache decode stages a segment's queries through LDS in two rounds (k-steps
+// 0..15 and 32..33, then 16..31 and 34..35), each wave in its own 18 KiB of ring slots 2
+// and 3, which no load touches before the first step: 32 heads x 512 B of latent chunks,
+// then 32 heads x 64 B of RoPE chunks.
+constexpr int kQStageBytes = 18432;
+constexpr int kQStageRope = 16384;
+static_assert(2 * kTileBytes + 4 * kQStageBytes <= kSlots * kTileBytes, "query stage in slots 2 and 3");
+// Code placement of the bf16-cache kernel's steady-state loop.  With the loop's first
+// instruction at 28 mod 32 bytes (so at 28 or 60 mod 64) the batch-4 x 2-query workload
+// measured 3-4% faster than at the other 4-byte offsets (a sweep of s_nop padding in the
+// prologue, code otherwise identical; the two query units of a sequence then fetch 1.03x
+// the cache bytes instead of up to 1.29x); batch 64 and the short workloads did not move.
+// The cause is not known.  This many s_nop instructions, executed once per workgroup,
+// put the loop there; a CPU test checks the offset in the compiled code.
+constexpr int kLoopPadNops = 1;
 
 // Scalar read of a value that no kernel of the launch writes (block table,
 // sequence lengths, plan_kernel's prefix sums): through the constant address space
@@ -343,10 +363,12 @@ void decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   WorkRange wr;
   if (!work_range(a, lane, wr)) return;
+  if constexpr (!kF8) {
+#pragma unroll
+    for (int i = 0; i < kLoopPadNops; ++i) asm volatile("s_nop 0");
+  }
   const int g = blockIdx.x;
   const int start = wr.start, end = wr.end;
-  // queries before tiles at a segment start when the whole range is short (bf16 cache only)
-  const bool q_first = !kF8 && end - start <= kQFirstTiles;
 
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;       // which half of the wave
@@ -517,18 +539,9 @@ void decode_kernel(DecodeArgs a) {
     *(u32x4*)(pbuf + kPBytes + 32 * tid) = u32x4{0u, 0u, 0u, 0u};
     *(u32x4*)(pbuf + kPBytes + 32 * tid + 16) = u32x4{0u, 0u, 0u, 0u};
 
-    // Order of the segment's first loads.  A workgroup with a long range issues its first
-    // two tiles before the queries (its steady state is what counts; the other order
-    // measured 1-3% slower at batch 64); one with a short range issues the 144 KiB of
-    // queries first, which then stream in while the block-table entries of the first
-    // tiles arrive (the queries are as many bytes as four tiles, and issuing them takes a
-    // few thousand cycles): 1-4% less decode time at batch 16 (8-tile ranges), none at
-    // batch 1.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // earlier stores of this workgroup
-    if (!q_first) {
-      issue(0);
-      if (n_tiles > 1) issue(1);
-    }
+    issue(0);
+    if (n_tiles > 1) issue(1);
     if constexpr (kF8) {
       // tile 0 must be in bf16 before the first step; tile 1 may stay in flight
       if (n_tiles > 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
@@ -541,7 +554,7 @@ void decode_kernel(DecodeArgs a) {
     // 32w + l32, columns 16ks + 8hi .. +7 (k-steps 0..31 latent, 32..35 RoPE).
     const int head = wave_u * 32 + l32;
     s16x8 q[36];
-    {
+    if constexpr (kF8) {
       // lane offsets taken here (an opaque lane id): hoisted out of the segment loop they
       // would be spilled, and a reload between the loads waits for every load before it
       const int ln = opaque_lane();
@@ -552,10 +565,45 @@ void decode_kernel(DecodeArgs a) {
       for (int ks = 0; ks < 32; ++ks) q[ks] = *(const s16x8*)(qa + 16 * ks);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) q[32 + ks] = *(const s16x8*)(qr + 16 * ks);
-    }
-    if (q_first) {
-      issue(0);
-      if (n_tiles > 1) issue(1);
+    } else {
+      // Loaded straight into that layout, each load instruction touches 32 rows (one per
+      // head) and the 36 of them take ~9k cycles to issue; staged through LDS, each direct
+      // load copies 1 KiB of two heads' rows (8 cache lines) and the reads into the layout
+      // are conflict-free.  Stage of a round, per head h (0..31 within the wave): latent
+      // chunk c (16 B, 0..31 of the round) at 512h + 16 (c ^ (h & 15)); RoPE chunk c (0..3
+      // of the round) at kQStageRope + 64h + 16 (c ^ f(h)), f(h) = ((h >> 1) ^ (h >> 3)) & 3.
+      const uint32_t ln = (uint32_t)opaque_lane();
+      const uint32_t ql = ln & 31, qh = ln >> 5;
+      const uint32_t qst = lbase + 2 * kTileBytes + wave_u * kQStageBytes;
+      const unsigned char* qa_w = (const unsigned char*)(a.q_abs + ((size_t)u * kHeads + wave_u * 32) * kLatent);
+      const unsigned char* qr_w = (const unsigned char*)(a.q_r + ((size_t)u * kHeads + wave_u * 32) * kRope);
+      // load i of the latent part: lanes 0..31 fill head 2i's 32 slots, lanes 32..63 head
+      // 2i + 1's; slot s holds chunk s ^ (h & 15) = (l32 ^ hi) ^ 2 (i & 7)
+      const uint32_t lat_v = 1024 * qh + 16 * (ql ^ qh);
+      // load i of the RoPE part: lane l fills slot l & 3 of head 16i + l/4
+      const uint32_t rh = ln >> 2;
+      const uint32_t rope_v = 128 * rh + 16 * ((ln & 3) ^ (((rh >> 1) ^ (rh >> 3)) & 3));
+      // reads: head l32, chunk 2k' + hi of the round at slot (2k' + hi) ^ (l32 & 15)
+      const uint32_t lat_r = qst + 512 * ql + 16 * (qh ^ (ql & 15));
+      const uint32_t fr = ((ql >> 1) ^ (ql >> 3)) & 3;
+      const uint32_t rope_r = qst + kQStageRope + 64 * ql;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (r == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // round 0 read out
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          dma_q_b128(qa_w + 2048 * i, (lat_v + 512 * r) ^ (32u * (i & 7)), qst + 1024 * i);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          dma_q_b128(qr_w + 2048 * i, (rope_v + 64 * r) ^ (32u * i), qst + kQStageRope + 1024 * i);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stage (and its tiles) in LDS
+#pragma unroll
+        for (int kp = 0; kp < 16; ++kp) q[16 * r + kp] = lds_read_b128_at(lat_r ^ (32u * kp));
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) q[32 + 2 * r + kk] = lds_read_b128_at(rope_r + 16 * ((2 * kk + qh) ^ fr));
+      }
+      // read out before the first step, whose loads of tile 2 (any wave's) refill slot 2
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 
     // O^T[column block c][head block hb], kept as o[hb][c]: the PV products take V^T as the A
