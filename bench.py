@@ -286,32 +286,74 @@ def decode_flops(seqlens, s_q):
 AUTO_MIN_CHUNK = 4    # fewest tiles per workgroup when the library sizes the split (num_splits = 0)
 
 
-def split_summary(seqlens, s_q, workgroups, auto):
-    """The decode's split of a workload, for the report: the 32-token tiles of all
-    (sequence, query) units laid end to end and cut into equal ranges of whole tiles, one
-    per workgroup; a unit cut by a range boundary leaves one bf16 partial output (128 heads
-    x 512) per range it meets, which the merge reads back."""
-    tiles = []
+SEG_COST = 6          # tiles a segment start counts for in the library's own split
+COST_SPLIT_MIN = 48   # fewest tiles per range for which that split applies
+
+
+def unit_tiles(seqlens, s_q):
+    """32-token tiles of each (sequence, query) unit: query i of a sequence of L tokens sees
+    L - s_q + i + 1 keys."""
+    out = []
     for L in np.asarray(seqlens, dtype=np.int64):
         for i in range(s_q):
             vis = max(int(L) - s_q + i + 1, 0)
-            tiles.append((vis + 31) // 32)
+            out.append((vis + 31) // 32)
+    return np.asarray(out, dtype=np.int64)
+
+
+def split_plan(tiles, workgroups, auto):
+    """The decode's work split (the same rule as the kernels' work_range): the units' tiles
+    laid end to end on a cost line where each unit with tiles also counts SEG_COST tiles for
+    its segment start (only in the library's own split, with ranges of COST_SPLIT_MIN tiles or
+    more, and when the even split's boundaries do not all fall on unit starts), cut evenly
+    into ranges of ceil(cost / workgroups) (at least AUTO_MIN_CHUNK when auto). Returns the
+    workgroups with work as (g, start, end), tiles [start, end), the segment cost used and
+    the range length on the cost line."""
     tiles = np.asarray(tiles, dtype=np.int64)
-    total = int(tiles.sum())
-    even = -(-total // workgroups)
-    chunk = max(even, AUTO_MIN_CHUNK) if auto else even
-    used = -(-total // chunk)
+    min_chunk = AUTO_MIN_CHUNK if auto else 1
+    cum = np.concatenate([[0], np.cumsum(tiles)])
+    total = int(cum[-1])
+    chunk0 = max(-(-total // workgroups), min_chunk)
+    aligned = all(cum[u] % chunk0 == 0 for u in range(len(tiles)) if tiles[u] > 0)
+    seg = SEG_COST if (min_chunk > 1 and chunk0 >= COST_SPLIT_MIN and not aligned) else 0
+    ccum = np.concatenate([[0], np.cumsum(np.where(tiles > 0, tiles + seg, 0))])
+    T = int(ccum[-1])
+    chunk = max(-(-T // workgroups), min_chunk)
+
+    def tile_at(c):
+        u = int(np.searchsorted(ccum[:-1], c, side="right")) - 1   # last unit with ccum <= c
+        return int(cum[u]) + max(0, c - int(ccum[u]) - seg)
+
+    ranges = []
+    for g in range(workgroups):
+        cs = g * chunk
+        if cs >= T or total == 0:
+            break
+        ce = min(T, cs + chunk)
+        start, end = tile_at(cs), (total if ce >= T else tile_at(ce))
+        if end > start:
+            ranges.append((g, start, end))
+    return ranges, seg, chunk
+
+
+def split_summary(seqlens, s_q, workgroups, auto):
+    """The decode's split of a workload, for the report (split_plan); a unit cut by range
+    boundaries leaves one bf16 partial output (128 heads x 512) per range it meets, which
+    the merge reads back."""
+    tiles = unit_tiles(seqlens, s_q)
+    ranges, seg, _ = split_plan(tiles, workgroups, auto)
     cum = np.concatenate([[0], np.cumsum(tiles)])
     frags = 0
     for u in range(len(tiles)):
         if tiles[u] == 0:
             continue
-        first, last = cum[u] // chunk, (cum[u + 1] - 1) // chunk
-        if last > first:
-            frags += int(last - first + 1)
+        meet = sum(1 for _, a, b in ranges if a < cum[u + 1] and b > cum[u])
+        if meet > 1:
+            frags += meet
     part = frags * 128 * 512 * 2
-    return {"workgroups_launched": workgroups, "workgroups_with_tiles": used, "tiles": total,
-            "tiles_per_workgroup": chunk, "fragments": frags, "partial_bytes": part,
+    return {"workgroups_launched": workgroups, "workgroups_with_tiles": len(ranges), "tiles": int(cum[-1]),
+            "tiles_per_workgroup": max((b - a for _, a, b in ranges), default=0), "segment_cost_tiles": seg,
+            "fragments": frags, "partial_bytes": part,
             "partial_over_cache": round(part / (int(np.sum(seqlens)) * ROW_BYTES), 4)}
 
 

@@ -92,7 +92,8 @@ mla_status mla_absorb_q(const uint16_t* q_c, const uint16_t* w_uk, uint16_t* q_a
                         int32_t tokens, int32_t num_heads, void* stream);
 
 /* Workspace bytes needed by mla_decode_paged (fused = 0) or mla_decode
- * (fused = 1) for these parameters: the pages-per-unit prefix sums, the
+ * (fused = 1) for these parameters: the split plan (tile and cost prefix sums
+ * per (sequence, query) unit), the
  * normalised partial outputs and lse of sequences split across workgroups,
  * and, when fused, q_abs and out_latent.  The pages size the cache by its
  * 64-token pages of 1152-byte rows (sheratonhq.com sections 1 and 3) and say
@@ -385,7 +386,7 @@ int32_t mla_decode_num_workgroups(const mla_decode_params* p);
  * every (sequence, query) unit, of that row's latent dwords.
  *   kv_blocks, block_table, seqlens, p: as for mla_decode_paged (p->scale unused)
  *   sums       [mla_decode_num_workgroups(p) * 256] uint32, 4-byte aligned
- *   workspace  >= mla_decode_workspace_size(p, 0) bytes (the tile prefix sums) */
+ *   workspace  >= mla_decode_workspace_size(p, 0) bytes (the split plan) */
 mla_status mla_stream_pages(const uint16_t* kv_blocks, const int32_t* block_table, const int32_t* seqlens,
                             uint32_t* sums, const mla_decode_params* p, void* workspace, size_t workspace_bytes,
                             void* stream);

@@ -96,7 +96,7 @@ constexpr int kAutoMinChunk = 4;
 
 // Host-side launch helpers (defined in the kernel translation units).
 struct DecodePlanView {
-  int32_t* cum;       // [units + 1] prefix sums of pages per work unit
+  int32_t* cum;       // [2 units + 3] the split plan: tile and cost-line prefix sums, segment cost
   uint16_t* part_o;   // [2 * wgs, 128, 512] normalised partial outputs, bf16
   float* part_lse;    // [2 * wgs, 128] log2-domain lse of the partials
 };

@@ -74,6 +74,23 @@ __device__ __forceinline__ int split_chunk(int total, int W, int min_chunk) {
   return even > min_chunk ? even : min_chunk;
 }
 
+// Segment-aware split.  A workgroup pays about 20k cycles for every segment it starts
+// (queries, first tiles, epilogue), as much as ~6 tiles of streaming; with equal tile
+// counts a workgroup whose range spans two or three units finishes that much later than
+// one inside a single unit, and the slowest sets the launch time (batch 64: 517k
+// cycles against a 481k mean).  So the library's own split (min_chunk > 1) lays the units
+// end to end on a cost line where each unit with tiles costs its tiles plus kSegCost, and
+// cuts that line evenly: a range that takes in a unit start gets kSegCost fewer tiles.
+// Kept to even splits where it cannot pay: ranges under kCostSplitMin tiles (the
+// segment cost is then a large share of a range, and ranges shift by several tiles),
+// and splits whose range boundaries already fall on unit starts (every workgroup has one
+// segment; equal sequence lengths).  Explicit num_splits (min_chunk 1) split evenly.
+constexpr int kSegCost = 6;
+constexpr int kCostSplitMin = 48;
+__device__ __forceinline__ int split_seg_cost(int even_chunk, bool aligned, int min_chunk) {
+  return (min_chunk > 1 && even_chunk >= kCostSplitMin && !aligned) ? kSegCost : 0;
+}
+
 // LDS swizzles (the LDS has 64 banks of 4 bytes; a 16-byte read by 16 lanes, or
 // an 8-byte transposing read by 32 lanes, moves 256 bytes per cycle).
 // Latent rows (1024 B, a multiple of the bank width): chunk c of token t sits at
@@ -104,34 +121,48 @@ __device__ __forceinline__ int unit_tiles(int n_visible) {
   return n_visible > 0 ? (n_visible + kTile - 1) / kTile : 0;
 }
 
-// Prefix sums of tiles per work unit: cum[0] = 0, cum[u+1] = cum[u] + ceil(visible_u / 32).
+// The split plan of U work units, plan[2U + 3] int32: plan[0..U] tile prefix sums
+// (cum[u + 1] = cum[u] + ceil(visible_u / 32)), plan[U + 1 .. 2U + 1] the cost-line prefix
+// sums (ccum[u + 1] = ccum[u] + tiles_u + seg if tiles_u > 0), plan[2U + 2] = seg (0 or
+// kSegCost).  W is the decode's workgroup count.
 __global__ __attribute__((amdgpu_flat_work_group_size(1024, 1024)))
-void plan_kernel(DecodeArgs a, int32_t* cum) {
-  __shared__ int32_t warp_tot[16];
-  __shared__ int32_t carry_s;
+void plan_kernel(DecodeArgs a, int32_t* cum, int W) {
+  __shared__ int32_t warp_tot[16], warp_nz[16];
+  __shared__ int32_t carry_s, carry_nz;
   const int U = a.batch * a.s_q;
+  int32_t* ccum = cum + U + 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) { carry_s = 0; cum[0] = 0; }
+  if (tid == 0) { carry_s = 0; carry_nz = 0; cum[0] = 0; ccum[0] = 0; }
   __syncthreads();
+  // pass 1: tile prefix sums into cum, prefix counts of units with tiles into ccum
   for (int base = 0; base < U; base += 1024) {
     const int u = base + tid;
     const int tiles = u < U ? unit_tiles(unit_visible(a, u)) : 0;
-    // inclusive scan inside the wave
-    int x = tiles;
+    int x = tiles, z = tiles > 0 ? 1 : 0;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
+      const int y = __shfl_up(x, off, 64), yz = __shfl_up(z, off, 64);
+      if (lane >= off) { x += y; z += yz; }
     }
-    if (lane == 63) warp_tot[wave] = x;
+    if (lane == 63) { warp_tot[wave] = x; warp_nz[wave] = z; }
     __syncthreads();
-    int before = carry_s;
-    for (int w = 0; w < wave; ++w) before += warp_tot[w];
-    if (u < U) cum[u + 1] = before + x;
+    int before = carry_s, before_nz = carry_nz;
+    for (int w = 0; w < wave; ++w) { before += warp_tot[w]; before_nz += warp_nz[w]; }
+    if (u < U) { cum[u + 1] = before + x; ccum[u + 1] = before_nz + z; }
     __syncthreads();
-    if (tid == 1023) carry_s = before + x;
+    if (tid == 1023) { carry_s = before + x; carry_nz = before_nz + z; }
     __syncthreads();
   }
+  // pass 2: do the even split's range boundaries all fall on unit starts?
+  const int total = carry_s;
+  const int chunk0 = split_chunk(total, W, a.min_chunk);
+  int off_grid = 0;
+  for (int u = tid; u < U; u += 1024)
+    off_grid |= (cum[u + 1] > cum[u] && cum[u] % chunk0 != 0) ? 1 : 0;
+  const int seg = split_seg_cost(chunk0, __syncthreads_or(off_grid) == 0, a.min_chunk);
+  // pass 3: cost-line prefix sums
+  for (int u = tid; u < U; u += 1024) ccum[u + 1] = cum[u + 1] + seg * ccum[u + 1];
+  if (tid == 0) cum[2 * U + 2] = seg;
 }
 
 // ---------------------------------------------------------------------------- decode
@@ -274,7 +305,7 @@ static_assert(2 * kTileBytes + 4 * kQStageBytes <= kSlots * kTileBytes, "query s
 // the cache bytes instead of up to 1.29x); batch 64 and the short workloads did not move.
 // The cause is not known.  This many s_nop instructions, executed once per workgroup,
 // put the loop there; a CPU test checks the offset in the compiled code.
-constexpr int kLoopPadNops = 1;
+constexpr int kLoopPadNops = 9;
 
 // Scalar read of a value that no kernel of the launch writes (block table,
 // sequence lengths, plan_kernel's prefix sums): through the constant address space
@@ -285,18 +316,22 @@ __device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int64_t i) {
 }
 
 // A workgroup's share of the work: tiles [start, end) of the tiles of all units laid
-// end to end (chunk = ceil(total / W) per workgroup), unit u holding tile `start`, and
-// ubeg, the first tile of unit u.
+// end to end, unit u holding tile `start`, and ubeg, the first tile of unit u.  The
+// ranges cut the cost line (see split_seg_cost) evenly: workgroup g takes cost positions
+// [g chunk, (g + 1) chunk), chunk = split_chunk(T, W, min_chunk) over the line's length
+// T; a cost position c in unit u's interval [C_u, C_u+1) is tile cum_u + max(0, c - C_u -
+// seg).  With seg = 0 this is the even split of the tiles.
 struct WorkRange {
   int start, end, u, ubeg;
 };
 
 // False when the workgroup has no tiles.  Up to kSelfPlanUnits units every wave scans
-// the lengths itself (lane u holds unit u) and workgroup 0 publishes the prefix sums for
-// the combine; more units read plan_kernel's array.
+// the lengths itself (lane u holds unit u) and workgroup 0 publishes the plan (see
+// plan_kernel) for the combine; more units read plan_kernel's array.
 __device__ __forceinline__ bool work_range(const DecodeArgs& a, int lane, WorkRange& r) {
   const int U = a.batch * a.s_q;
-  int total, pex = 0;             // pex: exclusive prefix of this lane's unit
+  const int W = (int)gridDim.x;
+  int total, T, seg, pex = 0, cpex = 0;   // pex, cpex: this lane's unit's tile and cost prefixes
   const bool self_plan = U <= kSelfPlanUnits;
   if (self_plan) {
     const int tiles = lane < U ? unit_tiles(unit_visible(a, lane)) : 0;
@@ -308,33 +343,74 @@ __device__ __forceinline__ bool work_range(const DecodeArgs& a, int lane, WorkRa
     }
     total = __builtin_amdgcn_readlane(x, 63);
     pex = x - tiles;
+    const int chunk0 = split_chunk(total, W, a.min_chunk);
+    seg = 0;
+    cpex = pex;
+    T = total;
+    if (a.min_chunk > 1 && chunk0 >= kCostSplitMin) {   // short ranges skip the alignment test
+      const bool aligned = __builtin_amdgcn_ballot_w64(tiles > 0 && pex % chunk0 != 0) == 0;
+      seg = split_seg_cost(chunk0, aligned, a.min_chunk);
+      const uint64_t nz = __builtin_amdgcn_ballot_w64(tiles > 0);
+      cpex = pex + seg * __builtin_popcountll(nz & ((1ull << lane) - 1ull));
+      T = total + seg * __builtin_popcountll(nz);
+    }
     if (blockIdx.x == 0 && threadIdx.x < 64) {
-      if (lane < U) a.cum[lane + 1] = x;
-      if (lane == 0) a.cum[0] = 0;
+      int32_t* ccum = a.cum + U + 1;
+      if (lane < U) {
+        a.cum[lane + 1] = x;
+        ccum[lane + 1] = cpex + (tiles > 0 ? tiles + seg : 0);
+      }
+      if (lane == 0) {
+        a.cum[0] = 0;
+        ccum[0] = 0;
+        a.cum[2 * U + 2] = seg;
+      }
     }
   } else {
     total = ld_uniform(a.cum, U);
+    T = ld_uniform(a.cum, 2 * U + 1);
+    seg = ld_uniform(a.cum, 2 * U + 2);
   }
   if (total <= 0) return false;
-  const int chunk = split_chunk(total, (int)gridDim.x, a.min_chunk);
-  r.start = blockIdx.x * chunk;
-  if (r.start >= total) return false;
-  r.end = min(total, r.start + chunk);
-  // largest u with cum[u] <= start (then cum[u+1] > start)
+  const int chunk = split_chunk(T, W, a.min_chunk);
+  const int cs = blockIdx.x * chunk;
+  if (cs >= T) return false;
+  const int ce = min(T, cs + chunk);
+  // the unit holding cost position c: the last with ccum <= c (units without tiles have
+  // empty intervals, and one of them is never the last: the unit after it starts at the
+  // same position, and c < T)
+  int ue = 0, ce_base = 0, ce_tile0 = 0;
   if (self_plan) {
-    // the prefix sums do not decrease, so u + 1 lanes have theirs at or below start
-    r.u = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < U && pex <= r.start)) - 1;
+    // the prefix sums do not decrease, so u + 1 lanes have theirs at or below c
+    r.u = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < U && cpex <= cs)) - 1;
     r.ubeg = __builtin_amdgcn_readlane(pex, r.u);
-  } else {
-    int lo_u = 0, hi_u = U - 1;
-    while (lo_u < hi_u) {
-      const int mid = (lo_u + hi_u + 1) >> 1;
-      if (ld_uniform(a.cum, mid) <= r.start) lo_u = mid; else hi_u = mid - 1;
+    r.start = r.ubeg + max(0, cs - __builtin_amdgcn_readlane(cpex, r.u) - seg);
+    if (ce < T) {
+      ue = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < U && cpex <= ce)) - 1;
+      ce_tile0 = __builtin_amdgcn_readlane(pex, ue);
+      ce_base = __builtin_amdgcn_readlane(cpex, ue);
     }
-    r.u = lo_u;
+  } else {
+    const int32_t* ccum = a.cum + U + 1;
+    auto last_at_or_below = [&](int c) {
+      int lo_u = 0, hi_u = U - 1;
+      while (lo_u < hi_u) {
+        const int mid = (lo_u + hi_u + 1) >> 1;
+        if (ld_uniform(ccum, mid) <= c) lo_u = mid; else hi_u = mid - 1;
+      }
+      return lo_u;
+    };
+    r.u = last_at_or_below(cs);
     r.ubeg = ld_uniform(a.cum, r.u);
+    r.start = r.ubeg + max(0, cs - ld_uniform(ccum, r.u) - seg);
+    if (ce < T) {
+      ue = last_at_or_below(ce);
+      ce_tile0 = ld_uniform(a.cum, ue);
+      ce_base = ld_uniform(ccum, ue);
+    }
   }
-  return true;
+  r.end = ce < T ? ce_tile0 + max(0, ce - ce_base - seg) : total;
+  return r.start < r.end;
 }
 
 template <bool B>
@@ -1203,18 +1279,20 @@ void stream_kernel(DecodeArgs a, uint32_t* __restrict__ sums) {
 constexpr int kCombineHeads = 8;
 constexpr int kCombineBatch = 8;
 
-__device__ __forceinline__ int fragment_slot(int gg, int g0, int chunk, int ubeg) {
-  // The first fragment is its workgroup's second segment unless the unit starts
-  // exactly at that workgroup's range; every later fragment is a first segment.
-  return (gg == g0 && gg * chunk < ubeg) ? 2 * gg + 1 : 2 * gg;
+__device__ __forceinline__ int fragment_slot(int gg, int g0, int chunk, int cbeg) {
+  // The first fragment is a later segment of its workgroup when that workgroup's range
+  // starts before the unit on the cost line (it then holds tiles of an earlier unit);
+  // every later fragment is a first segment.
+  return (gg == g0 && gg * chunk < cbeg) ? 2 * gg + 1 : 2 * gg;
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void combine_kernel(DecodeArgs a, int W) {
   const int u = blockIdx.x;
   const int U = a.batch * a.s_q;
-  const int total = ld_uniform(a.cum, U);
+  const int T = ld_uniform(a.cum, 2 * U + 1), seg = ld_uniform(a.cum, 2 * U + 2);
   const int ubeg = ld_uniform(a.cum, u), uend = ld_uniform(a.cum, u + 1);
+  const int cbeg = ld_uniform(a.cum, U + 1 + u);   // the unit's start on the cost line
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31;
   const int head = blockIdx.y * kCombineHeads + 2 * (tid >> 6) + (lane >> 5);
   const int col = 4 * l32;   // + 128 v
@@ -1225,8 +1303,9 @@ void combine_kernel(DecodeArgs a, int W) {
     if (a.lse != nullptr && l32 == 0) a.lse[(size_t)u * kHeads + head] = -INFINITY;
     return;
   }
-  const int chunk = split_chunk(total, W, a.min_chunk);
-  const int g0 = ubeg / chunk, g1 = (uend - 1) / chunk;
+  // workgroups whose ranges hold the unit's first and last tiles (see work_range)
+  const int chunk = split_chunk(T, W, a.min_chunk);
+  const int g0 = (cbeg + seg) / chunk, g1 = (cbeg + seg + (uend - ubeg) - 1) / chunk;
   if (g0 == g1) return;
   const int F = g1 - g0 + 1;   // fragments of the unit, in workgroup order
 
@@ -1234,14 +1313,14 @@ void combine_kernel(DecodeArgs a, int W) {
   // 32 fragments' lse go out first and the first batch of partials right behind them (the
   // partials do not depend on the lse), so the wait for the lse leaves that batch in flight.
   auto frag_lse = [&](int f) {
-    return f < F ? a.part_lse[(size_t)fragment_slot(g0 + f, g0, chunk, ubeg) * kHeads + head] : -INFINITY;
+    return f < F ? a.part_lse[(size_t)fragment_slot(g0 + f, g0, chunk, cbeg) * kHeads + head] : -INFINITY;
   };
   auto load_batch = [&](int f0, u32x2 (&x)[kCombineBatch][4]) {
 #pragma unroll
     for (int j = 0; j < kCombineBatch; ++j) {
       const int f = f0 + j < F ? f0 + j : F - 1;   // past the end: a valid fragment, weight 0
       const uint16_t* src =
-          a.part_o + ((size_t)fragment_slot(g0 + f, g0, chunk, ubeg) * kHeads + head) * kLatent + col;
+          a.part_o + ((size_t)fragment_slot(g0 + f, g0, chunk, cbeg) * kHeads + head) * kLatent + col;
 #pragma unroll
       for (int v = 0; v < 4; ++v) x[j][v] = __builtin_nontemporal_load((const u32x2*)(src + 128 * v));
     }
@@ -1330,7 +1409,7 @@ hipError_t launch_decode(const uint16_t* q_abs, const uint16_t* q_r, const uint1
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = hipSuccess;
   if (decode_launches_plan(batch * s_q)) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a, plan.cum);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a, plan.cum, wgs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1358,7 +1437,7 @@ hipError_t launch_stream(const uint16_t* kv, const int32_t* bt, const int32_t* s
   a.num_pages = num_pages; a.batch = batch; a.s_q = s_q; a.max_blocks = max_blocks;
   a.last_page = (int)((num_pages < ((int64_t)1 << 31) ? num_pages : ((int64_t)1 << 31)) - 1);
   if (decode_launches_plan(batch * s_q)) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a, cum);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a, cum, wgs);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -100,8 +100,8 @@ WsLayout layout(const mla_decode_params* p, int wgs, bool fused) {
   const size_t units = (size_t)p->batch * p->s_q;
   WsLayout L;
   size_t off = 0;
-  L.cum = off;
-  off += round_up((units + 1) * sizeof(int32_t));
+  L.cum = off;   // the split plan: tile and cost-line prefix sums and the segment cost
+  off += round_up((2 * (units + 1) + 1) * sizeof(int32_t));
   L.part_lse = off;
   off += round_up((size_t)2 * wgs * mla::kHeads * sizeof(float));
   L.part_o = off;

@@ -120,3 +120,69 @@ def test_trace_summary_table(fake_root):
     assert "| decode_kernel<false> | 2 | 305.0 | 305.0 | 300.0 | 310.0 | 98.4% |" in text
     assert "| combine_kernel | 1 | 10.0 | 10.0 | 10.0 | 10.0 | 1.6% |" in text
     assert f"source_sha256 (decode sources): {bench.kernel_source_hash('decode')}" in text
+
+
+def _segments(ranges, tiles):
+    """Per workgroup range: (tiles, units it meets)."""
+    cum = np.concatenate([[0], np.cumsum(tiles)])
+    out = []
+    for _, a, b in ranges:
+        out.append((b - a, sum(1 for u in range(len(tiles)) if tiles[u] > 0 and a < cum[u + 1] and b > cum[u])))
+    return out
+
+
+def test_segment_aware_split_hand_counted():
+    """Units of 400, 100 and 300 tiles over 4 workgroups, library's own split.  The even
+    split, 200 tiles each, meets 1, 1, 2 and 1 units: cost (tiles + 6 per unit met) 206,
+    206, 212, 206.  The cost line puts 6 before each unit's tiles: [0,406) [406,512)
+    [512,818), cut in ranges of ceil(818 / 4) = 205.  Cost 205 is tile 205 - 6 = 199 of
+    unit 0, cost 410 tile 400 + max(0, 410 - 406 - 6) = 400, cost 615 tile 500 + 615 - 512
+    - 6 = 597: ranges [0,199) [199,400) [400,597) [597,800), costs 205, 207, 209, 209."""
+    ranges, seg, chunk = bench.split_plan([400, 100, 300], 4, True)
+    assert seg == 6 and chunk == 205
+    assert [(a, b) for _, a, b in ranges] == [(0, 199), (199, 400), (400, 597), (597, 800)]
+    assert [t + 6 * s for t, s in _segments(ranges, [400, 100, 300])] == [205, 207, 209, 209]
+    # the same units under an explicit split stay even
+    ranges, seg, chunk = bench.split_plan([400, 100, 300], 4, False)
+    assert seg == 0 and [(a, b) for _, a, b in ranges] == [(0, 200), (200, 400), (400, 600), (600, 800)]
+    # ranges on unit starts already (every range inside one unit): no change
+    ranges, seg, _ = bench.split_plan([256, 256, 512], 4, True)
+    assert seg == 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_segment_aware_split_properties(seed):
+    """Random workloads (zero-tile units included), 256 workgroups: the ranges tile the
+    line without gaps; the merge's formulas (first and last workgroup of a unit, and whether
+    the first fragment is a later segment of its workgroup) agree with the ranges; and the
+    largest range cost, tiles + 6 per unit met, is never above the even split's."""
+    rng = np.random.default_rng(seed)
+    for _ in range(20):
+        U = int(rng.integers(1, 150))
+        tiles = np.where(rng.random(U) < 0.1, 0, rng.integers(1, 1200, size=U))
+        for auto in (True, False):
+            ranges, seg, chunk = bench.split_plan(tiles, 256, auto)
+            if tiles.sum() == 0:
+                assert ranges == []
+                continue
+            assert ranges[0][1] == 0 and ranges[-1][2] == tiles.sum()
+            assert all(r[2] == s[1] for r, s in zip(ranges, ranges[1:]))
+            cum = np.concatenate([[0], np.cumsum(tiles)])
+            ccum = np.concatenate([[0], np.cumsum(np.where(tiles > 0, tiles + seg, 0))])
+            for u in range(U):
+                if tiles[u] == 0:
+                    continue
+                gs = [g for g, a, b in ranges if a < cum[u + 1] and b > cum[u]]
+                g0, g1 = (ccum[u] + seg) // chunk, (ccum[u] + seg + tiles[u] - 1) // chunk
+                assert gs == list(range(g0, g1 + 1))
+                start0 = [a for g, a, b in ranges if g == g0][0]
+                assert (start0 < cum[u]) == (g0 * chunk < ccum[u])
+            if auto:
+                cost = max(t + 6 * s for t, s in _segments(ranges, tiles))
+                plain_chunk = max(-(-int(tiles.sum()) // 256), 4)
+                plain = []
+                for g in range(256):
+                    a, b = g * plain_chunk, min(int(tiles.sum()), (g + 1) * plain_chunk)
+                    if a < b:
+                        plain.append((g, a, b))
+                assert cost <= max(t + 6 * s for t, s in _segments(plain, tiles)) + 1

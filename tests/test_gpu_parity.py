@@ -123,6 +123,35 @@ def test_decode_paged_around_the_in_kernel_plan_limit(batch, s_q, num_splits):
     assert_close(host_f64(ol), ref_ol, "out_latent")
     assert np.max(np.abs(lse.double().cpu().numpy() - ref_lse)) <= LSE_ATOL
 
+@pytest.mark.parametrize("batch,s_q", [(40, 1), (70, 1), (36, 2)])
+def test_decode_paged_segment_aware_split(batch, s_q):
+    """The library's own split over ragged lengths long enough for ranges of 48 tiles or
+    more, where it lays the units on a cost line (each unit start counts 6 tiles, so a range
+    that takes in a unit start gets fewer tiles): the in-kernel plan (40 units) and the plan
+    kernel (70 and 72 units), with sequences that have no visible token, against the oracle
+    for every sequence."""
+    import bench
+    rng = np.random.default_rng(90 + batch + s_q)
+    seqlens = [int(x) for x in rng.integers(s_q, 24000, size=batch)]
+    seqlens[3] = s_q - 1                      # a sequence whose queries see no token
+    seqlens[batch - 1] = 1                    # one token (query 0 of two sees none)
+    ranges, seg, _ = bench.split_plan(bench.unit_tiles(seqlens, s_q), 256, True)
+    assert seg == bench.SEG_COST and len(ranges) > 200, "the case must exercise the cost-line split"
+    inp = make_custom(91 + batch, batch, s_q, seqlens, extra_blocks=1)
+    _print_case(f"segment-aware split units={batch * s_q}", inp)
+    d = upload(inp)
+    qa = absorbed_inputs(inp)
+    ol, lse = _paged(inp, d, qa, 0)
+    ref_ol, ref_lse = oracle.decode_absorbed(qa, inp.q_r, inp.pool, inp.block_table, inp.seqlens, s_q, inp.scale)
+    got = host_f64(ol)
+    for b in range(batch):
+        assert_close(got[b:b + 1], ref_ol[b:b + 1], f"out_latent seq {b} (L={seqlens[b]})")
+    got_lse = lse.double().cpu().numpy()
+    empty = np.isneginf(ref_lse)
+    assert empty.any() and np.all(np.isneginf(got_lse[empty]))
+    assert np.max(np.abs(got_lse[~empty] - ref_lse[~empty])) <= LSE_ATOL
+
+
 @pytest.mark.parametrize("tiles_per_split", [1, 2, 3])
 @pytest.mark.parametrize("s_q", [1, 2])
 def test_decode_short_fragments_with_partial_tiles(tiles_per_split, s_q):
