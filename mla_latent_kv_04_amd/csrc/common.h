@@ -93,6 +93,12 @@ __device__ __forceinline__ s16x8 lds_read_b128_at(uint32_t addr) {
 // (16 workgroups), 32 us with 2 and 39-40 us with 1; larger workloads, whose even split
 // already gives 8 or more tiles per compute unit, are unaffected.
 constexpr int kAutoMinChunk = 4;
+// The segment-aware split (decode_kernel's work_range): a segment start counts as this
+// many tiles on the cost line, for ranges of at least kCostSplitMin tiles.
+constexpr int kSegCost = 6;
+constexpr int kCostSplitMin = 48;
+// Most workgroups a decode split uses (num_splits is at most 2^16).
+constexpr int kMaxSplits = 1 << 16;
 
 // Host-side launch helpers (defined in the kernel translation units).
 struct DecodePlanView {

@@ -85,8 +85,7 @@ __device__ __forceinline__ int split_chunk(int total, int W, int min_chunk) {
 // segment cost is then a large share of a range, and ranges shift by several tiles),
 // and splits whose range boundaries already fall on unit starts (every workgroup has one
 // segment; equal sequence lengths).  Explicit num_splits (min_chunk 1) split evenly.
-constexpr int kSegCost = 6;
-constexpr int kCostSplitMin = 48;
+// (kSegCost and kCostSplitMin are in common.h: the host checks bound the cost line.)
 __device__ __forceinline__ int split_seg_cost(int even_chunk, bool aligned, int min_chunk) {
   return (min_chunk > 1 && even_chunk >= kCostSplitMin && !aligned) ? kSegCost : 0;
 }

@@ -59,16 +59,20 @@ mla_status check_params(const mla_decode_params* p) {
   if (p->page_size != mla::kPage) return fail(MLA_ERR_UNSUPPORTED, "page_size %d (supported: 64)", p->page_size);
   if (p->max_blocks_per_seq < 1) return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", p->max_blocks_per_seq);
   if (p->max_blocks_per_seq > (1 << 24)) return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_seq too large");
-  if (p->num_splits < 0 || p->num_splits > (1 << 16)) return fail(MLA_ERR_INVALID_ARG, "num_splits %d", p->num_splits);
+  if (p->num_splits < 0 || p->num_splits > mla::kMaxSplits) return fail(MLA_ERR_INVALID_ARG, "num_splits %d", p->num_splits);
   if (p->num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages %lld < 1", (long long)p->num_pages);
   if (!(p->scale > 0.f) || p->scale > 1e30f) return fail(MLA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (p->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "reserved must be 0");
   if ((int64_t)p->batch * p->s_q > (1 << 24)) return fail(MLA_ERR_INVALID_ARG, "batch * s_q too large");
-  // The kernels sum 32-token tiles per (sequence, query) unit in 32-bit integers; a unit
-  // has at most 2 * max_blocks_per_seq tiles, so this bounds every prefix sum.
-  if ((int64_t)p->batch * p->s_q * p->max_blocks_per_seq * 2 > INT32_MAX)
-    return fail(MLA_ERR_INVALID_ARG, "batch * s_q * max_blocks_per_seq * 2 = %lld tiles exceeds 2^31 - 1",
-                (long long)p->batch * p->s_q * p->max_blocks_per_seq * 2);
+  // The kernels sum 32-token tiles per (sequence, query) unit in 32-bit integers, on a
+  // cost line where each unit also counts kSegCost tiles; a unit has at most 2 *
+  // max_blocks_per_seq tiles, and a range start may pass the line's end by one range
+  // (at most kMaxSplits), so this bounds every prefix sum and range position.
+  const int64_t line = (int64_t)p->batch * p->s_q * ((int64_t)p->max_blocks_per_seq * 2 + mla::kSegCost);
+  if (line + mla::kMaxSplits > INT32_MAX)
+    return fail(MLA_ERR_INVALID_ARG,
+                "batch * s_q * (max_blocks_per_seq * 2 + %d) + %d = %lld exceeds 2^31 - 1 (tile prefix sums)",
+                mla::kSegCost, mla::kMaxSplits, (long long)(line + mla::kMaxSplits));
   return MLA_OK;
 }
 

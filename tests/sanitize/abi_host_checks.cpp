@@ -101,7 +101,7 @@ int main() {
     mla_decode_params p = params();
     p.batch = 4096;
     p.s_q = 2;
-    p.max_blocks_per_seq = (1 << 17) - 1;
+    p.max_blocks_per_seq = 131064;   // 8192 units x (2 x 131064 + 6) + 65536 <= 2^31 - 1
     p.num_splits = 1 << 16;
     const size_t need = mla_decode_workspace_size(&p, 0);
     expect_true("largest accepted decode has a workspace size", need > 0);

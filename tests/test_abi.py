@@ -89,7 +89,11 @@ def test_page_sum_overflow_rejected(lib):
     assert st == _lib.MLA_ERR_INVALID_ARG
     st = lib.mla_decode_paged_mxfp8(A, A, A, A, A, A, None, ctypes.byref(over), A, 1 << 40, None)
     assert st == _lib.MLA_ERR_INVALID_ARG
-    fits = _params(batch=4096, s_q=2, max_blocks_per_seq=(1 << 17) - 1, num_splits=8)
+    # the cost line of the split adds 6 per unit and a range may start one range (at most
+    # 2^16) past its end: 8192 * (2 * 131064 + 6) + 65536 fits, 131065 does not
+    assert _paged(lib, _params(batch=4096, s_q=2, max_blocks_per_seq=131065, num_splits=8)) == \
+        _lib.MLA_ERR_INVALID_ARG
+    fits = _params(batch=4096, s_q=2, max_blocks_per_seq=131064, num_splits=8)
     assert lib.mla_decode_workspace_size(ctypes.byref(fits), 0) > 0
 
 
