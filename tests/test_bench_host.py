@@ -107,6 +107,14 @@ def test_committed_decode_traffic_matches_the_sources():
     assert t is not None and t["fetch"] > 1.3e9
 
 
+@pytest.mark.parametrize("kind", sorted(bench.TRAFFIC))
+def test_every_committed_traffic_summary_matches_its_sources(kind):
+    """Every kernel family's committed FETCH_SIZE/WRITE_SIZE summary was taken on the
+    sources in the tree (a header shared by several families changes all their hashes)."""
+    t = bench.load_traffic(kind)
+    assert t is not None and t["fetch"] > 0 and t["write"] > 0, f"profiles/{bench.TRAFFIC[kind]['file']}"
+
+
 def test_trace_summary_table(fake_root):
     d = fake_root / "trace"
     d.mkdir()
