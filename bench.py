@@ -425,6 +425,10 @@ def other_row(oi, orr, layers):
                            "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                            "kernel": "decode_kernel", "algorithmic_flops_per_launch": flops,
                            "hbm_GBps_of_cache": round(orr["cache_bytes"] / (dec_ms * 1e-3) / 1e9, 1)}
+        # HBM bytes of this workload's launch, where a counter summary for it is committed
+        t = load_traffic(oi.name) if oi.name in TRAFFIC else None
+        row["roofline"]["traffic"] = int(t["fetch"] + t["write"]) if t else None
+        row["roofline"]["traffic_split"] = t
     else:
         gb = orr["cache_bytes"] / (dec_ms * 1e-3) / 1e9
         row["roofline"] = {"bound": "hbm", "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
