@@ -243,6 +243,8 @@ def test_stream_pages_many_units_and_c3():
     in the benchmark's configuration."""
     rng = np.random.default_rng(63)
     for inp in (make_custom(64, 70, 1, [int(x) for x in rng.integers(1, 400, size=70)], extra_blocks=1),
+                # the plan kernel with the segment-aware split (ranges of 48+ tiles)
+                make_custom(65, 70, 1, [int(x) for x in rng.integers(1, 24000, size=70)], extra_blocks=1),
                 make_inputs("c3")):
         _print_case("stream", inp)
         d = upload(inp)

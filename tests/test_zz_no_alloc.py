@@ -46,7 +46,11 @@ def test_noalloc_matches_workspace_decode_twice(num_splits):
     import torch
     import mla_latent_kv_04_amd as mla
     rng = np.random.default_rng(90 + num_splits)
-    cases = [make_custom(91, 70, 1, [int(x) for x in rng.integers(1, 3000, size=70)], extra_blocks=1),
+    # largest first, each later call smaller: 70 long sequences (the plan kernel; with the
+    # library's own split the ranges are cut on the segment-aware cost line), 70 short ones,
+    # then 3 sequences of two queries
+    cases = [make_custom(93, 70, 1, [int(x) for x in rng.integers(1, 24000, size=70)], extra_blocks=1),
+             make_custom(91, 70, 1, [int(x) for x in rng.integers(1, 3000, size=70)], extra_blocks=1),
              make_custom(92, 3, 2, [2, 65, 700], extra_blocks=1)]
     for inp in cases:
         print(f"[case] noalloc splits={num_splits} B={inp.batch} s_q={inp.s_q}", flush=True)
